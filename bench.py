@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""bench.py -- time the bf16 delta-sync hot path on one MI355X.
+
+One step is one pass of the whole path over the resident snapshots of a
+parameter list:
+  1. delta_diff_many  (sender: bitwise change detection + compaction)
+  2. delta_apply_many (receiver: in-place scatter into its snapshot)
+  3. xor_mask         (sender, XOR mode: full-size mask)
+  4. xor_apply        (receiver, XOR mode: snapshot ^= mask)
+Step 2 turns the receiver snapshot into `new`, step 4 turns it back into
+`old`, so every step does identical work without any reset.
+
+Default workload: the Llama-7B-shaped list (291 tensors, 6,738,415,616 bf16
+elements), weights N(0, 0.02), bf16-resident step at lr 1e-6 (about 1 %
+changed).  Inputs are generated on the GPU and resident in HBM before timing.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+METRIC = "GB/s of bf16 weights diffed+compacted and applied; % of MI355X HBM peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c5"])
+    ap.add_argument("--lr", type=float, default=None)
+    ap.add_argument("--mode", default=None, choices=[None, "fp32_master", "bf16_resident"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU-time budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_bf16_delta_amd as sbd
+    from sparse_bf16_delta_amd.plan import ApplyPlan, DiffPlan
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    sbd.load()
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    cfg = workloads.CONFIGS[args.config]
+    lr = args.lr if args.lr is not None else (1e-6 if cfg.key == "c3" else cfg.lrs[0])
+    mode = args.mode or cfg.mode
+    numels = cfg.numels
+    n_model = sum(numels)
+    offs, n_alloc = workloads.flat_layout(numels)
+    log(f"[bench] device {props.name} ({getattr(props, 'gcnArchName', '?')}), "
+        f"{props.multi_processor_count} CUs, {props.total_memory / 2**30:.0f} GiB")
+    log(f"[bench] workload {cfg.key}: {len(numels)} tensors, {n_model:,} elements, "
+        f"lr {lr:g}, {mode}")
+
+    # ---- resident inputs: one flat arena per snapshot, 256-byte aligned params
+    t0 = time.perf_counter()
+    old = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
+    new = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
+    for t, (o, n) in enumerate(zip(offs, numels)):
+        sw, su = workloads.seeds(cfg.number, t)
+        workloads.fill_step_pair_(old[o:o + n], new[o:o + n], sw, su, lr, mode)
+    snap = old.clone()
+    mask = torch.empty(n_alloc, dtype=torch.int16, device=dev)
+    olds = [old[o:o + n] for o, n in zip(offs, numels)]
+    news = [new[o:o + n] for o, n in zip(offs, numels)]
+    snaps = [snap[o:o + n] for o, n in zip(offs, numels)]
+    torch.cuda.synchronize()
+    log(f"[bench] generated inputs in {time.perf_counter() - t0:.1f} s")
+
+    # ---- plans: capacity from one untimed sizing pass
+    cap = n_model // 8 + 65536
+    dplan = DiffPlan(olds, news, cap)
+    dplan.run()
+    nnz_total = dplan.changed()
+    if nnz_total > cap:
+        cap = nnz_total + 65536
+        dplan = DiffPlan(olds, news, cap)
+        dplan.run()
+        nnz_total = dplan.changed()
+    aplan = ApplyPlan(snaps)
+    density = nnz_total / n_model
+    log(f"[bench] changed {nnz_total:,} of {n_model:,} (density {density:.4%}, "
+        f"sparsity {1 - density:.4%})")
+
+    # correctness of one step before timing: apply gives new, XOR gives old back
+    aplan.run(dplan.idx, dplan.val, dplan.offsets, cap)
+    ok_apply = torch.equal(snap.view(torch.int16), new.view(torch.int16))
+    sbd.xor_mask(old, new, out=mask)
+    sbd.xor_apply_(snap, mask)
+    ok_xor = torch.equal(snap.view(torch.int16), old.view(torch.int16))
+    if not (ok_apply and ok_xor):
+        print(f"bench.py: step check failed (apply {ok_apply}, xor {ok_xor})", file=sys.stderr)
+        sys.exit(1)
+
+    # ---- algorithmic bytes per launch
+    nnz_dev = dplan.nnz
+    if nnz_total:
+        poff = torch.tensor(offs, dtype=torch.int64, device=dev)
+        base = torch.repeat_interleave(poff, nnz_dev)
+        pos = dplan.idx[:nnz_total].long() + base
+        lines128 = int(((pos >> 6)[1:] != (pos >> 6)[:-1]).sum().item()) + 1
+        lines64 = int(((pos >> 5)[1:] != (pos >> 5)[:-1]).sum().item()) + 1
+        del base, pos
+    else:
+        lines128 = lines64 = 0
+    b_diff = 4 * n_model + 6 * nnz_total
+    b_apply = 6 * nnz_total + 2 * 128 * lines128
+    b_apply64 = 6 * nnz_total + 2 * 64 * lines64
+    b_xor = 6 * n_alloc
+
+    stream = torch.cuda.current_stream(dev)
+    names = ["delta_diff_many", "delta_apply_many", "xor_mask", "xor_apply"]
+
+    def one_step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dplan.run()
+        if ev is not None:
+            ev[1].record(stream)
+        aplan.run(dplan.idx, dplan.val, dplan.offsets, cap)
+        if ev is not None:
+            ev[2].record(stream)
+        sbd.xor_mask(old, new, out=mask)
+        if ev is not None:
+            ev[3].record(stream)
+        sbd.xor_apply_(snap, mask)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        one_step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = 1e3 * wall / args.steps
+    op_ms = [sum(events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps))
+             / args.steps for i in range(4)]
+    if dplan.changed() != nnz_total or not torch.equal(snap.view(torch.int16),
+                                                       old.view(torch.int16)):
+        print("bench.py: timed steps changed the result", file=sys.stderr)
+        sys.exit(1)
+
+    alg = [b_diff, b_apply, b_xor, b_xor]
+    kernels = []
+    for name, ms, b in zip(names, op_ms, alg):
+        gbs = b / (ms * 1e-3) / 1e9
+        kernels.append({"kernel": name, "ms": round(ms, 4), "alg_bytes": b,
+                        "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "weights_gbs": round(2 * n_model / (ms * 1e-3) / 1e9, 1)})
+    for kk in kernels:
+        log(f"[bench] {kk['kernel']:17s} {kk['ms']:8.3f} ms  {kk['achieved_gbs']:8.1f} GB/s "
+            f"({100 * kk['frac']:.1f} % of peak)  weights {kk['weights_gbs']:.1f} GB/s")
+    dom = max(range(4), key=lambda i: op_ms[i])
+    roofline = {"bound": "hbm", "kernel": names[dom],
+                "achieved": kernels[dom]["achieved_gbs"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": kernels[dom]["frac"], "traffic": None}
+
+    # copy ceiling on the same arenas (one snapshot read + one written)
+    cs, ce = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mview = mask.view(torch.bfloat16)
+    mview.copy_(old)
+    torch.cuda.synchronize()
+    cs.record(stream)
+    for _ in range(3):
+        mview.copy_(old)
+    ce.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 3 * 4 * n_alloc / (cs.elapsed_time(ce) * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(2 * n_model / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.title}: {len(numels)} tensors, {n_model} bf16 elements, "
+                        f"{mode} step lr {lr:g}",
+            "tensors": len(numels), "elements": n_model, "lr": lr, "step_model": mode,
+            "changed": nnz_total, "density": round(density, 6),
+            "sparsity": round(1 - density, 6), "wire_bytes": 6 * nnz_total,
+            "touched_lines_128B": lines128, "touched_lines_64B": lines64,
+            "apply_alg_bytes_64B_lines": b_apply64,
+            "step": "diff_many + apply_many + xor_mask + xor_apply",
+        },
+        "roofline": roofline,
+        "kernels": kernels,
+        "sparse_sync_gbs": round(2 * n_model / ((op_ms[0] + op_ms[1]) * 1e-3) / 1e9, 1),
+        "copy_ceiling_gbs": round(copy_gbs, 1),
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+                   "cus": props.multi_processor_count, "torch": torch.__version__},
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, cfg, olds, news, dplan, nnz_total)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, cfg, olds, news, dplan, nnz_total):
+    """The CPU oracle, timed on this host on a bounded sample of the same
+    workload: whole tensors in list order until the time budget is used.
+    The sample's GPU deltas are compared with the oracle's on the way."""
+    import numpy as np
+    import torch
+
+    from oracle import oracle
+
+    import workloads
+
+    offs_dev = dplan.offsets.cpu().numpy()
+    done_bytes, spent, tensors, elems, identical = 0, 0.0, 0, 0, True
+    for p, (o_t, n_t) in enumerate(zip(olds, news)):
+        if spent >= args.cpu_seconds:
+            break
+        o = workloads.bits_numpy(o_t)
+        x = workloads.bits_numpy(n_t)
+        t0 = time.perf_counter()
+        idx, val = oracle.diff(o, x)
+        snap = o.copy()
+        oracle.apply_(snap, idx, val)
+        mask = oracle.xor_mask(o, x)
+        snap2 = o.copy()
+        oracle.xor_apply_(snap2, mask)
+        spent += time.perf_counter() - t0
+        done_bytes += 2 * o.size
+        tensors += 1
+        elems += o.size
+        a, b = int(offs_dev[p]), int(offs_dev[p + 1])
+        if b <= dplan.capacity:
+            gi = dplan.idx[a:b].cpu().numpy()
+            gv = dplan.val[a:b].view(torch.int16).cpu().numpy().view(np.uint16)
+            identical &= bool(np.array_equal(gi, idx) and np.array_equal(gv, val))
+    gbs = done_bytes / spent / 1e9 if spent > 0 else None
+    log(f"[bench] cpu oracle: {tensors} tensors, {elems:,} elements, {spent:.1f} s, "
+        f"{gbs:.3f} GB/s, parity on sample: {identical}")
+    return {"value": round(gbs, 4) if gbs else None, "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"first {tensors} of {len(olds)} tensors ({elems} elements), full step "
+                      "(diff, apply, xor_mask, xor_apply) per tensor, single-threaded C",
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
+            "sample_parity_identical": identical}
+
+
+if __name__ == "__main__":
+    main()

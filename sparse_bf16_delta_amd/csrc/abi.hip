@@ -1,0 +1,221 @@
+// abi.hip -- the extern "C" entry points declared in include/sbd.h:
+// argument validation, workspace layout, parameter-table upload and launch.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "sbd.h"
+#include "sbd_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+delta_status fail(delta_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return s;
+}
+
+delta_status ok() { return DELTA_OK; }
+
+delta_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DELTA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kInt32Max = 2147483647LL;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+namespace sbd {
+
+int64_t max_tiles_for(int64_t total_elems, int32_t nparams) {
+  // each parameter adds at most one partial tile
+  return total_elems / kDiffTile + int64_t(nparams) + 1;
+}
+
+WsLayout ws_layout(int64_t max_tiles, int32_t nparams) {
+  WsLayout L;
+  L.counter = 0;
+  L.state = 256;
+  L.tile_param = L.state + align256(sizeof(uint64_t) * size_t(max_tiles));
+  L.table = L.tile_param + align256(sizeof(int32_t) * size_t(max_tiles));
+  const size_t entry = sizeof(DiffParam) > sizeof(SnapParam) ? sizeof(DiffParam) : sizeof(SnapParam);
+  L.total = L.table + align256(entry * size_t(nparams > 0 ? nparams : 1));
+  return L;
+}
+
+}  // namespace sbd
+
+extern "C" {
+
+size_t delta_workspace_size(int64_t total_elems, int32_t nparams) {
+  if (total_elems < 0 || nparams < 0) return 0;
+  return sbd::ws_layout(sbd::max_tiles_for(total_elems, nparams), nparams).total;
+}
+
+const char* delta_last_error(void) { return g_error.c_str(); }
+
+delta_status delta_diff(const uint16_t* old_bits, const uint16_t* new_bits, int64_t n,
+                        int32_t* idx, uint16_t* val, int64_t capacity, int64_t* nnz, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (n < 0) return fail(DELTA_E_INVALID, "delta_diff: n=%lld < 0", (long long)n);
+  if (capacity < 0)
+    return fail(DELTA_E_INVALID, "delta_diff: capacity=%lld < 0", (long long)capacity);
+  if (n > kInt32Max)
+    return fail(DELTA_E_RANGE, "delta_diff: n=%lld exceeds the int32 index range",
+                (long long)n);
+  if (nnz == nullptr) return fail(DELTA_E_INVALID, "delta_diff: nnz is null");
+  if (n > 0 && (old_bits == nullptr || new_bits == nullptr))
+    return fail(DELTA_E_INVALID, "delta_diff: null input with n=%lld", (long long)n);
+  if (capacity > 0 && (idx == nullptr || val == nullptr))
+    return fail(DELTA_E_INVALID, "delta_diff: null output with capacity=%lld",
+                (long long)capacity);
+  const sbd::WsLayout L = sbd::ws_layout(sbd::max_tiles_for(n, 1), 1);
+  if (ws == nullptr || ws_bytes < L.total)
+    return fail(DELTA_E_WORKSPACE, "delta_diff: workspace %zu bytes, need %zu", ws_bytes,
+                L.total);
+  sbd::DiffParam single{old_bits, new_bits, n, 0};
+  const int64_t tiles = (n + sbd::kDiffTile - 1) / sbd::kDiffTile;
+  g_error.clear();
+  return hip_status(sbd::launch_diff(nullptr, single, 1, tiles, idx, val, capacity, nnz, nullptr,
+                                     ws, L, static_cast<hipStream_t>(stream)),
+                    "delta_diff launch");
+}
+
+delta_status delta_diff_many(int32_t nparams, const uint16_t* const* old_ptrs,
+                             const uint16_t* const* new_ptrs, const int64_t* numels,
+                             int32_t* idx, uint16_t* val, int64_t capacity, int64_t* nnz,
+                             int64_t* offsets, void* ws, size_t ws_bytes, void* stream) {
+  if (nparams < 0) return fail(DELTA_E_INVALID, "delta_diff_many: nparams=%d < 0", nparams);
+  if (capacity < 0)
+    return fail(DELTA_E_INVALID, "delta_diff_many: capacity=%lld < 0", (long long)capacity);
+  if (offsets == nullptr) return fail(DELTA_E_INVALID, "delta_diff_many: offsets is null");
+  if (nparams > 0 && (old_ptrs == nullptr || new_ptrs == nullptr || numels == nullptr ||
+                      nnz == nullptr))
+    return fail(DELTA_E_INVALID, "delta_diff_many: null parameter array");
+  std::vector<sbd::DiffParam> table(static_cast<size_t>(nparams > 0 ? nparams : 0));
+  int64_t total = 0, tiles = 0;
+  for (int32_t p = 0; p < nparams; ++p) {
+    const int64_t n = numels[p];
+    if (n < 0)
+      return fail(DELTA_E_INVALID, "delta_diff_many: numels[%d]=%lld < 0", p, (long long)n);
+    if (n > kInt32Max)
+      return fail(DELTA_E_RANGE, "delta_diff_many: numels[%d]=%lld exceeds the int32 index range",
+                  p, (long long)n);
+    if (n > 0 && (old_ptrs[p] == nullptr || new_ptrs[p] == nullptr))
+      return fail(DELTA_E_INVALID, "delta_diff_many: null tensor pointer for parameter %d", p);
+    table[p] = sbd::DiffParam{old_ptrs[p], new_ptrs[p], n, tiles};
+    tiles += (n + sbd::kDiffTile - 1) / sbd::kDiffTile;
+    total += n;
+  }
+  if (capacity > 0 && (idx == nullptr || val == nullptr))
+    return fail(DELTA_E_INVALID, "delta_diff_many: null output with capacity=%lld",
+                (long long)capacity);
+  const sbd::WsLayout L = sbd::ws_layout(sbd::max_tiles_for(total, nparams), nparams);
+  if (ws == nullptr || ws_bytes < L.total)
+    return fail(DELTA_E_WORKSPACE, "delta_diff_many: workspace %zu bytes, need %zu", ws_bytes,
+                L.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  sbd::DiffParam* d_table = reinterpret_cast<sbd::DiffParam*>(static_cast<char*>(ws) + L.table);
+  if (nparams > 0) {
+    const hipError_t e = hipMemcpyAsync(d_table, table.data(), sizeof(sbd::DiffParam) * table.size(),
+                                        hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_status(e, "delta_diff_many table copy");
+  }
+  g_error.clear();
+  sbd::DiffParam none{nullptr, nullptr, 0, 0};
+  return hip_status(sbd::launch_diff(nparams > 0 ? d_table : nullptr, none, nparams, tiles, idx,
+                                     val, capacity, nnz, offsets, ws, L, s),
+                    "delta_diff_many launch");
+}
+
+delta_status delta_apply(uint16_t* snapshot, int64_t n, const int32_t* idx, const uint16_t* val,
+                         int64_t nnz, int64_t* violations, void* stream) {
+  if (n < 0 || nnz < 0)
+    return fail(DELTA_E_INVALID, "delta_apply: n=%lld nnz=%lld", (long long)n, (long long)nnz);
+  if (n > kInt32Max)
+    return fail(DELTA_E_RANGE, "delta_apply: n=%lld exceeds the int32 index range",
+                (long long)n);
+  if (nnz > 0 && (snapshot == nullptr || idx == nullptr || val == nullptr))
+    return fail(DELTA_E_INVALID, "delta_apply: null pointer with nnz=%lld", (long long)nnz);
+  sbd::SnapParam single{snapshot, n};
+  g_error.clear();
+  return hip_status(sbd::launch_apply(nullptr, single, 1, nullptr, idx, val, nnz, violations,
+                                      static_cast<hipStream_t>(stream)),
+                    "delta_apply launch");
+}
+
+delta_status delta_apply_many(int32_t nparams, uint16_t* const* snap_ptrs, const int64_t* numels,
+                              const int32_t* idx, const uint16_t* val, const int64_t* offsets,
+                              int64_t max_nnz, int64_t* violations, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (nparams < 0 || max_nnz < 0)
+    return fail(DELTA_E_INVALID, "delta_apply_many: nparams=%d max_nnz=%lld", nparams,
+                (long long)max_nnz);
+  if (nparams == 0 || max_nnz == 0) {
+    g_error.clear();
+    return hip_status(sbd::launch_apply(nullptr, sbd::SnapParam{nullptr, 0}, 0, nullptr, nullptr,
+                                        nullptr, 0, violations, static_cast<hipStream_t>(stream)),
+                      "delta_apply_many launch");
+  }
+  if (snap_ptrs == nullptr || numels == nullptr || offsets == nullptr || idx == nullptr ||
+      val == nullptr)
+    return fail(DELTA_E_INVALID, "delta_apply_many: null pointer argument");
+  std::vector<sbd::SnapParam> table(static_cast<size_t>(nparams));
+  for (int32_t p = 0; p < nparams; ++p) {
+    const int64_t n = numels[p];
+    if (n < 0)
+      return fail(DELTA_E_INVALID, "delta_apply_many: numels[%d]=%lld < 0", p, (long long)n);
+    if (n > kInt32Max)
+      return fail(DELTA_E_RANGE,
+                  "delta_apply_many: numels[%d]=%lld exceeds the int32 index range", p,
+                  (long long)n);
+    if (n > 0 && snap_ptrs[p] == nullptr)
+      return fail(DELTA_E_INVALID, "delta_apply_many: null snapshot for parameter %d", p);
+    table[p] = sbd::SnapParam{snap_ptrs[p], n};
+  }
+  const size_t need = 256 + align256(sizeof(sbd::SnapParam) * size_t(nparams));
+  if (ws == nullptr || ws_bytes < need)
+    return fail(DELTA_E_WORKSPACE, "delta_apply_many: workspace %zu bytes, need %zu", ws_bytes,
+                need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  sbd::SnapParam* d_table = reinterpret_cast<sbd::SnapParam*>(static_cast<char*>(ws) + 256);
+  const hipError_t e = hipMemcpyAsync(d_table, table.data(), sizeof(sbd::SnapParam) * table.size(),
+                                      hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_status(e, "delta_apply_many table copy");
+  g_error.clear();
+  return hip_status(sbd::launch_apply(d_table, sbd::SnapParam{nullptr, 0}, nparams, offsets, idx,
+                                      val, max_nnz, violations, s),
+                    "delta_apply_many launch");
+}
+
+delta_status xor_mask(const uint16_t* old_bits, const uint16_t* new_bits, uint16_t* mask,
+                      int64_t n, void* stream) {
+  if (n < 0) return fail(DELTA_E_INVALID, "xor_mask: n=%lld < 0", (long long)n);
+  if (n > 0 && (old_bits == nullptr || new_bits == nullptr || mask == nullptr))
+    return fail(DELTA_E_INVALID, "xor_mask: null pointer with n=%lld", (long long)n);
+  g_error.clear();
+  return hip_status(sbd::launch_xor_mask(old_bits, new_bits, mask, n,
+                                         static_cast<hipStream_t>(stream)),
+                    "xor_mask launch");
+}
+
+delta_status xor_apply(uint16_t* snapshot, const uint16_t* mask, int64_t n, void* stream) {
+  if (n < 0) return fail(DELTA_E_INVALID, "xor_apply: n=%lld < 0", (long long)n);
+  if (n > 0 && (snapshot == nullptr || mask == nullptr))
+    return fail(DELTA_E_INVALID, "xor_apply: null pointer with n=%lld", (long long)n);
+  g_error.clear();
+  return hip_status(sbd::launch_xor_apply(snapshot, mask, n, static_cast<hipStream_t>(stream)),
+                    "xor_apply launch");
+}
+
+}  // extern "C"

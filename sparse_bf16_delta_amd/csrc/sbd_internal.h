@@ -1,0 +1,64 @@
+// Internal declarations shared by the HIP translation units of libsbd.
+// Not installed; the public contract is include/sbd.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sbd {
+
+// ---------------------------------------------------------------------------
+// Diff / compaction tiling.  One workgroup of 256 lanes (four wave64s) owns a
+// tile of kDiffIters * 256 * 8 elements: every lane issues kDiffIters 16-byte
+// loads per input, one wave covers 1 KB contiguous per load.  Tiles never
+// straddle parameters.
+// ---------------------------------------------------------------------------
+constexpr int kDiffBlock = 256;
+constexpr int kDiffWaves = kDiffBlock / 64;
+constexpr int kVec = 8;  // bf16 per 16-byte load
+constexpr int kDiffIters = 8;
+constexpr int64_t kDiffTile = int64_t(kDiffBlock) * kVec * kDiffIters;  // 16384
+
+// Parameter descriptor as stored in the workspace (32 bytes).
+struct DiffParam {
+  const uint16_t* old_bits;
+  const uint16_t* new_bits;
+  int64_t numel;
+  int64_t first_tile;
+};
+
+struct SnapParam {
+  uint16_t* snap;
+  int64_t numel;
+};
+
+// Workspace layout: [header 256 B | tile state 8 B/tile | tile->param 4 B/tile
+// | parameter table 32 B/param].  All offsets are 256-byte aligned.
+struct WsLayout {
+  size_t counter;     // uint32 dynamic tile counter
+  size_t state;       // uint64 per tile: status (2 bits) | count (62 bits)
+  size_t tile_param;  // int32 per tile
+  size_t table;       // DiffParam / SnapParam per parameter
+  size_t total;
+};
+
+WsLayout ws_layout(int64_t max_tiles, int32_t nparams);
+int64_t max_tiles_for(int64_t total_elems, int32_t nparams);
+
+// Launchers return hipSuccess or the launch error.
+hipError_t launch_diff(const DiffParam* d_table, const DiffParam& single, int32_t nparams,
+                       int64_t total_tiles, int32_t* idx, uint16_t* val, int64_t capacity,
+                       int64_t* nnz, int64_t* offsets, void* ws, const WsLayout& L,
+                       hipStream_t stream);
+
+hipError_t launch_apply(const SnapParam* d_table, const SnapParam& single, int32_t nparams,
+                        const int64_t* offsets, const int32_t* idx, const uint16_t* val,
+                        int64_t max_nnz, int64_t* violations, hipStream_t stream);
+
+hipError_t launch_xor_mask(const uint16_t* a, const uint16_t* b, uint16_t* out, int64_t n,
+                           hipStream_t stream);
+hipError_t launch_xor_apply(uint16_t* snap, const uint16_t* mask, int64_t n,
+                            hipStream_t stream);
+
+}  // namespace sbd

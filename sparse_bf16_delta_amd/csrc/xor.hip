@@ -1,0 +1,95 @@
+// xor.hip -- the XOR-mask mode: mask = old ^ new and snapshot ^= mask.
+//
+// What is computed (humans& weight-sync summary, first paragraph): the
+// trainer XORs old and new weights bit by bit into a mask the size of the
+// model; the receiver XORs that mask into its old weights to obtain the new
+// ones, with no floating-point arithmetic.  Applying the same mask twice
+// restores the original.
+//
+// How, on gfx950: a pure stream.  Each workgroup of 256 lanes moves 4 x 16 B
+// per lane per operand (16 KB per operand per workgroup) with all loads in
+// flight before the first store; a grid-stride loop bounds the grid.  The
+// mask may alias an input (and the snapshot is both input and output), so no
+// pointer is declared restrict.  Unaligned operands fall back to 2-byte
+// accesses.
+#include "sbd_internal.h"
+
+namespace sbd {
+namespace {
+
+constexpr int kXorBlock = 256;
+constexpr int kXorIters = 4;
+constexpr int64_t kXorChunkVec = int64_t(kXorBlock) * kXorIters;  // uint4 per workgroup step
+
+__global__ __launch_bounds__(kXorBlock) void xor_vec_kernel(const uint4* a, const uint4* b,
+                                                            uint4* out, int64_t nvec,
+                                                            const uint16_t* a_tail,
+                                                            const uint16_t* b_tail,
+                                                            uint16_t* out_tail, int tail) {
+  const int64_t stride = int64_t(gridDim.x) * kXorChunkVec;
+  for (int64_t base = int64_t(blockIdx.x) * kXorChunkVec; base < nvec; base += stride) {
+    uint4 x[kXorIters], y[kXorIters];
+#pragma unroll
+    for (int k = 0; k < kXorIters; ++k) {
+      const int64_t v = base + int64_t(k) * kXorBlock + threadIdx.x;
+      if (v < nvec) {
+        x[k] = a[v];
+        y[k] = b[v];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kXorIters; ++k) {
+      const int64_t v = base + int64_t(k) * kXorBlock + threadIdx.x;
+      if (v < nvec)
+        out[v] = make_uint4(x[k].x ^ y[k].x, x[k].y ^ y[k].y, x[k].z ^ y[k].z, x[k].w ^ y[k].w);
+    }
+  }
+  // the last n % 8 elements
+  if (blockIdx.x == 0 && int(threadIdx.x) < tail)
+    out_tail[threadIdx.x] = uint16_t(a_tail[threadIdx.x] ^ b_tail[threadIdx.x]);
+}
+
+__global__ __launch_bounds__(kXorBlock) void xor_scalar_kernel(const uint16_t* a,
+                                                               const uint16_t* b, uint16_t* out,
+                                                               int64_t n) {
+  const int64_t stride = int64_t(gridDim.x) * kXorBlock;
+  for (int64_t i = int64_t(blockIdx.x) * kXorBlock + threadIdx.x; i < n; i += stride)
+    out[i] = uint16_t(a[i] ^ b[i]);
+}
+
+hipError_t launch_xor3(const uint16_t* a, const uint16_t* b, uint16_t* out, int64_t n,
+                       hipStream_t stream) {
+  if (n <= 0) return hipGetLastError();
+  const bool aligned = ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
+                         reinterpret_cast<uintptr_t>(out)) & 15u) == 0;
+  if (aligned) {
+    const int64_t nvec = n / kVec;
+    const int tail = int(n - nvec * kVec);
+    int64_t blocks = (nvec + kXorChunkVec - 1) / kXorChunkVec;
+    if (blocks < 1) blocks = 1;
+    if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
+    xor_vec_kernel<<<dim3(unsigned(blocks)), dim3(kXorBlock), 0, stream>>>(
+        reinterpret_cast<const uint4*>(a), reinterpret_cast<const uint4*>(b),
+        reinterpret_cast<uint4*>(out), nvec, a + nvec * kVec, b + nvec * kVec,
+        out + nvec * kVec, tail);
+  } else {
+    int64_t blocks = (n + kXorBlock - 1) / kXorBlock;
+    if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
+    xor_scalar_kernel<<<dim3(unsigned(blocks)), dim3(kXorBlock), 0, stream>>>(a, b, out, n);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_xor_mask(const uint16_t* a, const uint16_t* b, uint16_t* out, int64_t n,
+                           hipStream_t stream) {
+  return launch_xor3(a, b, out, n, stream);
+}
+
+hipError_t launch_xor_apply(uint16_t* snap, const uint16_t* mask, int64_t n,
+                            hipStream_t stream) {
+  return launch_xor3(snap, mask, snap, n, stream);
+}
+
+}  // namespace sbd

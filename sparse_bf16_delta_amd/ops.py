@@ -1,0 +1,228 @@
+"""torch-facing wrappers over libsbd's C ABI: argument checks and marshalling.
+
+Every step of the hot path runs in libsbd's HIP kernels; torch supplies device
+memory and the current stream only.  Names mirror the sources' callables:
+
+  diff(old, new)                  -- per-tensor sparse delta (verl review,
+                                     `shard_delta_indices`)
+  diff_many(olds, news)           -- batched over a parameter list
+                                     (verl review, `gather_v_batched_to_rank0`)
+  apply_(snap, idx, val)          -- in-place scatter (TRL article, section 4.3)
+  apply_many_(snaps, idx, val, offsets)
+  xor_mask(old, new)              -- XOR-mask mode (humans& summary)
+  xor_apply_(snap, mask)
+
+Bit patterns travel as bfloat16 tensors (int16/uint16 views are accepted too);
+indices are int32, counts and offsets int64, all on the same device.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Sequence
+
+import torch
+
+from ._abi import DeltaError, DeltaRangeError, check, load
+
+INT32_MAX = (1 << 31) - 1
+_BIT_DTYPES = (torch.bfloat16, torch.int16, torch.uint16)
+
+_workspaces: dict = {}
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _bits(t, what: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype not in _BIT_DTYPES:
+        # cf. the verl review: an unsupported element size is a ValueError
+        raise ValueError(f"{what}: unsupported dtype {t.dtype}; expected bfloat16 bits")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: must be on a GPU, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    return t
+
+
+def _range(n: int, what: str):
+    if n > INT32_MAX:
+        raise DeltaRangeError(2, f"{what}: {n} elements exceed the int32 index range")
+
+
+def workspace_size(total_elems: int, nparams: int) -> int:
+    return int(load().delta_workspace_size(int(total_elems), int(nparams)))
+
+
+def workspace(nbytes: int, device: torch.device) -> torch.Tensor:
+    """A cached uint8 workspace per (device, stream), grown on demand.  Calls
+    sharing a stream are ordered, so they may share it."""
+    device = torch.device(device)
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def default_capacity(n: int) -> int:
+    """Every element when that is at most 256 MB of output, else an eighth of
+    the elements plus slack; an overflow is detected and redone exactly."""
+    if 6 * n <= (256 << 20):
+        return n
+    return n // 8 + 65536
+
+
+def diff(old: torch.Tensor, new: torch.Tensor, capacity: int | None = None):
+    """(idx int32[k], val bfloat16[k]) of the positions whose bits differ."""
+    _bits(old, "old")
+    _bits(new, "new")
+    if old.numel() != new.numel() or old.device != new.device:
+        raise ValueError("old and new must have the same numel and device")
+    n = old.numel()
+    _range(n, "diff")
+    dev = old.device
+    lib = load()
+    cap = default_capacity(n) if capacity is None else int(capacity)
+    ws = workspace(lib.delta_workspace_size(n, 1), dev)
+    nnz = torch.empty(1, dtype=torch.int64, device=dev)
+    while True:
+        idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+        val = torch.empty(max(cap, 1), dtype=torch.bfloat16, device=dev)
+        check(lib.delta_diff(_ptr(old), _ptr(new), n, _ptr(idx), _ptr(val), cap, _ptr(nnz),
+                             _ptr(ws), ws.numel(), _stream(dev)))
+        k = int(nnz.item())  # the one device->host read
+        if k <= cap:
+            return idx[:k], val[:k]
+        cap = k
+
+
+def diff_many(olds: Sequence[torch.Tensor], news: Sequence[torch.Tensor],
+              capacity: int | None = None):
+    """Batched diff: (idx_cat int32, val_cat bf16, nnz int64[P], offsets int64[P+1]),
+    parameter-local indices concatenated in list order."""
+    if len(olds) != len(news):
+        raise ValueError("olds and news differ in length")
+    if not olds:
+        raise ValueError("empty parameter list")
+    dev = olds[0].device
+    numels = []
+    for p, (o, x) in enumerate(zip(olds, news)):
+        _bits(o, f"olds[{p}]")
+        _bits(x, f"news[{p}]")
+        if o.numel() != x.numel() or o.device != dev or x.device != dev:
+            raise ValueError(f"parameter {p}: numel or device mismatch")
+        _range(o.numel(), f"parameter {p}")
+        numels.append(o.numel())
+    k = len(olds)
+    total = sum(numels)
+    lib = load()
+    cap = default_capacity(total) if capacity is None else int(capacity)
+    ws = workspace(lib.delta_workspace_size(total, k), dev)
+    optrs = (ctypes.c_void_p * k)(*[o.data_ptr() for o in olds])
+    nptrs = (ctypes.c_void_p * k)(*[x.data_ptr() for x in news])
+    nums = (ctypes.c_int64 * k)(*numels)
+    nnz = torch.empty(k, dtype=torch.int64, device=dev)
+    offsets = torch.empty(k + 1, dtype=torch.int64, device=dev)
+    while True:
+        idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+        val = torch.empty(max(cap, 1), dtype=torch.bfloat16, device=dev)
+        check(lib.delta_diff_many(k, optrs, nptrs, nums, _ptr(idx), _ptr(val), cap, _ptr(nnz),
+                                  _ptr(offsets), _ptr(ws), ws.numel(), _stream(dev)))
+        t = int(offsets[k].item())  # the one device->host read
+        if t <= cap:
+            return idx[:t], val[:t], nnz, offsets
+        cap = t
+
+
+def _violations(dev, enabled: bool):
+    return torch.empty(1, dtype=torch.int64, device=dev) if enabled else None
+
+
+def _raise_on_violations(v):
+    if v is not None:
+        bad = int(v.item())
+        if bad:
+            raise DeltaError(1, f"{bad} delta entries out of range or not strictly ascending")
+
+
+def apply_(snap: torch.Tensor, idx: torch.Tensor, val: torch.Tensor, check_indices=False):
+    """snap.view(-1)[idx] = val in place; returns snap."""
+    _bits(snap, "snapshot")
+    _bits(val, "val")
+    if idx.dtype != torch.int32 or idx.device != snap.device or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 tensor on the snapshot's device")
+    if idx.numel() != val.numel() or val.device != snap.device:
+        raise ValueError("idx and val must have equal length on the snapshot's device")
+    n = snap.numel()
+    _range(n, "apply")
+    v = _violations(snap.device, check_indices)
+    check(load().delta_apply(_ptr(snap), n, _ptr(idx), _ptr(val), idx.numel(),
+                             _ptr(v) if v is not None else None, _stream(snap.device)))
+    _raise_on_violations(v)
+    return snap
+
+
+def apply_many_(snaps: Sequence[torch.Tensor], idx: torch.Tensor, val: torch.Tensor,
+                offsets: torch.Tensor, max_nnz: int | None = None, check_indices=False):
+    """Batched in-place scatter of a diff_many result into `snaps`."""
+    if not snaps:
+        raise ValueError("empty parameter list")
+    dev = snaps[0].device
+    for p, s in enumerate(snaps):
+        _bits(s, f"snaps[{p}]")
+        if s.device != dev:
+            raise ValueError(f"snaps[{p}] on another device")
+        _range(s.numel(), f"parameter {p}")
+    _bits(val, "val")
+    k = len(snaps)
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.device != dev:
+        raise ValueError("idx must be a contiguous int32 tensor on the snapshots' device")
+    if offsets.dtype != torch.int64 or offsets.numel() != k + 1 or offsets.device != dev:
+        raise ValueError("offsets must be int64[nparams+1] on the snapshots' device")
+    if val.numel() != idx.numel() or val.device != dev:
+        raise ValueError("idx and val must have equal length")
+    m = idx.numel() if max_nnz is None else min(int(max_nnz), idx.numel())
+    lib = load()
+    ws = workspace(lib.delta_workspace_size(0, k), dev)
+    sptrs = (ctypes.c_void_p * k)(*[s.data_ptr() for s in snaps])
+    nums = (ctypes.c_int64 * k)(*[s.numel() for s in snaps])
+    v = _violations(dev, check_indices)
+    check(lib.delta_apply_many(k, sptrs, nums, _ptr(idx), _ptr(val), _ptr(offsets.contiguous()),
+                               m, _ptr(v) if v is not None else None, _ptr(ws), ws.numel(),
+                               _stream(dev)))
+    _raise_on_violations(v)
+    return snaps
+
+
+def xor_mask(old: torch.Tensor, new: torch.Tensor, out: torch.Tensor | None = None):
+    """mask = old ^ new (bit patterns) as an int16 tensor shaped like old."""
+    _bits(old, "old")
+    _bits(new, "new")
+    if old.numel() != new.numel() or old.device != new.device:
+        raise ValueError("old and new must have the same numel and device")
+    if out is None:
+        out = torch.empty(old.shape, dtype=torch.int16, device=old.device)
+    else:
+        _bits(out, "out")
+        if out.numel() != old.numel() or out.device != old.device:
+            raise ValueError("out must match old in numel and device")
+    check(load().xor_mask(_ptr(old), _ptr(new), _ptr(out), old.numel(), _stream(old.device)))
+    return out
+
+
+def xor_apply_(snap: torch.Tensor, mask: torch.Tensor):
+    """snap ^= mask in place; returns snap."""
+    _bits(snap, "snapshot")
+    _bits(mask, "mask")
+    if snap.numel() != mask.numel() or snap.device != mask.device:
+        raise ValueError("snapshot and mask must have the same numel and device")
+    check(load().xor_apply(_ptr(snap), _ptr(mask), snap.numel(), _stream(snap.device)))
+    return snap

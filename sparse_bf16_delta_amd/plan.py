@@ -1,0 +1,101 @@
+"""Persistent plans for a fixed parameter list: the per-step sync loop of an
+RL trainer calls the C ABI with buffers allocated once, and reads nothing
+back unless asked.
+
+An RL run syncs the same parameters every step, so the pointer arrays, the
+workspace and a delta buffer of fixed capacity are built once.  A step then
+costs one ctypes call per side; the true count lands in device memory and is
+read only when the caller needs it (TRL article section 4.2: one delta per
+optimizer step; verl review notes: one stacked device-to-host read).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Sequence
+
+import torch
+
+from ._abi import DeltaError, check, load
+from .ops import _bits, _ptr, _range, _stream
+
+
+class DiffPlan:
+    """Sender side: delta_diff_many over fixed (old, new) snapshot lists."""
+
+    def __init__(self, olds: Sequence[torch.Tensor], news: Sequence[torch.Tensor],
+                 capacity: int):
+        if len(olds) != len(news) or not olds:
+            raise ValueError("need two equally long, non-empty parameter lists")
+        self.device = olds[0].device
+        for p, (o, x) in enumerate(zip(olds, news)):
+            _bits(o, f"olds[{p}]")
+            _bits(x, f"news[{p}]")
+            if o.numel() != x.numel() or o.device != self.device or x.device != self.device:
+                raise ValueError(f"parameter {p}: numel or device mismatch")
+            _range(o.numel(), f"parameter {p}")
+        self.nparams = k = len(olds)
+        self.numels = [o.numel() for o in olds]
+        self.total = sum(self.numels)
+        self.capacity = int(capacity)
+        self._keep = (list(olds), list(news))
+        self._optrs = (ctypes.c_void_p * k)(*[o.data_ptr() for o in olds])
+        self._nptrs = (ctypes.c_void_p * k)(*[x.data_ptr() for x in news])
+        self._nums = (ctypes.c_int64 * k)(*self.numels)
+        lib = load()
+        dev = self.device
+        self.ws = torch.empty(lib.delta_workspace_size(self.total, k), dtype=torch.uint8, device=dev)
+        self.idx = torch.empty(max(self.capacity, 1), dtype=torch.int32, device=dev)
+        self.val = torch.empty(max(self.capacity, 1), dtype=torch.bfloat16, device=dev)
+        self.nnz = torch.empty(k, dtype=torch.int64, device=dev)
+        self.offsets = torch.empty(k + 1, dtype=torch.int64, device=dev)
+
+    def run(self):
+        """Enqueue the diff on the current stream; returns without syncing."""
+        check(load().delta_diff_many(self.nparams, self._optrs, self._nptrs, self._nums,
+                                     _ptr(self.idx), _ptr(self.val), self.capacity,
+                                     _ptr(self.nnz), _ptr(self.offsets), _ptr(self.ws),
+                                     self.ws.numel(), _stream(self.device)))
+
+    def changed(self) -> int:
+        """True total count (one device-to-host read)."""
+        return int(self.offsets[self.nparams].item())
+
+    def result(self):
+        """(idx, val, nnz, offsets) of the last run; raises if the capacity was
+        too small (the caller re-plans with a larger one)."""
+        t = self.changed()
+        if t > self.capacity:
+            raise DeltaError(3, f"delta of {t} entries exceeds the capacity {self.capacity}")
+        return self.idx[:t], self.val[:t], self.nnz, self.offsets
+
+
+class ApplyPlan:
+    """Receiver side: delta_apply_many into fixed resident snapshots."""
+
+    def __init__(self, snaps: Sequence[torch.Tensor]):
+        if not snaps:
+            raise ValueError("empty parameter list")
+        self.device = snaps[0].device
+        for p, s in enumerate(snaps):
+            _bits(s, f"snaps[{p}]")
+            if s.device != self.device:
+                raise ValueError(f"snaps[{p}] on another device")
+            _range(s.numel(), f"parameter {p}")
+        self.nparams = k = len(snaps)
+        self._keep = list(snaps)
+        self._sptrs = (ctypes.c_void_p * k)(*[s.data_ptr() for s in snaps])
+        self._nums = (ctypes.c_int64 * k)(*[s.numel() for s in snaps])
+        self.ws = torch.empty(load().delta_workspace_size(0, k), dtype=torch.uint8,
+                              device=self.device)
+
+    def run(self, idx: torch.Tensor, val: torch.Tensor, offsets: torch.Tensor,
+            max_nnz: int | None = None, violations: torch.Tensor | None = None):
+        """Enqueue the scatter of a diff_many-layout delta; returns without syncing.
+        Entries j < min(offsets[nparams], max_nnz) are applied."""
+        if offsets.numel() != self.nparams + 1 or offsets.dtype != torch.int64:
+            raise ValueError("offsets must be int64[nparams+1]")
+        m = idx.numel() if max_nnz is None else int(max_nnz)
+        check(load().delta_apply_many(self.nparams, self._sptrs, self._nums, _ptr(idx), _ptr(val),
+                                      _ptr(offsets), m,
+                                      _ptr(violations) if violations is not None else None,
+                                      _ptr(self.ws), self.ws.numel(), _stream(self.device)))

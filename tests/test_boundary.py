@@ -1,0 +1,137 @@
+"""The C-ABI boundary without a GPU: the library loads, exports every entry
+point include/sbd.h declares, sizes workspaces, and rejects bad arguments
+before touching the device.  The Python layer rejects bad tensors."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from conftest import ROOT
+
+import sparse_bf16_delta_amd as sbd
+from sparse_bf16_delta_amd import _abi
+
+HEADER = os.path.join(ROOT, "include", "sbd.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_path():
+    names = header_functions()
+    for want in ("delta_workspace_size", "delta_diff", "delta_diff_many", "delta_apply",
+                 "delta_apply_many", "xor_mask", "xor_apply", "delta_last_error"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _abi.load()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert set(header_functions()) == set(_abi.SIGNATURES)
+
+
+def test_single_hip_runtime_in_process():
+    _abi.load()
+    maps = open("/proc/self/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(paths) == 1, paths
+
+
+def test_workspace_size():
+    lib = _abi.load()
+    assert lib.delta_workspace_size(-1, 1) == 0
+    assert lib.delta_workspace_size(1, -1) == 0
+    a = lib.delta_workspace_size(1 << 20, 1)
+    b = lib.delta_workspace_size(1 << 30, 1)
+    c = lib.delta_workspace_size(1 << 30, 300)
+    assert 0 < a < b < c
+    # 8 B scan state + 4 B map per 16384-element tile, plus the table
+    assert b >= 12 * ((1 << 30) // 16384)
+    assert c - b >= 300 * 32 - 512
+
+
+def _err(lib):
+    return lib.delta_last_error().decode()
+
+
+def test_argument_errors_return_before_any_launch():
+    lib = _abi.load()
+    one = ctypes.c_void_p(16)  # never dereferenced: every call below is rejected first
+    assert lib.delta_diff(one, one, -1, one, one, 0, one, one, 1 << 20, None) == _abi.DELTA_E_INVALID
+    assert "n=-1" in _err(lib)
+    assert lib.delta_diff(one, one, 1 << 31, one, one, 0, one, one, 1 << 40, None) == _abi.DELTA_E_RANGE
+    assert "int32" in _err(lib)
+    assert lib.delta_diff(one, one, 10, one, one, 0, None, one, 1 << 20, None) == _abi.DELTA_E_INVALID
+    assert lib.delta_diff(None, one, 10, one, one, 5, one, one, 1 << 20, None) == _abi.DELTA_E_INVALID
+    assert lib.delta_diff(one, one, 10, None, one, 5, one, one, 1 << 20, None) == _abi.DELTA_E_INVALID
+    assert lib.delta_diff(one, one, 10, one, one, -1, one, one, 1 << 20, None) == _abi.DELTA_E_INVALID
+    assert lib.delta_diff(one, one, 10, one, one, 5, one, one, 16, None) == _abi.DELTA_E_WORKSPACE
+    assert lib.delta_diff(one, one, 10, one, one, 5, one, None, 1 << 20, None) == _abi.DELTA_E_WORKSPACE
+    ptrs = (ctypes.c_void_p * 2)(16, 16)
+    big = (ctypes.c_int64 * 2)(10, 1 << 31)
+    neg = (ctypes.c_int64 * 2)(10, -3)
+    assert lib.delta_diff_many(2, ptrs, ptrs, big, one, one, 10, one, one, one, 1 << 40,
+                               None) == _abi.DELTA_E_RANGE
+    assert "numels[1]" in _err(lib)
+    assert lib.delta_diff_many(2, ptrs, ptrs, neg, one, one, 10, one, one, one, 1 << 40,
+                               None) == _abi.DELTA_E_INVALID
+    assert lib.delta_diff_many(-1, ptrs, ptrs, neg, one, one, 10, one, one, one, 1 << 40,
+                               None) == _abi.DELTA_E_INVALID
+    assert lib.delta_diff_many(2, ptrs, ptrs, big, one, one, 10, one, None, one, 1 << 40,
+                               None) == _abi.DELTA_E_INVALID
+    nul = (ctypes.c_void_p * 2)(16, None)
+    ok2 = (ctypes.c_int64 * 2)(10, 10)
+    assert lib.delta_diff_many(2, nul, ptrs, ok2, one, one, 10, one, one, one, 1 << 40,
+                               None) == _abi.DELTA_E_INVALID
+    assert lib.delta_diff_many(2, ptrs, ptrs, ok2, one, one, 10, one, one, one, 64,
+                               None) == _abi.DELTA_E_WORKSPACE
+    assert lib.delta_apply(one, -1, one, one, 3, None, None) == _abi.DELTA_E_INVALID
+    assert lib.delta_apply(one, 1 << 31, one, one, 3, None, None) == _abi.DELTA_E_RANGE
+    assert lib.delta_apply(None, 10, one, one, 3, None, None) == _abi.DELTA_E_INVALID
+    assert lib.delta_apply_many(2, ptrs, big, one, one, one, 5, None, one, 1 << 20,
+                                None) == _abi.DELTA_E_RANGE
+    assert lib.delta_apply_many(2, ptrs, ok2, one, one, one, 5, None, one, 8,
+                                None) == _abi.DELTA_E_WORKSPACE
+    assert lib.delta_apply_many(2, ptrs, ok2, one, one, None, 5, None, one, 1 << 20,
+                                None) == _abi.DELTA_E_INVALID
+    assert lib.xor_mask(one, None, one, 5, None) == _abi.DELTA_E_INVALID
+    assert lib.xor_mask(one, one, one, -5, None) == _abi.DELTA_E_INVALID
+    assert lib.xor_apply(None, one, 5, None) == _abi.DELTA_E_INVALID
+
+
+def test_python_layer_rejects_bad_tensors():
+    cpu = torch.zeros(8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        sbd.diff(cpu, cpu)
+    with pytest.raises(ValueError, match="dtype"):
+        sbd.diff(torch.zeros(8, dtype=torch.float32), torch.zeros(8, dtype=torch.float32))
+    with pytest.raises(TypeError):
+        sbd.xor_mask([1, 2], [1, 2])
+    with pytest.raises(ValueError):
+        sbd.diff_many([], [])
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(_abi, "_lib", None)
+    monkeypatch.setattr(_abi, "LIB_PATH", os.path.join(ROOT, "no_such_libsbd.so"))
+    with pytest.raises(ImportError, match="no CPU fallback"):
+        _abi.load()
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The package never imports, links or opens anything under oracle/."""
+    pkg = os.path.join(ROOT, "sparse_bf16_delta_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f
+    assert "oracle" not in open(HEADER).read().lower()
