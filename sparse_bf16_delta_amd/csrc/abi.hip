@@ -44,10 +44,10 @@ int64_t max_tiles_for(int64_t total_elems, int32_t nparams) {
 
 WsLayout ws_layout(int64_t max_tiles, int32_t nparams) {
   WsLayout L;
-  L.counter = 0;
+  L.flag = 0;
   L.state = 256;
-  L.tile_param = L.state + align256(sizeof(uint64_t) * size_t(max_tiles));
-  L.table = L.tile_param + align256(sizeof(int32_t) * size_t(max_tiles));
+  L.tile_desc = L.state + align256(sizeof(uint64_t) * size_t(max_tiles));
+  L.table = L.tile_desc + align256(sizeof(TileDesc) * size_t(max_tiles));
   const size_t entry = sizeof(DiffParam) > sizeof(SnapParam) ? sizeof(DiffParam) : sizeof(SnapParam);
   L.total = L.table + align256(entry * size_t(nparams > 0 ? nparams : 1));
   return L;
@@ -84,7 +84,7 @@ delta_status delta_diff(const uint16_t* old_bits, const uint16_t* new_bits, int6
     return fail(DELTA_E_WORKSPACE, "delta_diff: workspace %zu bytes, need %zu", ws_bytes,
                 L.total);
   sbd::DiffParam single{old_bits, new_bits, n, 0};
-  const int64_t tiles = (n + sbd::kDiffTile - 1) / sbd::kDiffTile;
+  const int64_t tiles = (n + sbd::kDiffTile - 1) / sbd::kDiffTile;  // < kMaxTiles for n < 2^31
   g_error.clear();
   return hip_status(sbd::launch_diff(nullptr, single, 1, tiles, idx, val, capacity, nnz, nullptr,
                                      ws, L, static_cast<hipStream_t>(stream)),
@@ -120,6 +120,9 @@ delta_status delta_diff_many(int32_t nparams, const uint16_t* const* old_ptrs,
   if (capacity > 0 && (idx == nullptr || val == nullptr))
     return fail(DELTA_E_INVALID, "delta_diff_many: null output with capacity=%lld",
                 (long long)capacity);
+  if (tiles >= sbd::kMaxTiles)
+    return fail(DELTA_E_RANGE, "delta_diff_many: %lld tiles exceed one launch (%lld)",
+                (long long)tiles, (long long)sbd::kMaxTiles);
   const sbd::WsLayout L = sbd::ws_layout(sbd::max_tiles_for(total, nparams), nparams);
   if (ws == nullptr || ws_bytes < L.total)
     return fail(DELTA_E_WORKSPACE, "delta_diff_many: workspace %zu bytes, need %zu", ws_bytes,

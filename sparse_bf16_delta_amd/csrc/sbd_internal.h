@@ -11,7 +11,7 @@ namespace sbd {
 // ---------------------------------------------------------------------------
 // Diff / compaction tiling.  One workgroup of 256 lanes (four wave64s) owns a
 // tile of kDiffIters * 256 * 8 elements: every lane issues kDiffIters 16-byte
-// loads per input, one wave covers 1 KB contiguous per load.  Tiles never
+// loads per input, one wave covering 1 KB contiguous per load.  Tiles never
 // straddle parameters.
 // ---------------------------------------------------------------------------
 constexpr int kDiffBlock = 256;
@@ -19,6 +19,9 @@ constexpr int kDiffWaves = kDiffBlock / 64;
 constexpr int kVec = 8;  // bf16 per 16-byte load
 constexpr int kDiffIters = 8;
 constexpr int64_t kDiffTile = int64_t(kDiffBlock) * kVec * kDiffIters;  // 16384
+// One workgroup per tile: the grid (tiles x 256 lanes) must stay below 2^32
+// work-items.  2^24 tiles are 2.7e11 elements, more than HBM holds twice.
+constexpr int64_t kMaxTiles = int64_t(1) << 24;
 
 // Parameter descriptor as stored in the workspace (32 bytes).
 struct DiffParam {
@@ -28,17 +31,30 @@ struct DiffParam {
   int64_t first_tile;
 };
 
+// Per-tile descriptor written by the prepare kernel (32 bytes).
+struct TileDesc {
+  const uint16_t* old_bits;  // first element of the tile
+  const uint16_t* new_bits;
+  int32_t e0;                // parameter-local index of that element
+  int32_t valid;             // elements of the tile inside the parameter
+  int64_t pad;
+};
+
+// A tile's compacted entries are staged in LDS (4 bytes each) when at most
+// this many elements changed; denser tiles are written directly.
+constexpr int kStageCap = 4096;
+
 struct SnapParam {
   uint16_t* snap;
   int64_t numel;
 };
 
-// Workspace layout: [header 256 B | tile state 8 B/tile | tile->param 4 B/tile
-// | parameter table 32 B/param].  All offsets are 256-byte aligned.
+// Workspace layout: [header 256 B | tile state 8 B/tile | tile descriptor
+// 32 B/tile | parameter table 32 B/param].  All offsets are 256-byte aligned.
 struct WsLayout {
-  size_t counter;     // uint32 dynamic tile counter
+  size_t flag;        // uint32 look-back timeout flag
   size_t state;       // uint64 per tile: status (2 bits) | count (62 bits)
-  size_t tile_param;  // int32 per tile
+  size_t tile_desc;   // TileDesc per tile
   size_t table;       // DiffParam / SnapParam per parameter
   size_t total;
 };
