@@ -77,8 +77,16 @@ size_t delta_workspace_size(int64_t total_elems, int32_t nparams);
  *  capacity            entries beyond `capacity` are never written.
  *  nnz                 device int64[1]: receives the TRUE number of changed
  *                      elements, even when it exceeds `capacity` -- the caller
- *                      then re-allocates and calls again.
+ *                      then re-allocates and calls again.  -1 on a scan
+ *                      failure (see below).
  *  ws, ws_bytes        workspace of at least delta_workspace_size(n, 1) bytes.
+ * Scan failure: the compaction computes every 16384-element tile's output
+ * offset in one pass, each tile waiting for the counts of the tiles before
+ * it.  Every such wait is bounded (about 2.7 s without progress).  If one
+ * ever expires -- it does not while the GPU makes progress on this kernel --
+ * no wrong delta is reported: nnz (and, for delta_diff_many, every nnz and
+ * offsets entry) reads -1 and idx/val are unspecified.  Treat a negative
+ * count as an error; calling again is safe.
  * Errors: DELTA_E_INVALID (null pointers, n < 0, capacity < 0),
  * DELTA_E_RANGE (n > 2^31-1), DELTA_E_WORKSPACE, DELTA_E_HIP.
  */
@@ -105,6 +113,7 @@ delta_status delta_diff(const uint16_t *old_bits, const uint16_t *new_bits, int6
  *  offsets             device int64[nparams+1]: exclusive running sum of nnz
  *                      (offsets[nparams] is the true total).  Parameter p's
  *                      entries are idx/val[offsets[p] .. offsets[p+1]).
+ *                      All -1 on a scan failure (see delta_diff).
  *  ws, ws_bytes        at least delta_workspace_size(sum(numels), nparams).
  * The parameter table (32 bytes per tensor) is copied host-to-device on
  * `stream`; HIP performs copies from pageable host memory synchronously, so

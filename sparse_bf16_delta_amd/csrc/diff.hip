@@ -181,7 +181,9 @@ __global__ __launch_bounds__(kDiffBlock) void diff_kernel(
     uint16_t* __restrict__ val, int64_t capacity, uint64_t* __restrict__ state,
     uint32_t* __restrict__ flag) {
   constexpr int kGroups = kDiffIters * kDiffWaves;
-  static_assert(kGroups <= 64, "groups must fit one wave");
+  constexpr int kPerLane = (kGroups + 63) / 64;
+  static_assert(kGroups <= 128, "groups must fit two per lane of one wave");
+  static_assert(kDiffTile <= 65536, "tile-local indices are staged in 16 bits");
   __shared__ uint32_t s_stage[kStageCap];  // (tile-local index << 16) | new bits
   __shared__ uint32_t s_wtot[kGroups];
   __shared__ uint32_t s_woff[kGroups];
@@ -248,14 +250,28 @@ __global__ __launch_bounds__(kDiffBlock) void diff_kernel(
 
   // ---- wave 0: group offsets in element order; publish the tile count ------
   if (wave == 0) {
-    const uint32_t v = lane < kGroups ? s_wtot[lane] : 0u;
-    uint32_t inc = v;
+    // lane l owns groups [l * kPerLane, (l + 1) * kPerLane)
+    uint32_t v[kPerLane];
+    uint32_t own = 0;
+#pragma unroll
+    for (int q = 0; q < kPerLane; ++q) {
+      const int g = lane * kPerLane + q;
+      v[q] = g < kGroups ? s_wtot[g] : 0u;
+      own += v[q];
+    }
+    uint32_t inc = own;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const uint32_t y = __shfl_up(inc, o, 64);
       if (lane >= o) inc += y;
     }
-    if (lane < kGroups) s_woff[lane] = inc - v;
+    uint32_t run = inc - own;
+#pragma unroll
+    for (int q = 0; q < kPerLane; ++q) {
+      const int g = lane * kPerLane + q;
+      if (g < kGroups) s_woff[g] = run;
+      run += v[q];
+    }
     const uint32_t agg = __shfl(inc, 63, 64);
     if (lane == 0) {
       s_agg = agg;
@@ -287,9 +303,15 @@ __global__ __launch_bounds__(kDiffBlock) void diff_kernel(
     }
   }
 
+  // ---- sparse tiles: waves 1-3 leave; wave 0 finishes alone ---------------
+  const bool solo = agg <= static_cast<uint32_t>(kSoloCap);
+  if (solo) {
+    __syncthreads();  // staging complete
+    if (wave != 0) return;
+  }
+  uint64_t excl = 0;
   // ---- wave 0: decoupled look-back over the preceding tiles ----------------
   if (wave == 0) {
-    uint64_t excl = 0;
     if (tile > 0) {
       int64_t hi = tile - 1;
       long long t_wait = -1;
@@ -322,14 +344,18 @@ __global__ __launch_bounds__(kDiffBlock) void diff_kernel(
     }
     if (lane == 0) s_excl = excl;
   }
-  __syncthreads();
+  if (!solo) {
+    __syncthreads();
+    excl = s_excl;
+  }
 
   // ---- emit ----------------------------------------------------------------
-  const uint64_t tbase = s_excl;
+  const uint64_t tbase = excl;
   const uint64_t cap = static_cast<uint64_t>(capacity);
   if (staged) {
     // coalesced copy of the staged entries
-    for (uint32_t p = static_cast<uint32_t>(tid); p < agg; p += kDiffBlock) {
+    const uint32_t step = solo ? 64u : uint32_t(kDiffBlock);
+    for (uint32_t p = static_cast<uint32_t>(solo ? lane : tid); p < agg; p += step) {
       const uint64_t o = tbase + p;
       if (o < cap) {
         const uint32_t w = s_stage[p];

@@ -14,7 +14,7 @@ namespace sbd {
 // loads per input, one wave covering 1 KB contiguous per load.  Tiles never
 // straddle parameters.
 // ---------------------------------------------------------------------------
-constexpr int kDiffBlock = 256;
+constexpr int kDiffBlock = 512;
 constexpr int kDiffWaves = kDiffBlock / 64;
 constexpr int kVec = 8;  // bf16 per 16-byte load
 constexpr int kDiffIters = 8;
@@ -43,6 +43,9 @@ struct TileDesc {
 // A tile's compacted entries are staged in LDS (4 bytes each) when at most
 // this many elements changed; denser tiles are written directly.
 constexpr int kStageCap = 4096;
+// Tiles with at most this many changes are finished by wave 0 alone (the
+// other waves leave early and free their registers for new workgroups).
+constexpr int kSoloCap = 1024;
 
 struct SnapParam {
   uint16_t* snap;

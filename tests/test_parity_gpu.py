@@ -14,9 +14,10 @@ import workloads
 
 pytestmark = pytest.mark.gpu
 
-TILE = 16384
-SIZES = [0, 1, 7, 8, 9, 63, 64, 65, 511, 512, 513, 2047, 2048, 2049, TILE - 1, TILE, TILE + 1,
-         2 * TILE + 3, 5 * TILE - 8, 100_003, 1 << 20]
+TILE = 32768  # elements per compaction tile (the sizes below also straddle 16K and 64K)
+SIZES = [0, 1, 7, 8, 9, 63, 64, 65, 511, 512, 513, 2047, 2048, 2049, 16383, 16385,
+         TILE - 1, TILE, TILE + 1, 2 * TILE + 3, 65535, 65537, 5 * TILE - 8, 100_003,
+         (1 << 20) + 5]
 FRACS = [0.0, 0.01, 0.5, 1.0]
 
 
