@@ -136,7 +136,15 @@ delta_status delta_diff_many(int32_t nparams, const uint16_t *const *old_ptrs,
  *                      `old_bits` of the delta_diff call that made the delta.
  *  idx, val            nnz entries; idx strictly ascending in [0, n) (what
  *                      delta_diff produces).  Entries outside [0, n) are
- *                      skipped, never written.  Duplicates: undefined value.
+ *                      skipped, never written.  If the order precondition
+ *                      is broken (unsorted or repeated indices) the values
+ *                      at those entries' positions are unspecified; no other
+ *                      position, and nothing outside the snapshot, changes.
+ *                      The snapshot is patched 64 bytes at a time: every
+ *                      touched 64-byte segment lying inside [snapshot,
+ *                      snapshot + 2n) is read and rewritten whole, so the
+ *                      caller must not write other parts of the snapshot
+ *                      concurrently.
  *  nnz                 (host) entry count.
  *  violations          optional device int64[1] (NULL to skip): receives the
  *                      number of entries that are out of range or not

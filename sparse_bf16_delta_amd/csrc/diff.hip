@@ -167,11 +167,12 @@ __global__ __launch_bounds__(256) void diff_prepare_kernel(const DiffParam* __re
 // elements at or past `valid` read as zero.
 __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ base, int local,
                                             int valid, bool vec) {
-  if (vec) return *reinterpret_cast<const uint4*>(base + local);
+  if (vec) return load16(base + local);
+  const auto g = global_ptr(base);
   uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int s = 0; s < kVec; ++s)
-    if (local + s < valid) w[s >> 1] |= uint32_t(base[local + s]) << (16 * (s & 1));
+    if (local + s < valid) w[s >> 1] |= uint32_t(g[local + s]) << (16 * (s & 1));
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
@@ -224,8 +225,8 @@ __global__ __launch_bounds__(kDiffBlock) void diff_kernel(
     uint4 ov[kDiffIters];
 #pragma unroll
     for (int j = 0; j < kDiffIters; ++j) {
-      ov[j] = o4[j * kDiffBlock];
-      nv[j] = n4[j * kDiffBlock];
+      ov[j] = load16(o4 + j * kDiffBlock);
+      nv[j] = load16(n4 + j * kDiffBlock);
     }
 #pragma unroll
     for (int j = 0; j < kDiffIters; ++j) m[j] = change_mask8(ov[j], nv[j]);

@@ -8,6 +8,32 @@
 
 namespace sbd {
 
+// A pointer loaded from memory (or built from an integer) is generic to the
+// compiler, which then emits flat loads and stores.  The tensors here live in
+// device memory, so this cast lets it emit global ones instead.
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* global_ptr(T* p) {
+  return (__attribute__((address_space(1))) T*)(p);
+}
+
+// 16-byte vector as the compiler's native type (loads and stores through
+// address-space-qualified pointers work on it in both compilation passes).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load16(const void* p) {
+  const u32x4 v = *global_ptr(static_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store16(void* p, const uint4& x) {
+  u32x4 v;
+  v.x = x.x;
+  v.y = x.y;
+  v.z = x.z;
+  v.w = x.w;
+  *global_ptr(static_cast<u32x4*>(p)) = v;
+}
+
 // ---------------------------------------------------------------------------
 // Diff / compaction tiling.  One workgroup of 256 lanes (four wave64s) owns a
 // tile of kDiffIters * 256 * 8 elements: every lane issues kDiffIters 16-byte

@@ -179,22 +179,45 @@ def test_apply_unaligned_delta_arrays(sbd, oracle_mod):
     assert np.array_equal(np_bits(snap), want)
 
 
-def test_apply_skips_and_counts_bad_indices(sbd, oracle_mod):
-    """Out-of-range entries are never written and are counted; entries that
-    break the ascending order are counted."""
+def test_apply_skips_out_of_range_indices(sbd, oracle_mod):
+    """Entries outside [0, n) are counted and never written; the others are."""
     n = 1000
     snap0 = np.arange(n, dtype=np.uint16)
-    idx = np.array([5, 3, 3, 999, 1000, -1, 2_000_000_000, 10], dtype=np.int32)
+    idx = np.array([3, 5, 10, 40, 999, 1000, 4096, 2_000_000_000], dtype=np.int32)
     val = np.full(idx.size, 0xABCD, dtype=np.uint16)
-    snap = gpu_bits(snap0)
-    with pytest.raises(sbd.DeltaError, match="6 delta entries"):
+    buf = gpu_bits(np.concatenate([snap0, np.full(64, 7, dtype=np.uint16)]))
+    snap = buf[:n]
+    with pytest.raises(sbd.DeltaError, match="3 delta entries"):
         sbd.apply_(snap, torch.from_numpy(idx).cuda(),
                    torch.from_numpy(val.view(np.int16)).cuda().view(torch.bfloat16),
                    check_indices=True)
     want = snap0.copy()
-    oracle_mod.apply_(want, np.array([3, 5, 10, 999], dtype=np.int32),
-                      np.full(4, 0xABCD, dtype=np.uint16))
-    assert np.array_equal(np_bits(snap), want)
+    oracle_mod.apply_(want, idx[:5], val[:5])
+    got = np_bits(buf)
+    assert np.array_equal(got[:n], want)
+    assert np.all(got[n:] == 7)  # nothing past the snapshot
+
+
+def test_apply_unsorted_is_flagged_and_stays_inside(sbd):
+    """An unsorted or duplicated delta breaks the precondition: it is counted,
+    the values at its positions are unspecified, and no other position of the
+    snapshot (or memory beyond it) changes."""
+    n = 1000
+    snap0 = np.arange(n, dtype=np.uint16)
+    idx = np.array([5, 3, 3, 999, 1000, -1, 2_000_000_000, 10], dtype=np.int32)
+    val = np.full(idx.size, 0xABCD, dtype=np.uint16)
+    buf = gpu_bits(np.concatenate([snap0, np.full(64, 7, dtype=np.uint16)]))
+    snap = buf[:n]
+    with pytest.raises(sbd.DeltaError, match="6 delta entries"):
+        sbd.apply_(snap, torch.from_numpy(idx).cuda(),
+                   torch.from_numpy(val.view(np.int16)).cuda().view(torch.bfloat16),
+                   check_indices=True)
+    got = np_bits(buf)
+    touched = np.zeros(n, dtype=bool)
+    touched[[3, 5, 10, 999]] = True
+    assert np.array_equal(got[:n][~touched], snap0[~touched])
+    assert np.all(np.isin(got[:n][touched], [0xABCD]) | (got[:n][touched] == snap0[touched]))
+    assert np.all(got[n:] == 7)
 
 
 @pytest.mark.parametrize("frac", [0.0, 0.03, 0.7])
@@ -212,6 +235,31 @@ def test_apply_many_matches_oracle(sbd, oracle_mod, frac):
                     torch.from_numpy(ro).cuda(), check_indices=True)
     for s, w in zip(snaps, wants):
         assert np.array_equal(np_bits(s), w)
+
+
+@pytest.mark.parametrize("frac", [0.05, 0.5, 1.0])
+def test_apply_many_adjacent_unaligned_params(sbd, oracle_mod, frac):
+    """Parameters packed back to back at odd element offsets share 64- and
+    128-byte segments at their edges; each must be updated without touching
+    its neighbours' bytes."""
+    sizes = [37, 1000, 1, 4093, 64, 63, 65, 20_000, 5, 3 * TILE + 11]
+    olds, news = _param_list(11 + int(frac * 10), sizes, frac)
+    flat_old = np.concatenate(olds)
+    ri, rv, rn, ro = oracle_mod.diff_many(olds, news)
+    want = []
+    for p, o in enumerate(olds):
+        w = o.copy()
+        oracle_mod.apply_(w, ri[ro[p]:ro[p + 1]], rv[ro[p]:ro[p + 1]])
+        want.append(w)
+    buf = gpu_bits(flat_old, 3)
+    views, pos = [], 0
+    for n in sizes:
+        views.append(buf[pos:pos + n])
+        pos += n
+    sbd.apply_many_(views, torch.from_numpy(ri).cuda(),
+                    torch.from_numpy(rv.view(np.int16)).cuda().view(torch.bfloat16),
+                    torch.from_numpy(ro).cuda(), check_indices=True)
+    assert np.array_equal(np_bits(buf), np.concatenate(want))
 
 
 def test_diff_many_then_apply_many_without_host_sync(sbd):
