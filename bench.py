@@ -27,6 +27,44 @@ import time
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 METRIC = "GB/s of bf16 weights diffed+compacted and applied; % of MI355X HBM peak"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "sparse_bf16_delta_amd", "csrc")
+# HBM bytes measured by rocprofv3 counters, per kernel, for the default
+# workload; valid only while the kernel sources hash to the recorded value.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llama7b_traffic.json")
+KERNEL_SOURCES = {
+    "delta_diff_many": ("diff.hip", "sbd_internal.h"),
+    "delta_apply_many": ("apply.hip", "sbd_internal.h"),
+    "xor_mask": ("xor.hip", "sbd_internal.h"),
+    "xor_apply": ("xor.hip", "sbd_internal.h"),
+}
+
+
+def source_hash(kernel):
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_key):
+    """{kernel: bytes per launch} from the committed counter summary, for the
+    kernels whose sources are unchanged since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    if rec.get("workload_key") != workload_key:
+        return {}
+    out = {}
+    for k, v in rec.get("kernels", {}).items():
+        if k in KERNEL_SOURCES and v.get("source_sha256") == source_hash(k):
+            out[k] = v.get("hbm_bytes_per_launch")
+    return out
 
 
 def log(*a):
@@ -182,19 +220,22 @@ def main():
         sys.exit(1)
 
     alg = [b_diff, b_apply, b_xor, b_xor]
+    workload_key = f"{cfg.key}:{mode}:{lr:g}"
+    traffic = measured_traffic(workload_key)
     kernels = []
     for name, ms, b in zip(names, op_ms, alg):
         gbs = b / (ms * 1e-3) / 1e9
         kernels.append({"kernel": name, "ms": round(ms, 4), "alg_bytes": b,
                         "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
-                        "weights_gbs": round(2 * n_model / (ms * 1e-3) / 1e9, 1)})
+                        "weights_gbs": round(2 * n_model / (ms * 1e-3) / 1e9, 1),
+                        "traffic": traffic.get(name)})
     for kk in kernels:
         log(f"[bench] {kk['kernel']:17s} {kk['ms']:8.3f} ms  {kk['achieved_gbs']:8.1f} GB/s "
             f"({100 * kk['frac']:.1f} % of peak)  weights {kk['weights_gbs']:.1f} GB/s")
     dom = max(range(4), key=lambda i: op_ms[i])
     roofline = {"bound": "hbm", "kernel": names[dom],
                 "achieved": kernels[dom]["achieved_gbs"], "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": kernels[dom]["frac"], "traffic": None}
+                "unit": "GB/s", "frac": kernels[dom]["frac"], "traffic": traffic.get(names[dom])}
 
     # copy ceiling on the same arenas (one snapshot read + one written)
     cs, ce = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -230,6 +271,7 @@ def main():
             "touched_lines_128B": lines128, "touched_lines_64B": lines64,
             "apply_alg_bytes_64B_lines": b_apply64,
             "step": "diff_many + apply_many + xor_mask + xor_apply",
+            "workload_key": workload_key,
         },
         "roofline": roofline,
         "kernels": kernels,
