@@ -52,8 +52,10 @@ typedef enum {
  * delta_diff_many and delta_apply_many need for a parameter list of
  * `nparams` tensors holding `total_elems` elements in all (an upper bound
  * that holds for any split of the elements).  Pure host function.
- * The workspace holds the per-tile scan state of the single-pass compaction
- * and the device copy of the parameter table; its contents on entry do not
+ * The workspace holds, per 32768-element tile of the compaction, its change
+ * count, its running offset, its descriptor and two staging slots (4 KB and
+ * 16 KB) for its compacted entries -- about 0.63 bytes per element -- plus
+ * the device copy of the parameter table.  Its contents on entry do not
  * matter and are clobbered.  Returns 0 for negative arguments.
  */
 size_t delta_workspace_size(int64_t total_elems, int32_t nparams);
@@ -77,16 +79,10 @@ size_t delta_workspace_size(int64_t total_elems, int32_t nparams);
  *  capacity            entries beyond `capacity` are never written.
  *  nnz                 device int64[1]: receives the TRUE number of changed
  *                      elements, even when it exceeds `capacity` -- the caller
- *                      then re-allocates and calls again.  -1 on a scan
- *                      failure (see below).
+ *                      then re-allocates and calls again.
  *  ws, ws_bytes        workspace of at least delta_workspace_size(n, 1) bytes.
- * Scan failure: the compaction computes every 16384-element tile's output
- * offset in one pass, each tile waiting for the counts of the tiles before
- * it.  Every such wait is bounded (about 2.7 s without progress).  If one
- * ever expires -- it does not while the GPU makes progress on this kernel --
- * no wrong delta is reported: nnz (and, for delta_diff_many, every nnz and
- * offsets entry) reads -1 and idx/val are unspecified.  Treat a negative
- * count as an error; calling again is safe.
+ * The work is five kernel launches on `stream` (count and stage, two scans,
+ * place, dense tiles); no workgroup waits for another.
  * Errors: DELTA_E_INVALID (null pointers, n < 0, capacity < 0),
  * DELTA_E_RANGE (n > 2^31-1), DELTA_E_WORKSPACE, DELTA_E_HIP.
  */
@@ -113,7 +109,6 @@ delta_status delta_diff(const uint16_t *old_bits, const uint16_t *new_bits, int6
  *  offsets             device int64[nparams+1]: exclusive running sum of nnz
  *                      (offsets[nparams] is the true total).  Parameter p's
  *                      entries are idx/val[offsets[p] .. offsets[p+1]).
- *                      All -1 on a scan failure (see delta_diff).
  *  ws, ws_bytes        at least delta_workspace_size(sum(numels), nparams).
  * The parameter table (32 bytes per tensor) is copied host-to-device on
  * `stream`; HIP performs copies from pageable host memory synchronously, so
@@ -140,11 +135,6 @@ delta_status delta_diff_many(int32_t nparams, const uint16_t *const *old_ptrs,
  *                      is broken (unsorted or repeated indices) the values
  *                      at those entries' positions are unspecified; no other
  *                      position, and nothing outside the snapshot, changes.
- *                      The snapshot is patched 64 bytes at a time: every
- *                      touched 64-byte segment lying inside [snapshot,
- *                      snapshot + 2n) is read and rewritten whole, so the
- *                      caller must not write other parts of the snapshot
- *                      concurrently.
  *  nnz                 (host) entry count.
  *  violations          optional device int64[1] (NULL to skip): receives the
  *                      number of entries that are out of range or not

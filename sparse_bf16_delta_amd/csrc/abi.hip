@@ -43,13 +43,21 @@ int64_t max_tiles_for(int64_t total_elems, int32_t nparams) {
 }
 
 WsLayout ws_layout(int64_t max_tiles, int32_t nparams) {
+  const size_t tiles = size_t(max_tiles);
+  const size_t chunks = (tiles + size_t(kScanChunk) - 1) / size_t(kScanChunk);
   WsLayout L;
-  L.flag = 0;
-  L.state = 256;
-  L.tile_desc = L.state + align256(sizeof(uint64_t) * size_t(max_tiles));
-  L.table = L.tile_desc + align256(sizeof(TileDesc) * size_t(max_tiles));
+  L.ndense = 0;
+  L.counts = 256;
+  L.inpfx = L.counts + align256(sizeof(uint32_t) * tiles);
+  L.chunk_tot = L.inpfx + align256(sizeof(uint32_t) * tiles);
+  L.chunk_base = L.chunk_tot + align256(sizeof(uint32_t) * chunks);
+  L.dense_list = L.chunk_base + align256(sizeof(uint64_t) * (chunks + 1));
+  L.tile_desc = L.dense_list + align256(sizeof(int32_t) * tiles);
+  L.table = L.tile_desc + align256(sizeof(TileDesc) * tiles);
   const size_t entry = sizeof(DiffParam) > sizeof(SnapParam) ? sizeof(DiffParam) : sizeof(SnapParam);
-  L.total = L.table + align256(entry * size_t(nparams > 0 ? nparams : 1));
+  L.compact = L.table + align256(entry * size_t(nparams > 0 ? nparams : 1));
+  L.wide = L.compact + sizeof(uint32_t) * size_t(kCompactWords) * tiles;
+  L.total = L.wide + sizeof(uint32_t) * size_t(kWideWords) * tiles;
   return L;
 }
 

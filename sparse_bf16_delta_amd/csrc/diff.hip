@@ -8,62 +8,55 @@
 // concatenates the parameters' outputs in list order with per-parameter
 // counts (same review, `gather_v_batched_to_rank0`).
 //
-// How, on gfx950:
-//  * Each workgroup (256 lanes = 4 wave64s) owns one tile of 16384 elements
-//    that never straddles a parameter.  A prepare kernel writes each tile's
-//    descriptor (base pointers, first index, length), so a workgroup does one
-//    uniform load before its data loads.  A lane issues eight 16-byte loads of
-//    `old` and eight of `new` up front (all in flight together); one wave
-//    covers 1 KB contiguous per load instruction.
-//  * Per 16-byte chunk the lane forms an 8-bit change mask; its popcount
-//    c in [0, 8] is prefix-summed across the wave with four ballots over the
-//    bits of c plus mbcnt (no shuffles), giving each lane its output slot.
-//  * Wave totals go through LDS; a 32-entry scan in wave 0 yields each
-//    (iteration, wave) group's offset inside the tile, in ascending element
-//    order (iteration-major, then wave, then lane, then slot), and the tile's
-//    count, which is published at once.
-//  * The compacted tile is staged in LDS as (tile-local index << 16 | bits),
-//    4 bytes per entry, up to 4096 entries (16 KB); after the look-back the
-//    workgroup copies it out with coalesced stores.  A denser tile skips the
-//    staging and writes directly, re-reading its changed 16-byte chunks of
-//    `new`, which it has just read and which are still cached.
-//  * Tile offsets come from a single-pass decoupled look-back scan.  Tile t
-//    is workgroup t: the dispatcher starts workgroups in increasing id order,
-//    so every tile a workgroup waits for has already started.  (A global
-//    atomic tile counter would guarantee that without relying on dispatch
-//    order, but one serialized atomic per tile cost a third of the kernel's
-//    time.)  Each tile publishes its count and then its inclusive prefix in
-//    one 64-bit word (2-bit status | 62-bit count) with agent-scope atomics,
-//    and wave 0 of a tile walks back 64 predecessors per step.  Only that
-//    word carries information between workgroups, so relaxed atomics
-//    suffice.
-//  * Every wait is bounded: a tile that sees no progress for about 2^28
-//    ticks of the constant-rate wall clock (about 2.7 s at 100 MHz) raises a
-//    flag in the workspace and stops waiting; the finalize kernel then
-//    reports -1 for every count instead of a wrong delta.
-//  * Registers hold one tile's data only until it is staged, and LDS holds
-//    16 KB per workgroup, so six workgroups share a CU.
-//  * `old` and `new` are read exactly once: the 4n-byte read plus the 6-byte
-//    write per changed element is the whole HBM traffic, apart from 40 bytes
-//    of scan state and descriptor per tile.
+// How, on gfx950: three phases in five short launches, and no workgroup ever
+// waits for another one.
+//  1. Count and stage.  One workgroup of 512 lanes (eight wave64s) per tile
+//     of 32768 elements; a tile never straddles a parameter.  A lane issues
+//     eight 16-byte loads of `old` and eight of `new` up front, so a CU keeps
+//     hundreds of KB of reads in flight.  Per 16-byte chunk the lane forms an
+//     8-bit change mask; its popcount is prefix-summed across the wave with
+//     four ballots over its bits plus mbcnt, and the 64 (iteration, wave)
+//     group totals are scanned in LDS, giving every change its slot inside
+//     the tile in ascending element order.  A tile with at most 4096 changes
+//     is compacted in LDS as (tile-local index << 16 | new bits) and copied
+//     with 16-byte nontemporal stores into a workspace slot of its own: a
+//     4 KB one for up to 1024 changes, else a 16 KB one.  (A sparse tile's
+//     entries then land close to the previous tile's: at a 16 KB stride the
+//     few KB each tile writes cost measurably more HBM time.)  A denser tile
+//     stores its 4 KB change mask instead.  The tile count goes to a per-tile
+//     array and the workgroup ends.
+//  2. Scan.  One workgroup per 4096 tiles scans their counts (prefix inside
+//     the chunk, chunk total) and lists the dense tiles; one workgroup scans
+//     the chunk totals and writes the per-parameter counts and offsets.
+//  3. Place.  One workgroup per 16 consecutive tiles copies their staged
+//     entries to the final position: consecutive tiles have consecutive
+//     outputs, so this is one contiguous run of coalesced idx and val
+//     stores.  Dense tiles are re-read (`new` only, steered by the stored
+//     mask) and written directly by a second, small grid.
+// Why not a single pass with a decoupled look-back: waiting for the
+// predecessors' prefix holds a workgroup's registers and LDS while its loads
+// are done, which keeps the next tile's loads from being issued; measured on
+// the 7B-shaped list it cost more than the 8 extra bytes per changed element
+// that the slot round trip adds here.
+// Traffic: the 4n-byte read happens once; a sparse tile adds 4 bytes written
+// and 4 read per changed element, a dense tile re-reads `new` (2 bytes per
+// element), and the tile count, prefix and descriptor add 40 bytes per tile.
 #include "sbd_internal.h"
 
 namespace sbd {
 namespace {
 
-constexpr uint64_t kFlagAgg = 1ull << 62;
-constexpr uint64_t kFlagPfx = 2ull << 62;
-constexpr uint64_t kCountMask = (1ull << 62) - 1;
-// Longest wait for predecessor tiles, in wall-clock ticks.
-constexpr long long kSpinTicks = 1ll << 28;
+constexpr int kGroups = kDiffIters * kDiffWaves;
+static_assert(kGroups <= 64, "one (iteration, wave) group per lane of a wave");
+static_assert(kDiffIters <= 8, "a lane's change mask is at most 8 bytes");
+static_assert(kDiffTile <= 65536, "tile-local indices are staged in 16 bits");
+static_assert(kStageCap % 4 == 0, "staged entries are copied four at a time");
+static_assert(kCompactWords * 4 >= kDiffBlock * 8, "a compact slot holds a tile's change mask");
+static_assert(kCompactCap % 4 == 0 && kCompactCap <= kStageCap, "slot tiers");
+static_assert(kScanChunk == kScanBlock * 4, "a scan lane takes four tiles");
+static_assert(kMaxTiles / kScanChunk <= kScanBlock * 4, "the chunk totals fit one workgroup");
 
-__device__ __forceinline__ uint64_t load_state(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void store_state(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
@@ -98,9 +91,14 @@ __device__ __forceinline__ uint32_t wave_prefix_c(uint32_t c, uint32_t& total) {
   return lanes_below(b0) + 2u * lanes_below(b1) + 4u * lanes_below(b2) + 8u * lanes_below(b3);
 }
 
-__device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
+// Inclusive prefix sum over the 64 lanes of a wave.
+template <typename T>
+__device__ __forceinline__ T wave_inclusive(T v, int lane) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  for (int o = 1; o < 64; o <<= 1) {
+    const T y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
   return v;
 }
 
@@ -126,43 +124,6 @@ __device__ __forceinline__ void stage_slot(uint32_t mm, uint32_t& pos, uint32_t 
   }
 }
 
-// Clears the scan state and the timeout flag; for a parameter list also
-// writes every tile's descriptor (base pointers, first index, length), so the
-// main kernel needs one load, not a parameter search, before its data loads.
-template <bool kMany>
-__global__ __launch_bounds__(256) void diff_prepare_kernel(const DiffParam* __restrict__ table,
-                                                           int32_t nparams, int64_t total_tiles,
-                                                           uint64_t* __restrict__ state,
-                                                           TileDesc* __restrict__ tdesc,
-                                                           uint32_t* __restrict__ flag) {
-  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; t < total_tiles; t += stride) {
-    state[t] = 0;
-    if constexpr (kMany) {
-      // largest p whose first tile is <= t (skips empty parameters)
-      int32_t lo = 0, hi = nparams - 1;
-      while (lo < hi) {
-        const int32_t mid = (lo + hi + 1) >> 1;
-        if (table[mid].first_tile <= t)
-          lo = mid;
-        else
-          hi = mid - 1;
-      }
-      const DiffParam d = table[lo];
-      const int64_t e0 = (t - d.first_tile) * kDiffTile;
-      const int64_t left = d.numel - e0;
-      TileDesc td;
-      td.old_bits = d.old_bits + e0;
-      td.new_bits = d.new_bits + e0;
-      td.e0 = static_cast<int32_t>(e0);
-      td.valid = static_cast<int32_t>(left < kDiffTile ? left : kDiffTile);
-      td.pad = 0;
-      tdesc[t] = td;
-    }
-  }
-  if (blockIdx.x == 0 && threadIdx.x == 0) *flag = 0u;
-}
-
 // 16 bytes (8 elements) of a tile starting at tile-local element `local`;
 // elements at or past `valid` read as zero.
 __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ base, int local,
@@ -176,57 +137,117 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ base, i
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+struct TileView {
+  const uint16_t* ob;
+  const uint16_t* nb;
+  int32_t e0;     // parameter-local index of the tile's first element
+  int32_t valid;  // elements of the tile inside the parameter
+};
+
 template <bool kMany>
-__global__ __launch_bounds__(kDiffBlock) void diff_kernel(
-    const TileDesc* __restrict__ tdesc, DiffParam single, int32_t* __restrict__ idx,
-    uint16_t* __restrict__ val, int64_t capacity, uint64_t* __restrict__ state,
-    uint32_t* __restrict__ flag) {
-  constexpr int kGroups = kDiffIters * kDiffWaves;
-  constexpr int kPerLane = (kGroups + 63) / 64;
-  static_assert(kGroups <= 128, "groups must fit two per lane of one wave");
-  static_assert(kDiffTile <= 65536, "tile-local indices are staged in 16 bits");
-  __shared__ uint32_t s_stage[kStageCap];  // (tile-local index << 16) | new bits
+__device__ __forceinline__ TileView tile_view(const TileDesc* __restrict__ tdesc,
+                                              const DiffParam& single, int64_t t) {
+  TileView v;
+  if constexpr (kMany) {
+    const TileDesc td = tdesc[t];
+    v.ob = td.old_bits;
+    v.nb = td.new_bits;
+    v.e0 = td.e0;
+    v.valid = td.valid;
+  } else {
+    const int64_t first = t * kDiffTile;
+    const int64_t left = single.numel - first;
+    v.ob = single.old_bits + first;
+    v.nb = single.new_bits + first;
+    v.e0 = static_cast<int32_t>(first);
+    v.valid = static_cast<int32_t>(left < kDiffTile ? left : kDiffTile);
+  }
+  return v;
+}
+
+// From the lanes' change masks: each lane's offset inside its (iteration,
+// wave) group (lp), each group's offset inside the tile in ascending element
+// order -- iteration-major, then wave, then lane, then slot -- (goff), and the
+// tile's count (agg), in every lane.  Contains one barrier; s_wtot must not
+// be in use by other waves.
+__device__ __forceinline__ void tile_offsets(const uint32_t (&m)[kDiffIters],
+                                             uint32_t (&lp)[kDiffIters],
+                                             uint32_t (&goff)[kDiffIters], uint32_t& agg,
+                                             uint32_t* s_wtot, int lane, int wave) {
+#pragma unroll
+  for (int j = 0; j < kDiffIters; ++j) {
+    uint32_t tot;
+    lp[j] = wave_prefix_c(static_cast<uint32_t>(__popc(m[j])), tot);
+    if (lane == 0) s_wtot[j * kDiffWaves + wave] = tot;
+  }
+  __syncthreads();
+  // every wave scans the 64 group totals itself: no second barrier
+  const uint32_t own = lane < kGroups ? s_wtot[lane] : 0u;
+  const uint32_t inc = wave_inclusive(own, lane);
+  const uint32_t excl = inc - own;
+  agg = static_cast<uint32_t>(__shfl(static_cast<int>(inc), 63, 64));
+#pragma unroll
+  for (int j = 0; j < kDiffIters; ++j)
+    goff[j] = static_cast<uint32_t>(__shfl(static_cast<int>(excl), j * kDiffWaves + wave, 64));
+}
+
+// For a parameter list: every tile's descriptor (base pointers, first index,
+// length), so a workgroup needs one load, not a parameter search, before its
+// data loads.
+__global__ __launch_bounds__(256) void diff_prepare_kernel(const DiffParam* __restrict__ table,
+                                                           int32_t nparams, int64_t total_tiles,
+                                                           TileDesc* __restrict__ tdesc) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; t < total_tiles; t += stride) {
+    // largest p whose first tile is <= t (skips empty parameters)
+    int32_t lo = 0, hi = nparams - 1;
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if (table[mid].first_tile <= t)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const DiffParam d = table[lo];
+    const int64_t e0 = (t - d.first_tile) * kDiffTile;
+    const int64_t left = d.numel - e0;
+    TileDesc td;
+    td.old_bits = d.old_bits + e0;
+    td.new_bits = d.new_bits + e0;
+    td.e0 = static_cast<int32_t>(e0);
+    td.valid = static_cast<int32_t>(left < kDiffTile ? left : kDiffTile);
+    td.pad = 0;
+    tdesc[t] = td;
+  }
+}
+
+// Phase 1: count the tile's changes; stage sparse tiles, record dense ones.
+template <bool kMany>
+__global__ __launch_bounds__(kDiffBlock) void diff_count_kernel(
+    const TileDesc* __restrict__ tdesc, DiffParam single, uint32_t* __restrict__ counts,
+    uint32_t* __restrict__ compact, uint32_t* __restrict__ wide, uint32_t* __restrict__ ndense) {
+  __shared__ __attribute__((aligned(16))) uint32_t s_stage[kStageCap];
   __shared__ uint32_t s_wtot[kGroups];
-  __shared__ uint32_t s_woff[kGroups];
-  __shared__ uint32_t s_agg;
-  __shared__ uint64_t s_excl;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t tile = blockIdx.x;
+  const TileView tv = tile_view<kMany>(tdesc, single, tile);
+  const bool vec = tv.valid == kDiffTile &&
+                   ((reinterpret_cast<uintptr_t>(tv.ob) | reinterpret_cast<uintptr_t>(tv.nb)) &
+                    15u) == 0;
 
-  const uint16_t* ob;
-  const uint16_t* nb;
-  int32_t e0, valid;
-  if constexpr (kMany) {
-    const TileDesc td = tdesc[tile];
-    ob = td.old_bits;
-    nb = td.new_bits;
-    e0 = td.e0;
-    valid = td.valid;
-  } else {
-    const int64_t first = tile * kDiffTile;
-    const int64_t left = single.numel - first;
-    ob = single.old_bits + first;
-    nb = single.new_bits + first;
-    e0 = static_cast<int32_t>(first);
-    valid = static_cast<int32_t>(left < kDiffTile ? left : kDiffTile);
-  }
-  const bool vec = valid == kDiffTile &&
-                   ((reinterpret_cast<uintptr_t>(ob) | reinterpret_cast<uintptr_t>(nb)) & 15u) == 0;
-
-  // ---- load, compare, count ------------------------------------------------
   uint4 nv[kDiffIters];
   uint32_t m[kDiffIters];
   if (vec) {
-    const uint4* o4 = reinterpret_cast<const uint4*>(ob) + tid;
-    const uint4* n4 = reinterpret_cast<const uint4*>(nb) + tid;
+    const uint4* o4 = reinterpret_cast<const uint4*>(tv.ob) + tid;
+    const uint4* n4 = reinterpret_cast<const uint4*>(tv.nb) + tid;
     uint4 ov[kDiffIters];
 #pragma unroll
     for (int j = 0; j < kDiffIters; ++j) {
-      ov[j] = load16(o4 + j * kDiffBlock);
-      nv[j] = load16(n4 + j * kDiffBlock);
+      ov[j] = load16_stream(o4 + j * kDiffBlock);
+      nv[j] = load16_stream(n4 + j * kDiffBlock);
     }
 #pragma unroll
     for (int j = 0; j < kDiffIters; ++j) m[j] = change_mask8(ov[j], nv[j]);
@@ -235,61 +256,24 @@ __global__ __launch_bounds__(kDiffBlock) void diff_kernel(
 #pragma unroll
     for (int j = 0; j < kDiffIters; ++j) {
       const int local = j * kDiffBlock * kVec + tid * kVec;
-      const uint4 o = load_chunk(ob, local, valid, false);
-      nv[j] = load_chunk(nb, local, valid, false);
+      const uint4 o = load_chunk(tv.ob, local, tv.valid, false);
+      nv[j] = load_chunk(tv.nb, local, tv.valid, false);
       m[j] = change_mask8(o, nv[j]);
     }
   }
-  uint32_t lp[kDiffIters];
-#pragma unroll
-  for (int j = 0; j < kDiffIters; ++j) {
-    uint32_t tot;
-    lp[j] = wave_prefix_c(static_cast<uint32_t>(__popc(m[j])), tot);
-    if (lane == 0) s_wtot[j * kDiffWaves + wave] = tot;
-  }
-  __syncthreads();
 
-  // ---- wave 0: group offsets in element order; publish the tile count ------
-  if (wave == 0) {
-    // lane l owns groups [l * kPerLane, (l + 1) * kPerLane)
-    uint32_t v[kPerLane];
-    uint32_t own = 0;
-#pragma unroll
-    for (int q = 0; q < kPerLane; ++q) {
-      const int g = lane * kPerLane + q;
-      v[q] = g < kGroups ? s_wtot[g] : 0u;
-      own += v[q];
-    }
-    uint32_t inc = own;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += y;
-    }
-    uint32_t run = inc - own;
-#pragma unroll
-    for (int q = 0; q < kPerLane; ++q) {
-      const int g = lane * kPerLane + q;
-      if (g < kGroups) s_woff[g] = run;
-      run += v[q];
-    }
-    const uint32_t agg = __shfl(inc, 63, 64);
-    if (lane == 0) {
-      s_agg = agg;
-      store_state(&state[tile], (tile == 0 ? kFlagPfx : kFlagAgg) | agg);
-    }
+  uint32_t lp[kDiffIters], goff[kDiffIters], agg;
+  tile_offsets(m, lp, goff, agg, s_wtot, lane, wave);
+  if (tid == 0) {
+    counts[tile] = agg;
+    if (tile == 0) *ndense = 0u;  // the scan kernel, launched next, lists dense tiles
   }
-  __syncthreads();
-
-  // ---- stage the compacted tile in LDS (when it fits) ----------------------
-  const uint32_t agg = s_agg;
-  const bool staged = agg <= static_cast<uint32_t>(kStageCap);
-  if (staged) {
+  if (agg <= static_cast<uint32_t>(kStageCap)) {
 #pragma unroll
     for (int j = 0; j < kDiffIters; ++j) {
       const uint32_t mm = m[j];
       if (mm != 0u) {
-        uint32_t pos = s_woff[j * kDiffWaves + wave] + lp[j];
+        uint32_t pos = goff[j] + lp[j];
         const uint32_t local = static_cast<uint32_t>(j * kDiffBlock * kVec + tid * kVec);
         const uint4 x = nv[j];
         stage_slot<0>(mm, pos, local, x, s_stage);
@@ -302,78 +286,202 @@ __global__ __launch_bounds__(kDiffBlock) void diff_kernel(
         stage_slot<7>(mm, pos, local, x, s_stage);
       }
     }
-  }
-
-  // ---- sparse tiles: waves 1-3 leave; wave 0 finishes alone ---------------
-  const bool solo = agg <= static_cast<uint32_t>(kSoloCap);
-  if (solo) {
-    __syncthreads();  // staging complete
-    if (wave != 0) return;
-  }
-  uint64_t excl = 0;
-  // ---- wave 0: decoupled look-back over the preceding tiles ----------------
-  if (wave == 0) {
-    if (tile > 0) {
-      int64_t hi = tile - 1;
-      long long t_wait = -1;
-      for (;;) {
-        const int64_t t = hi - lane;
-        const uint64_t f = t >= 0 ? load_state(&state[t]) : kFlagPfx;
-        const uint64_t pfx = __ballot((f >> 62) == 2u);
-        const uint64_t inv = __ballot((f >> 62) == 0u);
-        // lanes up to and including the nearest published prefix
-        const uint64_t upto = pfx ? (((pfx & (~pfx + 1ull)) << 1) - 1ull) : ~0ull;
-        if (inv & upto) {
-          const long long now = wall_clock64();
-          if (t_wait < 0) {
-            t_wait = now;
-          } else if (now - t_wait > kSpinTicks ||
-                     __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-            if (lane == 0)
-              __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;  // give up: the counts are reported as failed
-          }
-          __builtin_amdgcn_s_sleep(1);
-          continue;
-        }
-        t_wait = -1;
-        excl += wave_sum64(((upto >> lane) & 1ull) ? (f & kCountMask) : 0ull);
-        if (pfx) break;
-        hi -= 64;
-      }
-      if (lane == 0) store_state(&state[tile], kFlagPfx | (excl + agg));
-    }
-    if (lane == 0) s_excl = excl;
-  }
-  if (!solo) {
     __syncthreads();
-    excl = s_excl;
-  }
-
-  // ---- emit ----------------------------------------------------------------
-  const uint64_t tbase = excl;
-  const uint64_t cap = static_cast<uint64_t>(capacity);
-  if (staged) {
-    // coalesced copy of the staged entries
-    const uint32_t step = solo ? 64u : uint32_t(kDiffBlock);
-    for (uint32_t p = static_cast<uint32_t>(solo ? lane : tid); p < agg; p += step) {
-      const uint64_t o = tbase + p;
-      if (o < cap) {
-        const uint32_t w = s_stage[p];
-        idx[o] = e0 + static_cast<int32_t>(w >> 16);
-        val[o] = static_cast<uint16_t>(w & 0xFFFFu);
-      }
+    // 16-byte copies with the nontemporal hint (the slot is read once, by the
+    // placing kernel); the last one may carry up to three stale LDS words
+    // past `agg`, which stay inside the slot and are never read.
+    uint32_t* slot = agg <= static_cast<uint32_t>(kCompactCap) ? compact + tile * kCompactWords
+                                                               : wide + tile * kWideWords;
+    for (uint32_t p = static_cast<uint32_t>(tid) * 4u; p < agg; p += kDiffBlock * 4u) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(&s_stage[p]);
+      __builtin_nontemporal_store(w, global_ptr(reinterpret_cast<u32x4*>(slot + p)));
     }
   } else {
-    // dense tile: re-read the changed chunks of `new` (just read, so cached)
+    // dense: the change mask, one byte per 16-byte chunk, 8 bytes per lane
+    u32x2 w;
+    w.x = 0u;
+    w.y = 0u;
+#pragma unroll
+    for (int j = 0; j < kDiffIters; ++j) {
+      if (j < 4)
+        w.x |= m[j] << (8 * j);
+      else
+        w.y |= m[j] << (8 * (j - 4));
+    }
+    *global_ptr(reinterpret_cast<u32x2*>(compact + tile * kCompactWords) + tid) = w;
+  }
+}
+
+// Phase 2a: per chunk of kScanChunk tiles, each tile's exclusive prefix
+// inside the chunk and the chunk total; dense tiles are appended to a list
+// (in no particular order).
+__global__ __launch_bounds__(kScanBlock) void diff_scan_chunks_kernel(
+    const uint32_t* __restrict__ counts, int64_t total_tiles, uint32_t* __restrict__ inpfx,
+    uint32_t* __restrict__ chunk_tot, int32_t* __restrict__ dense_list,
+    uint32_t* __restrict__ ndense) {
+  __shared__ uint32_t s_w[kScanBlock / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t t0 = int64_t(blockIdx.x) * kScanChunk + int64_t(tid) * 4;
+  uint32_t v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t t = t0 + q;
+    v[q] = t < total_tiles ? counts[t] : 0u;
+    if (v[q] > static_cast<uint32_t>(kStageCap)) dense_list[atomicAdd(ndense, 1u)] = int32_t(t);
+  }
+  const uint32_t own = v[0] + v[1] + v[2] + v[3];
+  const uint32_t inc = wave_inclusive(own, lane);
+  if (lane == 63) s_w[wave] = inc;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int w = 0; w < wave; ++w) base += s_w[w];
+  uint32_t run = base + inc - own;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (t0 + q < total_tiles) inpfx[t0 + q] = run;
+    run += v[q];
+  }
+  if (tid == kScanBlock - 1) chunk_tot[blockIdx.x] = base + inc;
+}
+
+// Phase 2b: chunk bases (chunk_base[nchunks] = total) and the per-parameter
+// counts and offsets.
+template <bool kMany>
+__global__ __launch_bounds__(kScanBlock) void diff_base_kernel(
+    const DiffParam* __restrict__ table, int32_t nparams, int64_t total_tiles, int32_t nchunks,
+    const uint32_t* __restrict__ inpfx, const uint32_t* __restrict__ chunk_tot,
+    uint64_t* __restrict__ chunk_base, int64_t* __restrict__ nnz, int64_t* __restrict__ offsets) {
+  __shared__ uint64_t s_base[kMaxTiles / kScanChunk + 1];
+  __shared__ uint64_t s_w[kScanBlock / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c0 = tid * 4;
+  uint64_t v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = c0 + q < nchunks ? chunk_tot[c0 + q] : 0u;
+  const uint64_t own = v[0] + v[1] + v[2] + v[3];
+  const uint64_t inc = wave_inclusive(own, lane);
+  if (lane == 63) s_w[wave] = inc;
+  __syncthreads();
+  uint64_t base = 0;
+  for (int w = 0; w < wave; ++w) base += s_w[w];
+  uint64_t run = base + inc - own;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (c0 + q < nchunks) {
+      s_base[c0 + q] = run;
+      chunk_base[c0 + q] = run;
+    }
+    run += v[q];
+  }
+  if (tid == kScanBlock - 1) {
+    s_base[nchunks] = base + inc;
+    chunk_base[nchunks] = base + inc;
+  }
+  __syncthreads();
+  auto start = [&](int64_t ft) -> uint64_t {
+    return ft < total_tiles ? s_base[ft / kScanChunk] + inpfx[ft] : s_base[nchunks];
+  };
+  for (int64_t p = tid; p <= nparams; p += kScanBlock) {
+    const int64_t ft = p < nparams ? (kMany ? table[p].first_tile : 0) : total_tiles;
+    const uint64_t off = start(ft);
+    if (offsets) offsets[p] = static_cast<int64_t>(off);
+    if (p < nparams) {
+      const int64_t ft_next = (kMany && p + 1 < nparams) ? table[p + 1].first_tile : total_tiles;
+      nnz[p] = static_cast<int64_t>(start(ft_next) - off);
+    }
+  }
+}
+
+// Phase 3a: copy the staged entries of kPlaceTiles consecutive tiles, which
+// form one contiguous output run, to their final positions.
+template <bool kMany>
+__global__ __launch_bounds__(kDiffBlock) void diff_place_kernel(
+    const TileDesc* __restrict__ tdesc, int64_t total_tiles, int32_t nchunks,
+    const uint32_t* __restrict__ inpfx, const uint64_t* __restrict__ chunk_base,
+    const uint32_t* __restrict__ compact, const uint32_t* __restrict__ wide,
+    int32_t* __restrict__ idx, uint16_t* __restrict__ val, int64_t capacity) {
+  constexpr int kUnroll = 4;
+  __shared__ uint64_t s_off[kPlaceTiles + 1];
+  __shared__ int32_t s_e0[kPlaceTiles];
+  const int tid = threadIdx.x;
+  const int64_t t0 = int64_t(blockIdx.x) * kPlaceTiles;
+  const int64_t left = total_tiles - t0;
+  const int nt = static_cast<int>(left < kPlaceTiles ? left : kPlaceTiles);
+  if (tid <= nt) {
+    const int64_t t = t0 + tid;
+    s_off[tid] = t < total_tiles ? chunk_base[t / kScanChunk] + inpfx[t] : chunk_base[nchunks];
+    if (tid < nt) s_e0[tid] = kMany ? tdesc[t].e0 : static_cast<int32_t>(t * kDiffTile);
+  }
+  __syncthreads();
+  const uint64_t cap = static_cast<uint64_t>(capacity);
+  const uint64_t hi = s_off[nt] < cap ? s_off[nt] : cap;
+  int k = 0;  // tile of the current output position; only moves forward
+  for (uint64_t jb = s_off[0] + tid; jb < hi; jb += kUnroll * kDiffBlock) {
+    uint32_t w[kUnroll];
+    int kk[kUnroll];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint64_t j = jb + uint64_t(u) * kDiffBlock;
+      ok[u] = j < hi;
+      if (ok[u]) {
+        while (s_off[k + 1] <= j) ++k;  // stops below nt because j < s_off[nt]
+        kk[u] = k;
+        const uint64_t c = s_off[k + 1] - s_off[k];
+        ok[u] = c <= static_cast<uint64_t>(kStageCap);  // else dense: written by diff_dense_kernel
+        const uint32_t* slot = c <= static_cast<uint64_t>(kCompactCap)
+                                   ? compact + (t0 + k) * kCompactWords
+                                   : wide + (t0 + k) * kWideWords;
+        if (ok[u]) w[u] = *global_ptr(slot + (j - s_off[k]));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (ok[u]) {
+        const uint64_t j = jb + uint64_t(u) * kDiffBlock;
+        idx[j] = s_e0[kk[u]] + static_cast<int32_t>(w[u] >> 16);
+        val[j] = static_cast<uint16_t>(w[u] & 0xFFFFu);
+      }
+    }
+  }
+}
+
+// Phase 3b: dense tiles, from their change masks and a second read of `new`.
+template <bool kMany>
+__global__ __launch_bounds__(kDiffBlock) void diff_dense_kernel(
+    const TileDesc* __restrict__ tdesc, DiffParam single, const int32_t* __restrict__ dense_list,
+    const uint32_t* __restrict__ ndense, const uint32_t* __restrict__ inpfx,
+    const uint64_t* __restrict__ chunk_base, const uint32_t* __restrict__ compact,
+    int32_t* __restrict__ idx, uint16_t* __restrict__ val, int64_t capacity) {
+  __shared__ uint32_t s_wtot[kGroups];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const uint64_t cap = static_cast<uint64_t>(capacity);
+  const uint32_t nd = *ndense;
+  for (uint32_t i = blockIdx.x; i < nd; i += gridDim.x) {
+    const int64_t t = dense_list[i];
+    const TileView tv = tile_view<kMany>(tdesc, single, t);
+    const bool vec = tv.valid == kDiffTile && (reinterpret_cast<uintptr_t>(tv.nb) & 15u) == 0;
+    const u32x2 mw = *global_ptr(reinterpret_cast<const u32x2*>(compact + t * kCompactWords) + tid);
+    uint32_t m[kDiffIters];
+#pragma unroll
+    for (int j = 0; j < kDiffIters; ++j) m[j] = ((j < 4 ? mw.x : mw.y) >> (8 * (j & 3))) & 0xFFu;
+    uint32_t lp[kDiffIters], goff[kDiffIters], agg;
+    tile_offsets(m, lp, goff, agg, s_wtot, lane, wave);
+    const uint64_t tbase = chunk_base[t / kScanChunk] + inpfx[t];
 #pragma unroll
     for (int j = 0; j < kDiffIters; ++j) {
       const uint32_t mm = m[j];
       if (mm != 0u) {
-        uint64_t pos = tbase + s_woff[j * kDiffWaves + wave] + lp[j];
+        uint64_t pos = tbase + goff[j] + lp[j];
         const int local = j * kDiffBlock * kVec + tid * kVec;
-        const uint4 x = load_chunk(nb, local, valid, vec);
-        const int64_t ebase = int64_t(e0) + local;
+        const uint4 x = load_chunk(tv.nb, local, tv.valid, vec);
+        const int64_t ebase = int64_t(tv.e0) + local;
         emit_slot<0>(mm, pos, ebase, x, idx, val, cap);
         emit_slot<1>(mm, pos, ebase, x, idx, val, cap);
         emit_slot<2>(mm, pos, ebase, x, idx, val, cap);
@@ -384,34 +492,7 @@ __global__ __launch_bounds__(kDiffBlock) void diff_kernel(
         emit_slot<7>(mm, pos, ebase, x, idx, val, cap);
       }
     }
-  }
-}
-
-// Per-parameter counts and offsets from the tiles' inclusive prefixes.
-template <bool kMany>
-__global__ __launch_bounds__(256) void diff_finalize_kernel(const DiffParam* __restrict__ table,
-                                                            int32_t nparams, int64_t total_tiles,
-                                                            const uint64_t* __restrict__ state,
-                                                            const uint32_t* __restrict__ flag,
-                                                            int64_t* __restrict__ nnz,
-                                                            int64_t* __restrict__ offsets) {
-  const int64_t p = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (p > nparams) return;
-  if (*flag != 0u) {  // a look-back wait timed out: no count is trustworthy
-    if (offsets) offsets[p] = -1;
-    if (p < nparams) nnz[p] = -1;
-    return;
-  }
-  auto before = [&](int64_t ft) -> int64_t {
-    return ft == 0 ? 0 : static_cast<int64_t>(state[ft - 1] & kCountMask);
-  };
-  int64_t ft = total_tiles;
-  if (p < nparams) ft = kMany ? table[p].first_tile : 0;
-  const int64_t off = before(ft);
-  if (offsets) offsets[p] = off;
-  if (p < nparams) {
-    const int64_t ft_next = (kMany && p + 1 < nparams) ? table[p + 1].first_tile : total_tiles;
-    nnz[p] = before(ft_next) - off;
+    __syncthreads();  // s_wtot is rewritten for the next tile
   }
 }
 
@@ -422,40 +503,58 @@ hipError_t launch_diff(const DiffParam* d_table, const DiffParam& single, int32_
                        int64_t* nnz, int64_t* offsets, void* ws, const WsLayout& L,
                        hipStream_t stream) {
   char* base = static_cast<char*>(ws);
-  uint32_t* flag = reinterpret_cast<uint32_t*>(base + L.flag);
-  uint64_t* state = reinterpret_cast<uint64_t*>(base + L.state);
+  uint32_t* ndense = reinterpret_cast<uint32_t*>(base + L.ndense);
+  uint32_t* counts = reinterpret_cast<uint32_t*>(base + L.counts);
+  uint32_t* inpfx = reinterpret_cast<uint32_t*>(base + L.inpfx);
+  uint32_t* chunk_tot = reinterpret_cast<uint32_t*>(base + L.chunk_tot);
+  uint64_t* chunk_base = reinterpret_cast<uint64_t*>(base + L.chunk_base);
+  int32_t* dense_list = reinterpret_cast<int32_t*>(base + L.dense_list);
   TileDesc* tdesc = reinterpret_cast<TileDesc*>(base + L.tile_desc);
+  uint32_t* compact = reinterpret_cast<uint32_t*>(base + L.compact);
+  uint32_t* wide = reinterpret_cast<uint32_t*>(base + L.wide);
   // d_table == nullptr: one tensor (nparams == 1, `single`) or an empty list
   // (nparams == 0, no tiles).
   const bool many = d_table != nullptr;
-
-  int64_t prep_blocks = (total_tiles + 255) / 256;
-  if (prep_blocks < 1) prep_blocks = 1;
-  if (prep_blocks > 65536) prep_blocks = 65536;
-  if (many)
-    diff_prepare_kernel<true><<<dim3(unsigned(prep_blocks)), dim3(256), 0, stream>>>(
-        d_table, nparams, total_tiles, state, tdesc, flag);
-  else
-    diff_prepare_kernel<false><<<dim3(unsigned(prep_blocks)), dim3(256), 0, stream>>>(
-        nullptr, nparams, total_tiles, state, tdesc, flag);
+  const int32_t nchunks = static_cast<int32_t>((total_tiles + kScanChunk - 1) / kScanChunk);
+  const unsigned grid = static_cast<unsigned>(total_tiles);  // total_tiles < kMaxTiles
 
   if (total_tiles > 0) {
-    // one workgroup per tile, in tile order (total_tiles <= kMaxTiles)
-    if (many)
-      diff_kernel<true><<<dim3(unsigned(total_tiles)), dim3(kDiffBlock), 0, stream>>>(
-          tdesc, single, idx, val, capacity, state, flag);
-    else
-      diff_kernel<false><<<dim3(unsigned(total_tiles)), dim3(kDiffBlock), 0, stream>>>(
-          nullptr, single, idx, val, capacity, state, flag);
+    if (many) {
+      int64_t prep_blocks = (total_tiles + 255) / 256;
+      if (prep_blocks > 65536) prep_blocks = 65536;
+      diff_prepare_kernel<<<dim3(unsigned(prep_blocks)), dim3(256), 0, stream>>>(
+          d_table, nparams, total_tiles, tdesc);
+      diff_count_kernel<true><<<dim3(grid), dim3(kDiffBlock), 0, stream>>>(tdesc, single, counts,
+                                                                           compact, wide, ndense);
+    } else {
+      diff_count_kernel<false><<<dim3(grid), dim3(kDiffBlock), 0, stream>>>(nullptr, single,
+                                                                            counts, compact, wide, ndense);
+    }
+    diff_scan_chunks_kernel<<<dim3(unsigned(nchunks)), dim3(kScanBlock), 0, stream>>>(
+        counts, total_tiles, inpfx, chunk_tot, dense_list, ndense);
   }
-
-  const int64_t fin_blocks = (int64_t(nparams) + 1 + 255) / 256;
   if (many)
-    diff_finalize_kernel<true><<<dim3(unsigned(fin_blocks)), dim3(256), 0, stream>>>(
-        d_table, nparams, total_tiles, state, flag, nnz, offsets);
+    diff_base_kernel<true><<<dim3(1), dim3(kScanBlock), 0, stream>>>(
+        d_table, nparams, total_tiles, nchunks, inpfx, chunk_tot, chunk_base, nnz, offsets);
   else
-    diff_finalize_kernel<false><<<dim3(unsigned(fin_blocks)), dim3(256), 0, stream>>>(
-        nullptr, nparams, total_tiles, state, flag, nnz, offsets);
+    diff_base_kernel<false><<<dim3(1), dim3(kScanBlock), 0, stream>>>(
+        nullptr, nparams, total_tiles, nchunks, inpfx, chunk_tot, chunk_base, nnz, offsets);
+  if (total_tiles > 0) {
+    const unsigned place_grid = static_cast<unsigned>((total_tiles + kPlaceTiles - 1) / kPlaceTiles);
+    const unsigned dense_grid =
+        static_cast<unsigned>(total_tiles < kDenseGrid ? total_tiles : kDenseGrid);
+    if (many) {
+      diff_place_kernel<true><<<dim3(place_grid), dim3(kDiffBlock), 0, stream>>>(
+          tdesc, total_tiles, nchunks, inpfx, chunk_base, compact, wide, idx, val, capacity);
+      diff_dense_kernel<true><<<dim3(dense_grid), dim3(kDiffBlock), 0, stream>>>(
+          tdesc, single, dense_list, ndense, inpfx, chunk_base, compact, idx, val, capacity);
+    } else {
+      diff_place_kernel<false><<<dim3(place_grid), dim3(kDiffBlock), 0, stream>>>(
+          nullptr, total_tiles, nchunks, inpfx, chunk_base, compact, wide, idx, val, capacity);
+      diff_dense_kernel<false><<<dim3(dense_grid), dim3(kDiffBlock), 0, stream>>>(
+          nullptr, single, dense_list, ndense, inpfx, chunk_base, compact, idx, val, capacity);
+    }
+  }
   return hipGetLastError();
 }
 

@@ -25,6 +25,12 @@ __device__ __forceinline__ uint4 load16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// The same, with the nontemporal hint: for data read exactly once.
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(global_ptr(static_cast<const u32x4*>(p)));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ void store16(void* p, const uint4& x) {
   u32x4 v;
   v.x = x.x;
@@ -35,19 +41,19 @@ __device__ __forceinline__ void store16(void* p, const uint4& x) {
 }
 
 // ---------------------------------------------------------------------------
-// Diff / compaction tiling.  One workgroup of 256 lanes (four wave64s) owns a
-// tile of kDiffIters * 256 * 8 elements: every lane issues kDiffIters 16-byte
-// loads per input, one wave covering 1 KB contiguous per load.  Tiles never
-// straddle parameters.
+// Diff / compaction tiling.  One workgroup of 512 lanes (eight wave64s) owns a
+// tile of kDiffIters * 512 * 8 = 32768 elements: every lane issues kDiffIters
+// 16-byte loads per input, one wave covering 1 KB contiguous per load.  Tiles
+// never straddle parameters.
 // ---------------------------------------------------------------------------
 constexpr int kDiffBlock = 512;
 constexpr int kDiffWaves = kDiffBlock / 64;
 constexpr int kVec = 8;  // bf16 per 16-byte load
 constexpr int kDiffIters = 8;
-constexpr int64_t kDiffTile = int64_t(kDiffBlock) * kVec * kDiffIters;  // 16384
-// One workgroup per tile: the grid (tiles x 256 lanes) must stay below 2^32
-// work-items.  2^24 tiles are 2.7e11 elements, more than HBM holds twice.
-constexpr int64_t kMaxTiles = int64_t(1) << 24;
+constexpr int64_t kDiffTile = int64_t(kDiffBlock) * kVec * kDiffIters;  // 32768
+// One workgroup per tile: the grid (tiles x 512 lanes) must stay below 2^32
+// work-items.  2^23 tiles are 2.7e11 elements, more than HBM holds twice.
+constexpr int64_t kMaxTiles = int64_t(1) << 23;
 
 // Parameter descriptor as stored in the workspace (32 bytes).
 struct DiffParam {
@@ -66,25 +72,42 @@ struct TileDesc {
   int64_t pad;
 };
 
-// A tile's compacted entries are staged in LDS (4 bytes each) when at most
-// this many elements changed; denser tiles are written directly.
+// A tile with at most kStageCap changes is staged in LDS (4 bytes per entry)
+// and then copied to a workspace slot: a compact 4 KB slot when it has at
+// most kCompactCap changes, else a wide 16 KB one.  A denser tile stores its
+// change mask (one byte per 16-byte chunk, 8 per lane) in its compact slot.
 constexpr int kStageCap = 4096;
-// Tiles with at most this many changes are finished by wave 0 alone (the
-// other waves leave early and free their registers for new workgroups).
-constexpr int kSoloCap = 1024;
+constexpr int kCompactCap = 1024;
+constexpr int64_t kCompactWords = kCompactCap;  // uint32 per compact slot
+constexpr int64_t kWideWords = kStageCap;       // uint32 per wide slot
+// Tile counts are scanned in chunks of kScanChunk tiles, four per lane.
+constexpr int kScanBlock = 1024;
+constexpr int64_t kScanChunk = int64_t(kScanBlock) * 4;
+// Consecutive tiles whose staged entries one placing workgroup copies.
+constexpr int kPlaceTiles = 16;
+// Workgroups that share the dense tiles.
+constexpr int64_t kDenseGrid = 1024;
 
 struct SnapParam {
   uint16_t* snap;
   int64_t numel;
 };
 
-// Workspace layout: [header 256 B | tile state 8 B/tile | tile descriptor
-// 32 B/tile | parameter table 32 B/param].  All offsets are 256-byte aligned.
+// Workspace layout (all offsets 256-byte aligned): a 256-byte header, then
+// per tile a count, an in-chunk prefix, a dense-list entry, a descriptor, a
+// compact and a wide slot (20 KB), per chunk a total and a base, and the
+// parameter table.
 struct WsLayout {
-  size_t flag;        // uint32 look-back timeout flag
-  size_t state;       // uint64 per tile: status (2 bits) | count (62 bits)
+  size_t ndense;      // uint32: number of dense tiles
+  size_t counts;      // uint32 per tile: changed elements
+  size_t inpfx;       // uint32 per tile: exclusive prefix inside its chunk
+  size_t chunk_tot;   // uint32 per chunk
+  size_t chunk_base;  // uint64 per chunk, then the total
+  size_t dense_list;  // int32 per tile
   size_t tile_desc;   // TileDesc per tile
   size_t table;       // DiffParam / SnapParam per parameter
+  size_t compact;     // kCompactWords uint32 per tile
+  size_t wide;        // kWideWords uint32 per tile
   size_t total;
 };
 

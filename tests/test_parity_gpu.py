@@ -2,9 +2,11 @@
 
 Tolerance is zero everywhere: the path is integer and bit work, so nnz, the
 order of the indices and the value bits must be identical.  Sizes span
-several 16384-element tiles, ragged tails, unaligned views, empty and
-all-changed inputs, signed zeros and NaN payloads.  No oracle input or
-expected value comes from the GPU path.
+several 32768-element tiles, ragged tails, unaligned views, empty and
+all-changed inputs, signed zeros and NaN payloads, and tiles whose change
+counts sit on each side of the compaction's staging limits (1024 and 4096
+changes per tile).  No oracle input or expected value comes from the GPU
+path.
 """
 import numpy as np
 import pytest
@@ -77,6 +79,73 @@ def test_diff_unaligned_views(sbd, oracle_mod, pad_old, pad_new, n):
     gi, gv = sbd.diff(gpu_bits(old, pad_old), gpu_bits(new, pad_new))
     assert np.array_equal(gi.cpu().numpy(), ri)
     assert np.array_equal(np_bits(gv), rv)
+
+
+# changes per tile, straddling the compact-slot (1024), wide-slot (4096) and
+# dense limits; the last tile is ragged (5000 of 32768 elements, all changed)
+TILE_COUNTS = [0, 1, 1023, 1024, 1025, 4095, 4096, 4097, TILE, 3, TILE // 2, 1027, 5000]
+
+
+def tile_kinds_case(seed, counts=TILE_COUNTS, last_valid=5000):
+    rng = np.random.default_rng(seed)
+    n = (len(counts) - 1) * TILE + last_valid
+    old = rng.integers(0, 1 << 16, size=n, dtype=np.uint32).astype(np.uint16)
+    new = old.copy()
+    for t, c in enumerate(counts):
+        width = TILE if t < len(counts) - 1 else last_valid
+        pos = t * TILE + rng.choice(width, size=min(c, width), replace=False)
+        off = rng.integers(1, 1 << 16, size=pos.size, dtype=np.uint32).astype(np.uint16)
+        new[pos] = (old[pos].astype(np.uint32) + off).astype(np.uint16)
+    return old, new
+
+
+@pytest.mark.parametrize("pad", [0, 3])
+def test_diff_tile_kinds(sbd, oracle_mod, pad):
+    """Every staging path -- compact slot, wide slot, dense re-read -- and their
+    limits, aligned and unaligned, as one tensor and as a parameter list."""
+    old, new = tile_kinds_case(11 + pad)
+    ri, rv = oracle_mod.diff(old, new)
+    per_tile = np.bincount(ri // TILE, minlength=len(TILE_COUNTS))
+    assert per_tile.tolist() == TILE_COUNTS  # the fixture is what it claims
+    gi, gv = sbd.diff(gpu_bits(old, pad), gpu_bits(new, pad))
+    assert np.array_equal(gi.cpu().numpy(), ri)
+    assert np.array_equal(np_bits(gv), rv)
+    # the same tiles as a list of one-tile parameters plus the whole tensor
+    olds = [old[t * TILE:(t + 1) * TILE] for t in range(len(TILE_COUNTS))] + [old]
+    news = [new[t * TILE:(t + 1) * TILE] for t in range(len(TILE_COUNTS))] + [new]
+    ri2, rv2, rn2, ro2 = oracle_mod.diff_many(olds, news)
+    gi2, gv2, gn2, go2 = sbd.diff_many([gpu_bits(o, pad) for o in olds],
+                                       [gpu_bits(x, pad) for x in news])
+    assert np.array_equal(gn2.cpu().numpy(), rn2)
+    assert np.array_equal(go2.cpu().numpy(), ro2)
+    assert np.array_equal(gi2.cpu().numpy(), ri2)
+    assert np.array_equal(np_bits(gv2), rv2)
+
+
+@pytest.mark.parametrize("cut", [1024 + 1023 + 1, 1 + 1023 + 1024 + 1025 + 4095 + 7,
+                                 sum(TILE_COUNTS[:8]) + 100, sum(TILE_COUNTS) - 1])
+def test_diff_tile_kinds_capacity(sbd, oracle_mod, cut):
+    """A capacity that ends inside a compact, a wide and a dense tile's run:
+    the prefix is exact and nothing past the capacity is written."""
+    from sparse_bf16_delta_amd import _abi
+    from sparse_bf16_delta_amd.ops import _ptr, _stream
+
+    old, new = tile_kinds_case(23)
+    ri, rv = oracle_mod.diff(old, new)
+    n = old.size
+    lib = _abi.load()
+    o, x = gpu_bits(old), gpu_bits(new)
+    guard = 4096
+    idx = torch.full((cut + guard,), -7, dtype=torch.int32, device="cuda")
+    val = torch.full((cut + guard,), -7, dtype=torch.int16, device="cuda")
+    nnz = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ws = torch.empty(lib.delta_workspace_size(n, 1), dtype=torch.uint8, device="cuda")
+    _abi.check(lib.delta_diff(_ptr(o), _ptr(x), n, _ptr(idx), _ptr(val), cut, _ptr(nnz),
+                              _ptr(ws), ws.numel(), _stream(o.device)))
+    assert int(nnz.item()) == ri.size
+    assert np.array_equal(idx[:cut].cpu().numpy(), ri[:cut])
+    assert np.array_equal(np_bits(val[:cut]), rv[:cut])
+    assert bool((idx[cut:] == -7).all()) and bool((val[cut:] == -7).all())
 
 
 def test_diff_capacity_protocol(sbd, oracle_mod):
