@@ -53,9 +53,14 @@ def test_workspace_size():
     b = lib.delta_workspace_size(1 << 30, 1)
     c = lib.delta_workspace_size(1 << 30, 300)
     assert 0 < a < b < c
-    # 8 B scan state + 4 B map per 16384-element tile, plus the table
-    assert b >= 12 * ((1 << 30) // 16384)
-    assert c - b >= 300 * 32 - 512
+    # per 32768-element tile: two staging slots (4 KB + 16 KB), count, prefix,
+    # dense-list entry and a 32-byte descriptor; each extra parameter may add
+    # a partial tile and a 32-byte table entry
+    per_tile = 4096 + 16384 + 4 + 4 + 4 + 32
+    tiles = (1 << 30) // 32768
+    assert b >= per_tile * tiles
+    assert b <= per_tile * (tiles + 2) + 4096 * 4  # no more than the layout needs
+    assert c - b >= 299 * per_tile
 
 
 def _err(lib):
