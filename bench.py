@@ -77,7 +77,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c5"])
+    ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4"],
+                    help="c3 (default): the 7B-shaped list; c1, c2: smaller lists; "
+                         "c4: density sweep on one flat 2^28-element tensor (table on stderr)")
     ap.add_argument("--lr", type=float, default=None)
     ap.add_argument("--mode", default=None, choices=[None, "fp32_master", "bf16_resident"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -116,6 +118,9 @@ def main():
     sbd.load()
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
+    if args.config == "c4":
+        density_sweep(args, props)
+        return
     cfg = workloads.CONFIGS[args.config]
     lr = args.lr if args.lr is not None else (1e-6 if cfg.key == "c3" else cfg.lrs[0])
     mode = args.mode or cfg.mode
@@ -285,6 +290,82 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, cfg, olds, news, dplan, nnz_total)
     print(json.dumps(result), flush=True)
+
+
+def density_sweep(args, props):
+    """Sparse path (diff + apply) and XOR path (xor_mask + xor_apply) on one
+    flat 2^28-element tensor at each forced density, uniform and clustered:
+    times, algorithmic bytes and the density where XOR becomes cheaper."""
+    import torch
+
+    import sparse_bf16_delta_amd as sbd
+    from sparse_bf16_delta_amd.plan import ApplyPlan, DiffPlan
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    n = 1 << 28
+    reps = max(args.steps, 1)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    rows = []
+    log(f"[bench] density sweep, {n:,} elements, {reps} reps per op")
+    log(f"[bench] {'pattern':9s} {'density':>8s} {'changed':>11s} {'diff ms':>8s} {'%pk':>5s} "
+        f"{'apply ms':>9s} {'%pk':>5s} {'xor_mask':>9s} {'xor_apply':>10s} {'sparse/xor':>10s}")
+    for pattern in ("uniform", "clustered"):
+        for di, frac in enumerate(workloads.DENSITIES):
+            old, new, k = workloads.density_case(n, frac, pattern, di, device=dev)
+            snap = old.clone()
+            mask = torch.empty(n, dtype=torch.int16, device=dev)
+            cap = k + 65536
+            dplan = DiffPlan([old], [new], cap)
+            aplan = ApplyPlan([snap])
+            t_diff = timed(dplan.run)
+            got = dplan.changed()
+            t_apply = timed(lambda: aplan.run(dplan.idx, dplan.val, dplan.offsets, cap))
+            ok = got == k and torch.equal(snap.view(torch.int16), new.view(torch.int16))
+            t_mask = timed(lambda: sbd.xor_mask(old, new, out=mask))
+            t_xapp = timed(lambda: sbd.xor_apply_(snap, mask))
+            back = old if (args.warmup + reps) % 2 else new  # xor_apply is self-inverse
+            ok = ok and torch.equal(snap.view(torch.int16), back.view(torch.int16))
+            pos = dplan.idx[:k].long()
+            g128 = int(((pos >> 6)[1:] != (pos >> 6)[:-1]).sum().item()) + 1 if k else 0
+            b_diff, b_apply, b_xor = 4 * n + 6 * k, 6 * k + 256 * g128, 6 * n
+            f_diff = b_diff / (t_diff * 1e-3) / 1e9 / HBM_PEAK_GBS
+            f_apply = b_apply / (t_apply * 1e-3) / 1e9 / HBM_PEAK_GBS
+            ratio = (t_diff + t_apply) / (t_mask + t_xapp)
+            rows.append({"pattern": pattern, "density": frac, "changed": k, "diff_ms": round(t_diff, 4),
+                         "diff_frac": round(f_diff, 4), "apply_ms": round(t_apply, 4),
+                         "apply_frac": round(f_apply, 4), "touched_lines_128B": g128,
+                         "xor_mask_ms": round(t_mask, 4), "xor_apply_ms": round(t_xapp, 4),
+                         "sparse_over_xor": round(ratio, 3), "identical": ok})
+            log(f"[bench] {pattern:9s} {frac:8.3%} {k:11,d} {t_diff:8.3f} {100 * f_diff:5.1f} "
+                f"{t_apply:9.3f} {100 * f_apply:5.1f} {t_mask:9.3f} {t_xapp:10.3f} {ratio:10.2f}"
+                f"{'' if ok else '  MISMATCH'}")
+            del old, new, snap, mask, dplan, aplan, pos
+            if not ok:
+                print("bench.py: density sweep result mismatch", file=sys.stderr)
+                sys.exit(1)
+    print(json.dumps({
+        "metric": "density sweep: diff/apply and xor_mask/xor_apply times per density",
+        "value": None, "unit": "ms", "n_gpus": 1, "steps": reps, "warmup": args.warmup,
+        "higher_is_better": False, "dtype": "u16", "data": "synthetic",
+        "config": {"workload": f"flat {n}-element bf16 tensor, forced subsets, uniform and "
+                               f"clustered {workloads.CLUSTER_RUN}-element runs"},
+        "sweep": rows,
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None)},
+    }), flush=True)
 
 
 def cpu_baseline(args, cfg, olds, news, dplan, nnz_total):

@@ -168,12 +168,13 @@ __device__ __forceinline__ TileView tile_view(const TileDesc* __restrict__ tdesc
 // From the lanes' change masks: each lane's offset inside its (iteration,
 // wave) group (lp), each group's offset inside the tile in ascending element
 // order -- iteration-major, then wave, then lane, then slot -- (goff), and the
-// tile's count (agg), in every lane.  Contains one barrier; s_wtot must not
-// be in use by other waves.
+// tile's count (agg), in every lane; gexcl is the offset of group `lane`.
+// Contains one barrier; s_wtot must not be in use by other waves.
 __device__ __forceinline__ void tile_offsets(const uint32_t (&m)[kDiffIters],
                                              uint32_t (&lp)[kDiffIters],
                                              uint32_t (&goff)[kDiffIters], uint32_t& agg,
-                                             uint32_t* s_wtot, int lane, int wave) {
+                                             uint32_t& gexcl, uint32_t* s_wtot, int lane,
+                                             int wave) {
 #pragma unroll
   for (int j = 0; j < kDiffIters; ++j) {
     uint32_t tot;
@@ -185,6 +186,7 @@ __device__ __forceinline__ void tile_offsets(const uint32_t (&m)[kDiffIters],
   const uint32_t own = lane < kGroups ? s_wtot[lane] : 0u;
   const uint32_t inc = wave_inclusive(own, lane);
   const uint32_t excl = inc - own;
+  gexcl = excl;
   agg = static_cast<uint32_t>(__shfl(static_cast<int>(inc), 63, 64));
 #pragma unroll
   for (int j = 0; j < kDiffIters; ++j)
@@ -262,8 +264,8 @@ __global__ __launch_bounds__(kDiffBlock) void diff_count_kernel(
     }
   }
 
-  uint32_t lp[kDiffIters], goff[kDiffIters], agg;
-  tile_offsets(m, lp, goff, agg, s_wtot, lane, wave);
+  uint32_t lp[kDiffIters], goff[kDiffIters], agg, gexcl;
+  tile_offsets(m, lp, goff, agg, gexcl, s_wtot, lane, wave);
   if (tid == 0) {
     counts[tile] = agg;
     if (tile == 0) *ndense = 0u;  // the scan kernel, launched next, lists dense tiles
@@ -396,67 +398,95 @@ __global__ __launch_bounds__(kScanBlock) void diff_base_kernel(
   }
 }
 
-// Phase 3a: copy the staged entries of kPlaceTiles consecutive tiles, which
-// form one contiguous output run, to their final positions.
+// Phase 3a: copy the staged entries of `tiles_per_wg` consecutive tiles to
+// their final positions.  Consecutive tiles have consecutive outputs, so the
+// staged tiles' entries are walked as one flat run (dense tiles, written by
+// diff_dense_kernel, and empty ones are left out of it).
 template <bool kMany>
 __global__ __launch_bounds__(kDiffBlock) void diff_place_kernel(
-    const TileDesc* __restrict__ tdesc, int64_t total_tiles, int32_t nchunks,
+    const TileDesc* __restrict__ tdesc, int64_t total_tiles, int32_t nchunks, int32_t tiles_per_wg,
     const uint32_t* __restrict__ inpfx, const uint64_t* __restrict__ chunk_base,
     const uint32_t* __restrict__ compact, const uint32_t* __restrict__ wide,
     int32_t* __restrict__ idx, uint16_t* __restrict__ val, int64_t capacity) {
   constexpr int kUnroll = 4;
-  __shared__ uint64_t s_off[kPlaceTiles + 1];
+  __shared__ uint64_t s_off[kPlaceTiles + 1];  // output offset of each tile
   __shared__ int32_t s_e0[kPlaceTiles];
+  __shared__ uint32_t s_run[kPlaceTiles + 1];  // start of the m-th staged tile in the flat run
+  __shared__ int32_t s_tile[kPlaceTiles];      // which tile that is
+  __shared__ int32_t s_nrun;
   const int tid = threadIdx.x;
-  const int64_t t0 = int64_t(blockIdx.x) * kPlaceTiles;
+  const int64_t t0 = int64_t(blockIdx.x) * tiles_per_wg;
   const int64_t left = total_tiles - t0;
-  const int nt = static_cast<int>(left < kPlaceTiles ? left : kPlaceTiles);
+  const int nt = static_cast<int>(left < tiles_per_wg ? left : tiles_per_wg);
   if (tid <= nt) {
     const int64_t t = t0 + tid;
     s_off[tid] = t < total_tiles ? chunk_base[t / kScanChunk] + inpfx[t] : chunk_base[nchunks];
     if (tid < nt) s_e0[tid] = kMany ? tdesc[t].e0 : static_cast<int32_t>(t * kDiffTile);
   }
   __syncthreads();
+  if (tid == 0) {
+    uint32_t acc = 0;
+    int r = 0;
+    for (int k = 0; k < nt; ++k) {
+      const uint64_t c = s_off[k + 1] - s_off[k];
+      if (c != 0 && c <= static_cast<uint64_t>(kStageCap)) {
+        s_tile[r] = k;
+        s_run[r] = acc;
+        acc += static_cast<uint32_t>(c);
+        ++r;
+      }
+    }
+    s_run[r] = acc;
+    s_nrun = r;
+  }
+  __syncthreads();
+  const uint32_t total = s_run[s_nrun];
   const uint64_t cap = static_cast<uint64_t>(capacity);
-  const uint64_t hi = s_off[nt] < cap ? s_off[nt] : cap;
-  int k = 0;  // tile of the current output position; only moves forward
-  for (uint64_t jb = s_off[0] + tid; jb < hi; jb += kUnroll * kDiffBlock) {
+  int r = 0;  // staged tile of the current flat position; only moves forward
+  for (uint32_t qb = static_cast<uint32_t>(tid); qb < total; qb += kUnroll * kDiffBlock) {
     uint32_t w[kUnroll];
+    uint64_t jj[kUnroll];
     int kk[kUnroll];
     bool ok[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const uint64_t j = jb + uint64_t(u) * kDiffBlock;
-      ok[u] = j < hi;
+      const uint32_t q = qb + static_cast<uint32_t>(u * kDiffBlock);
+      ok[u] = q < total;
       if (ok[u]) {
-        while (s_off[k + 1] <= j) ++k;  // stops below nt because j < s_off[nt]
+        while (s_run[r + 1] <= q) ++r;  // stops below s_nrun because q < total
+        const int k = s_tile[r];
+        const uint32_t p = q - s_run[r];
+        jj[u] = s_off[k] + p;
         kk[u] = k;
-        const uint64_t c = s_off[k + 1] - s_off[k];
-        ok[u] = c <= static_cast<uint64_t>(kStageCap);  // else dense: written by diff_dense_kernel
-        const uint32_t* slot = c <= static_cast<uint64_t>(kCompactCap)
+        ok[u] = jj[u] < cap;
+        const uint32_t* slot = s_off[k + 1] - s_off[k] <= static_cast<uint64_t>(kCompactCap)
                                    ? compact + (t0 + k) * kCompactWords
                                    : wide + (t0 + k) * kWideWords;
-        if (ok[u]) w[u] = *global_ptr(slot + (j - s_off[k]));
+        if (ok[u]) w[u] = *global_ptr(slot + p);
       }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       if (ok[u]) {
-        const uint64_t j = jb + uint64_t(u) * kDiffBlock;
-        idx[j] = s_e0[kk[u]] + static_cast<int32_t>(w[u] >> 16);
-        val[j] = static_cast<uint16_t>(w[u] & 0xFFFFu);
+        idx[jj[u]] = s_e0[kk[u]] + static_cast<int32_t>(w[u] >> 16);
+        val[jj[u]] = static_cast<uint16_t>(w[u] & 0xFFFFu);
       }
     }
   }
 }
 
-// Phase 3b: dense tiles, from their change masks and a second read of `new`.
+// Phase 3b: dense tiles, from their change masks and a second read of the
+// changed 16-byte chunks of `new`.  Each of the tile's kDiffIters iterations
+// (at most kDiffBlock * kVec entries) is staged in LDS and copied out with
+// coalesced stores.
 template <bool kMany>
 __global__ __launch_bounds__(kDiffBlock) void diff_dense_kernel(
     const TileDesc* __restrict__ tdesc, DiffParam single, const int32_t* __restrict__ dense_list,
     const uint32_t* __restrict__ ndense, const uint32_t* __restrict__ inpfx,
     const uint64_t* __restrict__ chunk_base, const uint32_t* __restrict__ compact,
     int32_t* __restrict__ idx, uint16_t* __restrict__ val, int64_t capacity) {
+  static_assert(kDiffBlock * kVec <= kStageCap, "one iteration of a tile fits the stage");
+  __shared__ __attribute__((aligned(16))) uint32_t s_stage[kDiffBlock * kVec];
   __shared__ uint32_t s_wtot[kGroups];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -464,36 +494,80 @@ __global__ __launch_bounds__(kDiffBlock) void diff_dense_kernel(
   const uint64_t cap = static_cast<uint64_t>(capacity);
   const uint32_t nd = *ndense;
   for (uint32_t i = blockIdx.x; i < nd; i += gridDim.x) {
+    // opaque copy of the lane id: keeps the compiler from hoisting ~200
+    // per-lane index constants out of this loop into registers
+    int ltid = tid;
+    asm volatile("" : "+v"(ltid));
     const int64_t t = dense_list[i];
     const TileView tv = tile_view<kMany>(tdesc, single, t);
     const bool vec = tv.valid == kDiffTile && (reinterpret_cast<uintptr_t>(tv.nb) & 15u) == 0;
-    const u32x2 mw = *global_ptr(reinterpret_cast<const u32x2*>(compact + t * kCompactWords) + tid);
+    const u32x2 mw = *global_ptr(reinterpret_cast<const u32x2*>(compact + t * kCompactWords) + ltid);
     uint32_t m[kDiffIters];
+    uint4 x[kDiffIters];
 #pragma unroll
-    for (int j = 0; j < kDiffIters; ++j) m[j] = ((j < 4 ? mw.x : mw.y) >> (8 * (j & 3))) & 0xFFu;
-    uint32_t lp[kDiffIters], goff[kDiffIters], agg;
-    tile_offsets(m, lp, goff, agg, s_wtot, lane, wave);
+    for (int j = 0; j < kDiffIters; ++j) {
+      m[j] = ((j < 4 ? mw.x : mw.y) >> (8 * (j & 3))) & 0xFFu;
+      x[j] = m[j] != 0u ? load_chunk(tv.nb, j * kDiffBlock * kVec + ltid * kVec, tv.valid, vec)
+                        : make_uint4(0u, 0u, 0u, 0u);
+    }
+    uint32_t lp[kDiffIters], goff[kDiffIters], agg, gexcl;
+    tile_offsets(m, lp, goff, agg, gexcl, s_wtot, lane, wave);
     const uint64_t tbase = chunk_base[t / kScanChunk] + inpfx[t];
 #pragma unroll
     for (int j = 0; j < kDiffIters; ++j) {
+      // entries of iteration j occupy [jb, je) of the tile's output
+      const uint32_t jb = static_cast<uint32_t>(__shfl(static_cast<int>(gexcl), j * kDiffWaves, 64));
+      const uint32_t je =
+          j + 1 < kDiffIters
+              ? static_cast<uint32_t>(__shfl(static_cast<int>(gexcl), (j + 1) * kDiffWaves, 64))
+              : agg;
       const uint32_t mm = m[j];
       if (mm != 0u) {
-        uint64_t pos = tbase + goff[j] + lp[j];
-        const int local = j * kDiffBlock * kVec + tid * kVec;
-        const uint4 x = load_chunk(tv.nb, local, tv.valid, vec);
-        const int64_t ebase = int64_t(tv.e0) + local;
-        emit_slot<0>(mm, pos, ebase, x, idx, val, cap);
-        emit_slot<1>(mm, pos, ebase, x, idx, val, cap);
-        emit_slot<2>(mm, pos, ebase, x, idx, val, cap);
-        emit_slot<3>(mm, pos, ebase, x, idx, val, cap);
-        emit_slot<4>(mm, pos, ebase, x, idx, val, cap);
-        emit_slot<5>(mm, pos, ebase, x, idx, val, cap);
-        emit_slot<6>(mm, pos, ebase, x, idx, val, cap);
-        emit_slot<7>(mm, pos, ebase, x, idx, val, cap);
+        uint32_t pos = goff[j] + lp[j] - jb;
+        const uint32_t local = static_cast<uint32_t>(j * kDiffBlock * kVec + ltid * kVec);
+        stage_slot<0>(mm, pos, local, x[j], s_stage);
+        stage_slot<1>(mm, pos, local, x[j], s_stage);
+        stage_slot<2>(mm, pos, local, x[j], s_stage);
+        stage_slot<3>(mm, pos, local, x[j], s_stage);
+        stage_slot<4>(mm, pos, local, x[j], s_stage);
+        stage_slot<5>(mm, pos, local, x[j], s_stage);
+        stage_slot<6>(mm, pos, local, x[j], s_stage);
+        stage_slot<7>(mm, pos, local, x[j], s_stage);
       }
+      __syncthreads();
+      for (uint32_t p = static_cast<uint32_t>(tid); p < je - jb; p += kDiffBlock) {
+        const uint64_t o = tbase + jb + p;
+        if (o < cap) {
+          const uint32_t w = s_stage[p];
+          idx[o] = tv.e0 + static_cast<int32_t>(w >> 16);
+          val[o] = static_cast<uint16_t>(w & 0xFFFFu);
+        }
+      }
+      __syncthreads();  // the stage is refilled by the next iteration
     }
-    __syncthreads();  // s_wtot is rewritten for the next tile
   }
+}
+
+// Workgroups of diff_dense_kernel<kMany> that are resident at once on the
+// current device: its grid-stride loop hands each workgroup the same share of
+// dense tiles, so a larger grid would leave a tail.  Queried once per device.
+template <bool kMany>
+int64_t dense_grid_limit() {
+  static int64_t cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, diff_dense_kernel<kMany>,
+                                                     kDiffBlock, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        per_cu < 1 || cus < 1) {
+      (void)hipGetLastError();
+      return 256;
+    }
+    cached[dev] = int64_t(per_cu) * cus;
+  }
+  return cached[dev];
 }
 
 }  // namespace
@@ -540,17 +614,23 @@ hipError_t launch_diff(const DiffParam* d_table, const DiffParam& single, int32_
     diff_base_kernel<false><<<dim3(1), dim3(kScanBlock), 0, stream>>>(
         nullptr, nparams, total_tiles, nchunks, inpfx, chunk_tot, chunk_base, nnz, offsets);
   if (total_tiles > 0) {
-    const unsigned place_grid = static_cast<unsigned>((total_tiles + kPlaceTiles - 1) / kPlaceTiles);
+    // enough placing workgroups to fill the GPU, up to kPlaceTiles tiles each
+    int64_t per_wg = total_tiles / 2048;
+    per_wg = per_wg < 1 ? 1 : (per_wg > kPlaceTiles ? kPlaceTiles : per_wg);
+    const unsigned place_grid = static_cast<unsigned>((total_tiles + per_wg - 1) / per_wg);
+    const int64_t dense_max = many ? dense_grid_limit<true>() : dense_grid_limit<false>();
     const unsigned dense_grid =
-        static_cast<unsigned>(total_tiles < kDenseGrid ? total_tiles : kDenseGrid);
+        static_cast<unsigned>(total_tiles < dense_max ? total_tiles : dense_max);
     if (many) {
       diff_place_kernel<true><<<dim3(place_grid), dim3(kDiffBlock), 0, stream>>>(
-          tdesc, total_tiles, nchunks, inpfx, chunk_base, compact, wide, idx, val, capacity);
+          tdesc, total_tiles, nchunks, static_cast<int32_t>(per_wg), inpfx, chunk_base, compact,
+          wide, idx, val, capacity);
       diff_dense_kernel<true><<<dim3(dense_grid), dim3(kDiffBlock), 0, stream>>>(
           tdesc, single, dense_list, ndense, inpfx, chunk_base, compact, idx, val, capacity);
     } else {
       diff_place_kernel<false><<<dim3(place_grid), dim3(kDiffBlock), 0, stream>>>(
-          nullptr, total_tiles, nchunks, inpfx, chunk_base, compact, wide, idx, val, capacity);
+          nullptr, total_tiles, nchunks, static_cast<int32_t>(per_wg), inpfx, chunk_base, compact,
+          wide, idx, val, capacity);
       diff_dense_kernel<false><<<dim3(dense_grid), dim3(kDiffBlock), 0, stream>>>(
           nullptr, single, dense_list, ndense, inpfx, chunk_base, compact, idx, val, capacity);
     }

@@ -85,8 +85,6 @@ constexpr int kScanBlock = 1024;
 constexpr int64_t kScanChunk = int64_t(kScanBlock) * 4;
 // Consecutive tiles whose staged entries one placing workgroup copies.
 constexpr int kPlaceTiles = 16;
-// Workgroups that share the dense tiles.
-constexpr int64_t kDenseGrid = 1024;
 
 struct SnapParam {
   uint16_t* snap;
