@@ -187,6 +187,9 @@ def main():
     b_apply = 6 * nnz_total + 2 * 128 * lines128
     b_apply64 = 6 * nnz_total + 2 * 64 * lines64
     b_xor = 6 * n_alloc
+    # xor_apply reads the mask and rewrites only the 128-byte snapshot lines
+    # where it is nonzero, the lines holding a changed element (line model)
+    b_xor_apply = 2 * n_alloc + 2 * 128 * lines128
 
     stream = torch.cuda.current_stream(dev)
     names = ["delta_diff_many", "delta_apply_many", "xor_mask", "xor_apply"]
@@ -224,7 +227,7 @@ def main():
         print("bench.py: timed steps changed the result", file=sys.stderr)
         sys.exit(1)
 
-    alg = [b_diff, b_apply, b_xor, b_xor]
+    alg = [b_diff, b_apply, b_xor, b_xor_apply]
     workload_key = f"{cfg.key}:{mode}:{lr:g}"
     traffic = measured_traffic(workload_key)
     kernels = []

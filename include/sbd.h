@@ -183,7 +183,11 @@ delta_status xor_mask(const uint16_t *old_bits, const uint16_t *new_bits, uint16
  *
  * [XOR] first paragraph: the sampler XORs the mask into its old weights and
  * obtains the new ones without floating-point arithmetic.
- *  snapshot            n uint16, updated in place; mask n uint16.
+ *  snapshot            n uint16, updated in place; mask n uint16 (may alias
+ *                      the snapshot, which then becomes zero).
+ * Where the mask is zero the snapshot does not change, and when both are
+ * 16-byte aligned it is not even read there: only the 128-byte units whose
+ * mask is nonzero are read and rewritten.
  * Errors: DELTA_E_INVALID, DELTA_E_HIP.
  */
 delta_status xor_apply(uint16_t *snapshot, const uint16_t *mask, int64_t n, void *stream);

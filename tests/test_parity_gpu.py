@@ -359,6 +359,31 @@ def test_xor_matches_oracle(sbd, oracle_mod, n, pad):
     assert np.array_equal(np_bits(g_o), old)
 
 
+@pytest.mark.parametrize("frac", [0.0, 0.001, 0.02, 0.3, 1.0])
+@pytest.mark.parametrize("n,pad", [(TILE * 3 + 5, 0), (TILE * 3 + 5, 1), (100_003, 3), (15, 0)])
+def test_xor_apply_sparse_masks(sbd, oracle_mod, frac, n, pad):
+    """xor_apply leaves the snapshot untouched where the mask is zero: masks
+    from all-zero to all-nonzero, ragged tails and unaligned views."""
+    old, new = rand_case(int(frac * 1e4) + n + pad, n, frac, special=False)
+    want_mask = oracle_mod.xor_mask(old, new)
+    want = old.copy()
+    oracle_mod.xor_apply_(want, want_mask)
+    g_snap, g_mask = gpu_bits(old, pad), gpu_bits(want_mask, pad)
+    sbd.xor_apply_(g_snap, g_mask)
+    assert np.array_equal(np_bits(g_snap), want)
+    sbd.xor_apply_(g_snap, g_mask)
+    assert np.array_equal(np_bits(g_snap), old)
+
+
+def test_xor_apply_mask_aliasing_snapshot(sbd):
+    """snapshot ^= snapshot clears it, zero and nonzero units alike."""
+    old, _ = rand_case(5, 2 * TILE + 9, 0.0, special=False)
+    old[: TILE] = 0  # a run of all-zero units
+    g = gpu_bits(old)
+    sbd.xor_apply_(g, g)
+    assert not bool((g.view(torch.int16) != 0).any())
+
+
 def test_xor_mask_may_alias_new(sbd, oracle_mod):
     old, new = rand_case(77, 3 * TILE + 1, 0.1)
     want = oracle_mod.xor_mask(old, new)
