@@ -289,6 +289,58 @@ def test_apply_unsorted_is_flagged_and_stays_inside(sbd):
     assert np.all(got[n:] == 7)
 
 
+@pytest.mark.parametrize("frac", [0.02, 0.05, 0.1, 0.3])
+@pytest.mark.parametrize("pad", [0, 1, 8])
+def test_apply_dense_runs_and_boundaries(sbd, oracle_mod, frac, pad):
+    """Densities around the line-merge threshold, on a snapshot that is 16-byte
+    aligned (merge allowed), 2-byte aligned (scatter only) or offset by 16
+    bytes (lines not on 128-byte boundaries); chunk edges share lines."""
+    n = 9 * 2048 * 40 + 77
+    old, new = rand_case(int(frac * 100) + pad, n, frac, special=False)
+    ri, rv = oracle_mod.diff(old, new)
+    snap = gpu_bits(old, pad)
+    sbd.apply_(snap, torch.from_numpy(ri).cuda(),
+               torch.from_numpy(rv.view(np.int16)).cuda().view(torch.bfloat16))
+    assert np.array_equal(np_bits(snap), new)
+
+
+def test_apply_merge_with_broken_precondition_stays_inside(sbd):
+    """A chunk dense enough for the line merge but holding unsorted, repeated
+    and out-of-range entries: they are counted, only the broken entries'
+    positions may differ, every well-formed entry lands, and nothing outside
+    the snapshot changes (such a chunk is applied entry by entry)."""
+    rng = np.random.default_rng(3)
+    n = 40_000
+    snap0 = rng.integers(0, 1 << 16, size=n, dtype=np.uint32).astype(np.uint16)
+    idx = np.sort(rng.choice(np.arange(1000, 20_000), size=4096, replace=False)).astype(np.int32)
+    idx[100:110] = idx[100:110][::-1]          # unsorted
+    idx[500] = idx[499]                        # repeated
+    idx[900] = n + 5                           # out of range
+    idx[901] = -3                              # negative
+    val = rng.integers(0, 1 << 16, size=idx.size, dtype=np.uint32).astype(np.uint16)
+    buf = gpu_bits(np.concatenate([snap0, np.full(256, 7, dtype=np.uint16)]))
+    snap = buf[:n]
+    with pytest.raises(sbd.DeltaError, match="delta entries"):
+        sbd.apply_(snap, torch.from_numpy(idx).cuda(),
+                   torch.from_numpy(val.view(np.int16)).cuda().view(torch.bfloat16),
+                   check_indices=True)
+    got = np_bits(buf)
+    inr = idx[(idx >= 0) & (idx < n)]
+    touched = np.zeros(n, dtype=bool)
+    touched[inr] = True
+    assert np.array_equal(got[:n][~touched], snap0[~touched])
+    for i in np.flatnonzero(touched):  # the entry's value or, if repeated or unsorted, another of its
+        assert got[i] == snap0[i] or got[i] in set(val[idx == i].tolist())
+    # positions whose only entry is well-formed (sorted neighbourhood) hold its value
+    ok = np.ones(idx.size, dtype=bool)
+    ok[95:115] = False
+    ok[495:505] = False
+    ok[900:902] = False
+    good = idx[ok]
+    assert np.array_equal(got[good], val[ok])
+    assert np.all(got[n:] == 7)
+
+
 @pytest.mark.parametrize("frac", [0.0, 0.03, 0.7])
 def test_apply_many_matches_oracle(sbd, oracle_mod, frac):
     olds, news = _param_list(6, MANY_SIZES, frac)
