@@ -36,6 +36,8 @@ def _load():
     lib.oracle_diff.restype = i64
     lib.oracle_diff_many.argtypes = [i32, vp, vp, vp, vp, vp, i64, vp, vp]
     lib.oracle_diff_many.restype = ctypes.c_int
+    lib.oracle_shard_delta_many.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, vp, vp]
+    lib.oracle_shard_delta_many.restype = ctypes.c_int
     lib.oracle_apply.argtypes = [vp, i64, vp, vp, i64]
     lib.oracle_apply.restype = ctypes.c_int
     lib.oracle_xor_mask.argtypes = [vp, vp, vp, i64]
@@ -105,6 +107,57 @@ def diff_many(olds, news, capacity=None):
         raise ValueError("oracle_diff_many rejected its arguments")
     m = min(int(offsets[k]), cap)
     return idx[:m].copy(), val[:m].copy(), nnz, offsets
+
+
+def shard_delta_many(olds, news, flat_offsets, capacity=None):
+    """Sharded batched diff: (gidx_cat int64, val_cat, nnz[k], offsets[k+1]),
+    gidx = flat_offsets[p] + local index."""
+    olds = [_u16(o) for o in olds]
+    news = [_u16(x) for x in news]
+    if len(olds) != len(news) or len(olds) != len(flat_offsets):
+        raise ValueError("parameter lists differ in length")
+    k = len(olds)
+    numels = np.array([o.size for o in olds], dtype=np.int64)
+    for o, x in zip(olds, news):
+        if o.size != x.size:
+            raise ValueError("old and new differ in size")
+    fo = np.ascontiguousarray(flat_offsets, dtype=np.int64)
+    total = int(numels.sum())
+    cap = total if capacity is None else int(capacity)
+    gidx = np.empty(max(cap, 1), dtype=np.int64)
+    val = np.empty(max(cap, 1), dtype=np.uint16)
+    nnz = np.zeros(k, dtype=np.int64)
+    offsets = np.zeros(k + 1, dtype=np.int64)
+    optrs = (ctypes.c_void_p * max(k, 1))(*[_ptr(o) for o in olds])
+    nptrs = (ctypes.c_void_p * max(k, 1))(*[_ptr(x) for x in news])
+    rc = _load().oracle_shard_delta_many(
+        k, ctypes.addressof(optrs), ctypes.addressof(nptrs), _ptr(numels), _ptr(fo),
+        _ptr(gidx), _ptr(val), cap, _ptr(nnz), _ptr(offsets))
+    if rc != 0:
+        raise ValueError("oracle_shard_delta_many rejected its arguments")
+    m = min(int(offsets[k]), cap)
+    return gidx[:m].copy(), val[:m].copy(), nnz, offsets
+
+
+def shard0_rows(rows: int, world: int, rank: int):
+    """(first_row, row_count) of `rank`'s Shard(0) piece of a dimension of
+    `rows` rows over `world` ranks: equal pieces of ceil(rows / world) rows,
+    the last ones shorter or empty ([VERL] spec.py `derive_placement`, which
+    takes the global offset of the FSDP2 Shard(0) placement)."""
+    if rows < 0 or world < 1 or not 0 <= rank < world:
+        raise ValueError("bad shard geometry")
+    piece = (rows + world - 1) // world
+    first = min(piece * rank, rows)
+    return first, min(piece, rows - first)
+
+
+def shard0_flat_offset(full_shape, first_row: int) -> int:
+    """Flat offset of a Shard(0) piece starting at `first_row`: that row times
+    the product of the other dimensions ([VERL] spec.py `derive_placement`)."""
+    inner = 1
+    for d in full_shape[1:]:
+        inner *= int(d)
+    return int(first_row) * inner
 
 
 def apply_(snap_bits, idx, val):

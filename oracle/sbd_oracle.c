@@ -106,6 +106,57 @@ int oracle_diff_many(int32_t nparams, const uint16_t *const *olds,
 }
 
 /*
+ * oracle_shard_delta_many -- the sharded form: each parameter is one rank's
+ * local shard of a larger parameter, and positions are made global.
+ *
+ * [VERL] code-snippet section, sparse_gather.py `shard_delta_indices`: the
+ * local shard is compared bytewise exactly like a whole tensor, and every
+ * local index is shifted by the shard's flat offset into the full parameter,
+ * widened to int64.  spec.py `derive_placement`: under Shard(0) that flat
+ * offset is the shard's first row times the product of the remaining
+ * dimensions (computed by the caller and passed in flat_offsets).
+ *
+ * Same layout as oracle_diff_many (list order, per-parameter counts and
+ * running offsets, at most `capacity` entries written, true counts always
+ * reported), except that gidx is int64 and holds flat_offsets[p] + i.
+ * Returns 0, or -1 on a negative or over-long shard or a negative offset.
+ *
+ * Pins: for row splits of a tensor as Shard(0) makes them (torch's own shard
+ * size/offset routine), the shards' outputs concatenated in rank order equal
+ * oracle_diff of the whole tensor, widened; an offset past 2^31 stays exact;
+ * offset 0 reproduces oracle_diff_many.
+ */
+int oracle_shard_delta_many(int32_t nparams, const uint16_t *const *olds,
+                            const uint16_t *const *news, const int64_t *numels,
+                            const int64_t *flat_offsets, int64_t *gidx, uint16_t *val,
+                            int64_t capacity, int64_t *nnz, int64_t *offsets)
+{
+    int32_t p;
+    int64_t i, k = 0;
+    if (nparams < 0)
+        return -1;
+    for (p = 0; p < nparams; ++p)
+        if (numels[p] < 0 || numels[p] > ORACLE_INT32_MAX || flat_offsets[p] < 0)
+            return -1;
+    for (p = 0; p < nparams; ++p) {
+        int64_t start = k;
+        offsets[p] = start;
+        for (i = 0; i < numels[p]; ++i) {
+            if (olds[p][i] != news[p][i]) {
+                if (k < capacity) {
+                    gidx[k] = flat_offsets[p] + i;
+                    val[k] = news[p][i];
+                }
+                ++k;
+            }
+        }
+        nnz[p] = k - start;
+    }
+    offsets[nparams] = k;
+    return 0;
+}
+
+/*
  * oracle_apply -- scatter the delta into the resident snapshot, in place.
  *
  * [TRL] section 4.3 (the vLLM-side extension): the receiver flattens its bf16

@@ -360,3 +360,87 @@ def test_step_pair_matches_rne_of_exact_step(oracle_mod):
         x32 = base.sub(u, alpha=1e-5)
         assert np.array_equal(oracle_mod.bf16_rne_array(x32.double().numpy()),
                               workloads.bits_numpy(new))
+
+
+# ----------------------------------------------------------------------------
+# sharded diff (VERL code-snippet section `shard_delta_indices`; spec.py
+# `derive_placement`)
+# ----------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("rows", [1, 7, 10, 64, 1000, 1003])
+@pytest.mark.parametrize("world", [1, 2, 3, 8, 16])
+def test_shard0_rows_match_torch_placement(oracle_mod, rows, world):
+    """The row split is torch's own Shard(0) size/offset rule."""
+    from torch.distributed.tensor.placement_types import Shard
+
+    for rank in range(world):
+        size, first = Shard.local_shard_size_and_offset(rows, world, rank)
+        assert oracle_mod.shard0_rows(rows, world, rank) == (first, size)
+
+
+def test_shard0_flat_offset_is_row_major_index(oracle_mod):
+    """The flat offset of a row is numpy's row-major index of [row, 0, ...]."""
+    for shape in [(10, 3), (7, 4, 5), (3, 1, 2, 9), (1000, 4096)]:
+        for row in range(0, shape[0], max(1, shape[0] // 5)):
+            want = int(np.ravel_multi_index((row,) + (0,) * (len(shape) - 1), shape))
+            assert oracle_mod.shard0_flat_offset(shape, row) == want
+
+
+@pytest.mark.parametrize("world", [1, 2, 3, 5, 8])
+def test_shard_deltas_concatenate_to_the_full_diff(oracle_mod, world):
+    """Every rank diffs only its Shard(0) rows; in rank order the global
+    positions and values are exactly the whole tensor's diff."""
+    rng = np.random.default_rng(world)
+    shapes = [(1003, 37), (64, 128), (5, 3, 7)]
+    olds, news = [], []
+    for sh in shapes:
+        o, x = rand_bits(rng, int(np.prod(sh)), 0.05, special=True)
+        olds.append(o)
+        news.append(x)
+    per_param = {p: ([], []) for p in range(len(shapes))}
+    for rank in range(world):
+        lo_list, ln_list, offs = [], [], []
+        for p, sh in enumerate(shapes):
+            first, count = oracle_mod.shard0_rows(sh[0], world, rank)
+            inner = int(np.prod(sh[1:]))
+            lo_list.append(olds[p][first * inner:(first + count) * inner])
+            ln_list.append(news[p][first * inner:(first + count) * inner])
+            offs.append(oracle_mod.shard0_flat_offset(sh, first))
+        gi, gv, nnz, off = oracle_mod.shard_delta_many(lo_list, ln_list, offs)
+        for p in range(len(shapes)):
+            per_param[p][0].append(gi[off[p]:off[p + 1]])
+            per_param[p][1].append(gv[off[p]:off[p + 1]])
+    for p in range(len(shapes)):
+        want = np.flatnonzero(olds[p].view(np.int16) != news[p].view(np.int16))
+        got_i = np.concatenate(per_param[p][0])
+        got_v = np.concatenate(per_param[p][1])
+        assert got_i.dtype == np.int64
+        assert np.array_equal(got_i, want)
+        assert np.array_equal(got_v, news[p][want])
+
+
+def test_shard_delta_offsets_past_int32(oracle_mod):
+    """A shard deep inside a huge parameter: positions past 2^31 are exact."""
+    rng = np.random.default_rng(9)
+    o, x = rand_bits(rng, 5000, 0.1)
+    base = (1 << 31) + 12345
+    gi, gv, nnz, off = oracle_mod.shard_delta_many([o, o], [x, x], [base, 3 * (1 << 32)])
+    local = np.flatnonzero(o != x)
+    assert gi.tolist() == [base + int(i) for i in local] + [3 * (1 << 32) + int(i) for i in local]
+    assert int(off[2]) == 2 * local.size
+
+
+def test_shard_delta_offset_zero_is_diff_many(oracle_mod):
+    rng = np.random.default_rng(4)
+    olds, news = zip(*[rand_bits(rng, s, 0.03) for s in (100, 0, 4097, 65)])
+    gi, gv, nnz, off = oracle_mod.shard_delta_many(olds, news, [0, 0, 0, 0])
+    ri, rv, rn, ro = oracle_mod.diff_many(olds, news)
+    assert np.array_equal(gi, ri.astype(np.int64))
+    assert np.array_equal(gv, rv) and np.array_equal(nnz, rn) and np.array_equal(off, ro)
+
+
+def test_shard_delta_rejects_negative_offset(oracle_mod):
+    a = np.zeros(4, dtype=np.uint16)
+    with pytest.raises(ValueError):
+        oracle_mod.shard_delta_many([a], [a], [-1])
