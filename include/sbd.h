@@ -120,6 +120,35 @@ delta_status delta_diff_many(int32_t nparams, const uint16_t *const *old_ptrs,
                              int64_t *offsets, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * delta_diff_many_sharded -- delta_diff_many over one rank's shards, with
+ * global positions.
+ *
+ * [VERL] code-snippet section, sparse_gather.py `shard_delta_indices`: a
+ * rank diffs its local shard bytewise and shifts every local index by the
+ * shard's flat offset into the full parameter, as int64.  spec.py
+ * `derive_placement`: under FSDP's Shard(0) that flat offset is the shard's
+ * first row times the product of the other dimensions.  Concatenating the
+ * ranks' outputs for a parameter in rank order gives the whole parameter's
+ * delta with no merge.
+ *
+ * Arguments as delta_diff_many, except:
+ *  numels              (host) elements of each LOCAL shard, each in
+ *                      [0, 2^31-1] (local positions are computed in int32).
+ *  flat_offsets        (host) int64[nparams], each >= 0: the shard's offset
+ *                      into its full parameter.
+ *  idx                 int64 output: flat_offsets[p] + local index.
+ * Same workspace size, capacity protocol and counts/offsets as
+ * delta_diff_many.
+ * Errors: as delta_diff_many, plus DELTA_E_INVALID for a null flat_offsets or
+ * a negative offset, DELTA_E_RANGE when offset + numel overflows int64.
+ */
+delta_status delta_diff_many_sharded(int32_t nparams, const uint16_t *const *old_ptrs,
+                                     const uint16_t *const *new_ptrs, const int64_t *numels,
+                                     const int64_t *flat_offsets, int64_t *idx, uint16_t *val,
+                                     int64_t capacity, int64_t *nnz, int64_t *offsets,
+                                     void *ws, size_t ws_bytes, void *stream);
+
+/*
  * delta_apply -- scatter a delta into a resident bf16 snapshot, in place.
  *
  * [TRL] section 4.3 (vLLM side): the receiver assigns the values at the

@@ -20,8 +20,10 @@ from .ops import (  # noqa: F401
     xor_apply_,
     xor_mask,
 )
+from .sharding import flat_offset, shard0_piece  # noqa: F401
 
 __all__ = [
     "DeltaError", "DeltaRangeError", "load", "diff", "diff_many", "apply_", "apply_many_",
     "xor_mask", "xor_apply_", "workspace", "workspace_size", "default_capacity",
+    "shard0_piece", "flat_offset",
 ]

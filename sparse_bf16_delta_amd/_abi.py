@@ -39,6 +39,8 @@ SIGNATURES = {
     "delta_workspace_size": (_sz, [_i64, _i32]),
     "delta_diff": (_st, [_vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "delta_diff_many": (_st, [_i32, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "delta_diff_many_sharded": (_st, [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
+                                      _sz, _vp]),
     "delta_apply": (_st, [_vp, _i64, _vp, _vp, _i64, _vp, _vp]),
     "delta_apply_many": (_st, [_i32, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "xor_mask": (_st, [_vp, _vp, _vp, _i64, _vp]),

@@ -1,6 +1,7 @@
 // abi.hip -- the extern "C" entry points declared in include/sbd.h:
 // argument validation, workspace layout, parameter-table upload and launch.
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <string>
 #include <vector>
@@ -55,7 +56,16 @@ WsLayout ws_layout(int64_t max_tiles, int32_t nparams) {
   L.tile_desc = L.dense_list + align256(sizeof(int32_t) * tiles);
   L.table = L.tile_desc + align256(sizeof(TileDesc) * tiles);
   const size_t entry = sizeof(DiffParam) > sizeof(SnapParam) ? sizeof(DiffParam) : sizeof(SnapParam);
-  L.compact = L.table + align256(entry * size_t(nparams > 0 ? nparams : 1));
+  // The slots start a fixed 9472 bytes past a 1 MB boundary of the workspace,
+  // whatever the table sizes before them.  Where the 4 KB compact slots fall
+  // relative to HBM's channel interleave measurably changes the cost of the
+  // count kernel's slot writes; on the 7B-shaped list (diff_many, ms): 1 MB
+  // aligned 4.64, +256 B 4.66, +1280 B 4.56, +2048 B 4.65, +9472 B 4.55
+  // (the best of those tried; rotating each tile's start in its slot was
+  // worse still).
+  constexpr size_t kSlotAlign = size_t(1) << 20, kSlotSkew = 9472;
+  L.compact = (L.table + align256(entry * size_t(nparams > 0 ? nparams : 1)) + kSlotAlign - 1) /
+                  kSlotAlign * kSlotAlign + kSlotSkew;
   L.wide = L.compact + sizeof(uint32_t) * size_t(kCompactWords) * tiles;
   L.total = L.wide + sizeof(uint32_t) * size_t(kWideWords) * tiles;
   return L;
@@ -91,62 +101,98 @@ delta_status delta_diff(const uint16_t* old_bits, const uint16_t* new_bits, int6
   if (ws == nullptr || ws_bytes < L.total)
     return fail(DELTA_E_WORKSPACE, "delta_diff: workspace %zu bytes, need %zu", ws_bytes,
                 L.total);
-  sbd::DiffParam single{old_bits, new_bits, n, 0};
+  sbd::DiffParam single{old_bits, new_bits, n, 0, 0};
   const int64_t tiles = (n + sbd::kDiffTile - 1) / sbd::kDiffTile;  // < kMaxTiles for n < 2^31
   g_error.clear();
-  return hip_status(sbd::launch_diff(nullptr, single, 1, tiles, idx, val, capacity, nnz, nullptr,
-                                     ws, L, static_cast<hipStream_t>(stream)),
+  return hip_status(sbd::launch_diff(nullptr, single, 1, tiles, idx, false, val, capacity, nnz,
+                                     nullptr, ws, L, static_cast<hipStream_t>(stream)),
                     "delta_diff launch");
 }
 
-delta_status delta_diff_many(int32_t nparams, const uint16_t* const* old_ptrs,
-                             const uint16_t* const* new_ptrs, const int64_t* numels,
-                             int32_t* idx, uint16_t* val, int64_t capacity, int64_t* nnz,
-                             int64_t* offsets, void* ws, size_t ws_bytes, void* stream) {
-  if (nparams < 0) return fail(DELTA_E_INVALID, "delta_diff_many: nparams=%d < 0", nparams);
-  if (capacity < 0)
-    return fail(DELTA_E_INVALID, "delta_diff_many: capacity=%lld < 0", (long long)capacity);
-  if (offsets == nullptr) return fail(DELTA_E_INVALID, "delta_diff_many: offsets is null");
+}  // extern "C"
+
+namespace {
+
+// delta_diff_many and delta_diff_many_sharded: validation, table upload and
+// launch.  global_idx: int64 indices flat_offsets[p] + local index, else
+// parameter-local int32 indices.
+delta_status diff_many_impl(const char* fn, bool global_idx, int32_t nparams,
+                            const uint16_t* const* old_ptrs, const uint16_t* const* new_ptrs,
+                            const int64_t* numels, const int64_t* flat_offsets, void* idx,
+                            uint16_t* val,
+                            int64_t capacity, int64_t* nnz, int64_t* offsets, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (nparams < 0) return fail(DELTA_E_INVALID, "%s: nparams=%d < 0", fn, nparams);
+  if (capacity < 0) return fail(DELTA_E_INVALID, "%s: capacity=%lld < 0", fn, (long long)capacity);
+  if (offsets == nullptr) return fail(DELTA_E_INVALID, "%s: offsets is null", fn);
   if (nparams > 0 && (old_ptrs == nullptr || new_ptrs == nullptr || numels == nullptr ||
                       nnz == nullptr))
-    return fail(DELTA_E_INVALID, "delta_diff_many: null parameter array");
+    return fail(DELTA_E_INVALID, "%s: null parameter array", fn);
+  if (global_idx && nparams > 0 && flat_offsets == nullptr)
+    return fail(DELTA_E_INVALID, "%s: flat_offsets is null", fn);
   std::vector<sbd::DiffParam> table(static_cast<size_t>(nparams > 0 ? nparams : 0));
   int64_t total = 0, tiles = 0;
   for (int32_t p = 0; p < nparams; ++p) {
     const int64_t n = numels[p];
-    if (n < 0)
-      return fail(DELTA_E_INVALID, "delta_diff_many: numels[%d]=%lld < 0", p, (long long)n);
+    if (n < 0) return fail(DELTA_E_INVALID, "%s: numels[%d]=%lld < 0", fn, p, (long long)n);
     if (n > kInt32Max)
-      return fail(DELTA_E_RANGE, "delta_diff_many: numels[%d]=%lld exceeds the int32 index range",
-                  p, (long long)n);
+      return fail(DELTA_E_RANGE, "%s: numels[%d]=%lld exceeds the int32 index range", fn, p,
+                  (long long)n);
     if (n > 0 && (old_ptrs[p] == nullptr || new_ptrs[p] == nullptr))
-      return fail(DELTA_E_INVALID, "delta_diff_many: null tensor pointer for parameter %d", p);
-    table[p] = sbd::DiffParam{old_ptrs[p], new_ptrs[p], n, tiles};
+      return fail(DELTA_E_INVALID, "%s: null tensor pointer for parameter %d", fn, p);
+    int64_t fo = 0;
+    if (global_idx) {
+      fo = flat_offsets[p];
+      if (fo < 0)
+        return fail(DELTA_E_INVALID, "%s: flat_offsets[%d]=%lld < 0", fn, p, (long long)fo);
+      if (fo > INT64_MAX - n)
+        return fail(DELTA_E_RANGE, "%s: flat_offsets[%d] + numel overflows int64", fn, p);
+    }
+    table[p] = sbd::DiffParam{old_ptrs[p], new_ptrs[p], n, tiles, fo};
     tiles += (n + sbd::kDiffTile - 1) / sbd::kDiffTile;
     total += n;
   }
   if (capacity > 0 && (idx == nullptr || val == nullptr))
-    return fail(DELTA_E_INVALID, "delta_diff_many: null output with capacity=%lld",
-                (long long)capacity);
+    return fail(DELTA_E_INVALID, "%s: null output with capacity=%lld", fn, (long long)capacity);
   if (tiles >= sbd::kMaxTiles)
-    return fail(DELTA_E_RANGE, "delta_diff_many: %lld tiles exceed one launch (%lld)",
-                (long long)tiles, (long long)sbd::kMaxTiles);
+    return fail(DELTA_E_RANGE, "%s: %lld tiles exceed one launch (%lld)", fn, (long long)tiles,
+                (long long)sbd::kMaxTiles);
   const sbd::WsLayout L = sbd::ws_layout(sbd::max_tiles_for(total, nparams), nparams);
   if (ws == nullptr || ws_bytes < L.total)
-    return fail(DELTA_E_WORKSPACE, "delta_diff_many: workspace %zu bytes, need %zu", ws_bytes,
-                L.total);
+    return fail(DELTA_E_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, L.total);
   hipStream_t s = static_cast<hipStream_t>(stream);
   sbd::DiffParam* d_table = reinterpret_cast<sbd::DiffParam*>(static_cast<char*>(ws) + L.table);
   if (nparams > 0) {
     const hipError_t e = hipMemcpyAsync(d_table, table.data(), sizeof(sbd::DiffParam) * table.size(),
                                         hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return hip_status(e, "delta_diff_many table copy");
+    if (e != hipSuccess) return hip_status(e, "table copy");
   }
   g_error.clear();
-  sbd::DiffParam none{nullptr, nullptr, 0, 0};
+  sbd::DiffParam none{nullptr, nullptr, 0, 0, 0};
   return hip_status(sbd::launch_diff(nparams > 0 ? d_table : nullptr, none, nparams, tiles, idx,
-                                     val, capacity, nnz, offsets, ws, L, s),
-                    "delta_diff_many launch");
+                                     global_idx, val, capacity, nnz, offsets, ws, L, s),
+                    fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+delta_status delta_diff_many(int32_t nparams, const uint16_t* const* old_ptrs,
+                             const uint16_t* const* new_ptrs, const int64_t* numels,
+                             int32_t* idx, uint16_t* val, int64_t capacity, int64_t* nnz,
+                             int64_t* offsets, void* ws, size_t ws_bytes, void* stream) {
+  return diff_many_impl("delta_diff_many", false, nparams, old_ptrs, new_ptrs, numels, nullptr,
+                        idx, val, capacity, nnz, offsets, ws, ws_bytes, stream);
+}
+
+delta_status delta_diff_many_sharded(int32_t nparams, const uint16_t* const* old_ptrs,
+                                     const uint16_t* const* new_ptrs, const int64_t* numels,
+                                     const int64_t* flat_offsets, int64_t* idx, uint16_t* val,
+                                     int64_t capacity, int64_t* nnz, int64_t* offsets, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  return diff_many_impl("delta_diff_many_sharded", true, nparams, old_ptrs, new_ptrs, numels,
+                        flat_offsets, idx, val, capacity, nnz, offsets, ws, ws_bytes, stream);
 }
 
 delta_status delta_apply(uint16_t* snapshot, int64_t n, const int32_t* idx, const uint16_t* val,

@@ -103,19 +103,6 @@ __device__ __forceinline__ T wave_inclusive(T v, int lane) {
 }
 
 template <int S>
-__device__ __forceinline__ void emit_slot(uint32_t mm, uint64_t& pos, int64_t ebase,
-                                          const uint4& x, int32_t* __restrict__ idx,
-                                          uint16_t* __restrict__ val, uint64_t cap) {
-  if (mm & (1u << S)) {
-    if (pos < cap) {
-      idx[pos] = static_cast<int32_t>(ebase + S);
-      val[pos] = half_of<S>(x);
-    }
-    ++pos;
-  }
-}
-
-template <int S>
 __device__ __forceinline__ void stage_slot(uint32_t mm, uint32_t& pos, uint32_t local,
                                            const uint4& x, uint32_t* stage) {
   if (mm & (1u << S)) {
@@ -140,8 +127,9 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ base, i
 struct TileView {
   const uint16_t* ob;
   const uint16_t* nb;
-  int32_t e0;     // parameter-local index of the tile's first element
-  int32_t valid;  // elements of the tile inside the parameter
+  int32_t e0;           // parameter-local index of the tile's first element
+  int32_t valid;        // elements of the tile inside the parameter
+  int64_t flat_offset;  // the parameter's flat offset (sharded form)
 };
 
 template <bool kMany>
@@ -154,6 +142,7 @@ __device__ __forceinline__ TileView tile_view(const TileDesc* __restrict__ tdesc
     v.nb = td.new_bits;
     v.e0 = td.e0;
     v.valid = td.valid;
+    v.flat_offset = td.flat_offset;
   } else {
     const int64_t first = t * kDiffTile;
     const int64_t left = single.numel - first;
@@ -161,6 +150,7 @@ __device__ __forceinline__ TileView tile_view(const TileDesc* __restrict__ tdesc
     v.nb = single.new_bits + first;
     v.e0 = static_cast<int32_t>(first);
     v.valid = static_cast<int32_t>(left < kDiffTile ? left : kDiffTile);
+    v.flat_offset = 0;
   }
   return v;
 }
@@ -218,7 +208,7 @@ __global__ __launch_bounds__(256) void diff_prepare_kernel(const DiffParam* __re
     td.new_bits = d.new_bits + e0;
     td.e0 = static_cast<int32_t>(e0);
     td.valid = static_cast<int32_t>(left < kDiffTile ? left : kDiffTile);
-    td.pad = 0;
+    td.flat_offset = d.flat_offset;
     tdesc[t] = td;
   }
 }
@@ -402,15 +392,16 @@ __global__ __launch_bounds__(kScanBlock) void diff_base_kernel(
 // their final positions.  Consecutive tiles have consecutive outputs, so the
 // staged tiles' entries are walked as one flat run (dense tiles, written by
 // diff_dense_kernel, and empty ones are left out of it).
-template <bool kMany>
+template <bool kMany, typename IdxT>
 __global__ __launch_bounds__(kDiffBlock) void diff_place_kernel(
     const TileDesc* __restrict__ tdesc, int64_t total_tiles, int32_t nchunks, int32_t tiles_per_wg,
     const uint32_t* __restrict__ inpfx, const uint64_t* __restrict__ chunk_base,
     const uint32_t* __restrict__ compact, const uint32_t* __restrict__ wide,
-    int32_t* __restrict__ idx, uint16_t* __restrict__ val, int64_t capacity) {
+    IdxT* __restrict__ idx, uint16_t* __restrict__ val, int64_t capacity) {
+  static_assert(sizeof(IdxT) == 8 ? kMany : true, "global indices need a parameter table");
   constexpr int kUnroll = 4;
   __shared__ uint64_t s_off[kPlaceTiles + 1];  // output offset of each tile
-  __shared__ int32_t s_e0[kPlaceTiles];
+  __shared__ IdxT s_first[kPlaceTiles];  // index written for the tile's first element
   __shared__ uint32_t s_run[kPlaceTiles + 1];  // start of the m-th staged tile in the flat run
   __shared__ int32_t s_tile[kPlaceTiles];      // which tile that is
   __shared__ int32_t s_nrun;
@@ -421,7 +412,16 @@ __global__ __launch_bounds__(kDiffBlock) void diff_place_kernel(
   if (tid <= nt) {
     const int64_t t = t0 + tid;
     s_off[tid] = t < total_tiles ? chunk_base[t / kScanChunk] + inpfx[t] : chunk_base[nchunks];
-    if (tid < nt) s_e0[tid] = kMany ? tdesc[t].e0 : static_cast<int32_t>(t * kDiffTile);
+    if (tid < nt) {
+      if constexpr (kMany) {
+        if constexpr (sizeof(IdxT) == 8)
+          s_first[tid] = tdesc[t].flat_offset + tdesc[t].e0;
+        else
+          s_first[tid] = tdesc[t].e0;
+      } else {
+        s_first[tid] = static_cast<IdxT>(t * kDiffTile);
+      }
+    }
   }
   __syncthreads();
   if (tid == 0) {
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(kDiffBlock) void diff_place_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       if (ok[u]) {
-        idx[jj[u]] = s_e0[kk[u]] + static_cast<int32_t>(w[u] >> 16);
+        idx[jj[u]] = s_first[kk[u]] + static_cast<IdxT>(w[u] >> 16);
         val[jj[u]] = static_cast<uint16_t>(w[u] & 0xFFFFu);
       }
     }
@@ -479,12 +479,13 @@ __global__ __launch_bounds__(kDiffBlock) void diff_place_kernel(
 // changed 16-byte chunks of `new`.  Each of the tile's kDiffIters iterations
 // (at most kDiffBlock * kVec entries) is staged in LDS and copied out with
 // coalesced stores.
-template <bool kMany>
+template <bool kMany, typename IdxT>
 __global__ __launch_bounds__(kDiffBlock) void diff_dense_kernel(
     const TileDesc* __restrict__ tdesc, DiffParam single, const int32_t* __restrict__ dense_list,
     const uint32_t* __restrict__ ndense, const uint32_t* __restrict__ inpfx,
     const uint64_t* __restrict__ chunk_base, const uint32_t* __restrict__ compact,
-    int32_t* __restrict__ idx, uint16_t* __restrict__ val, int64_t capacity) {
+    IdxT* __restrict__ idx, uint16_t* __restrict__ val, int64_t capacity) {
+  static_assert(sizeof(IdxT) == 8 ? kMany : true, "global indices need a parameter table");
   static_assert(kDiffBlock * kVec <= kStageCap, "one iteration of a tile fits the stage");
   __shared__ __attribute__((aligned(16))) uint32_t s_stage[kDiffBlock * kVec];
   __shared__ uint32_t s_wtot[kGroups];
@@ -513,6 +514,8 @@ __global__ __launch_bounds__(kDiffBlock) void diff_dense_kernel(
     uint32_t lp[kDiffIters], goff[kDiffIters], agg, gexcl;
     tile_offsets(m, lp, goff, agg, gexcl, s_wtot, lane, wave);
     const uint64_t tbase = chunk_base[t / kScanChunk] + inpfx[t];
+    const IdxT first = sizeof(IdxT) == 8 ? static_cast<IdxT>(tv.flat_offset + tv.e0)
+                                         : static_cast<IdxT>(tv.e0);
 #pragma unroll
     for (int j = 0; j < kDiffIters; ++j) {
       // entries of iteration j occupy [jb, je) of the tile's output
@@ -539,7 +542,7 @@ __global__ __launch_bounds__(kDiffBlock) void diff_dense_kernel(
         const uint64_t o = tbase + jb + p;
         if (o < cap) {
           const uint32_t w = s_stage[p];
-          idx[o] = tv.e0 + static_cast<int32_t>(w >> 16);
+          idx[o] = first + static_cast<IdxT>(w >> 16);
           val[o] = static_cast<uint16_t>(w & 0xFFFFu);
         }
       }
@@ -551,14 +554,14 @@ __global__ __launch_bounds__(kDiffBlock) void diff_dense_kernel(
 // Workgroups of diff_dense_kernel<kMany> that are resident at once on the
 // current device: its grid-stride loop hands each workgroup the same share of
 // dense tiles, so a larger grid would leave a tail.  Queried once per device.
-template <bool kMany>
+template <bool kMany, typename IdxT>
 int64_t dense_grid_limit() {
   static int64_t cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   if (cached[dev] == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, diff_dense_kernel<kMany>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, diff_dense_kernel<kMany, IdxT>,
                                                      kDiffBlock, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         per_cu < 1 || cus < 1) {
@@ -572,10 +575,35 @@ int64_t dense_grid_limit() {
 
 }  // namespace
 
+namespace {
+
+// Phase 3: place the staged entries, then the dense tiles.
+template <bool kMany, typename IdxT>
+void launch_place(const TileDesc* tdesc, const DiffParam& single, int64_t total_tiles,
+                  int32_t nchunks, const uint32_t* inpfx, const uint64_t* chunk_base,
+                  const uint32_t* compact, const uint32_t* wide, const int32_t* dense_list,
+                  const uint32_t* ndense, IdxT* idx, uint16_t* val, int64_t capacity,
+                  hipStream_t stream) {
+  // enough placing workgroups to fill the GPU, up to kPlaceTiles tiles each
+  int64_t per_wg = total_tiles / 2048;
+  per_wg = per_wg < 1 ? 1 : (per_wg > kPlaceTiles ? kPlaceTiles : per_wg);
+  const unsigned place_grid = static_cast<unsigned>((total_tiles + per_wg - 1) / per_wg);
+  const int64_t dense_max = dense_grid_limit<kMany, IdxT>();
+  const unsigned dense_grid =
+      static_cast<unsigned>(total_tiles < dense_max ? total_tiles : dense_max);
+  diff_place_kernel<kMany, IdxT><<<dim3(place_grid), dim3(kDiffBlock), 0, stream>>>(
+      tdesc, total_tiles, nchunks, static_cast<int32_t>(per_wg), inpfx, chunk_base, compact, wide,
+      idx, val, capacity);
+  diff_dense_kernel<kMany, IdxT><<<dim3(dense_grid), dim3(kDiffBlock), 0, stream>>>(
+      tdesc, single, dense_list, ndense, inpfx, chunk_base, compact, idx, val, capacity);
+}
+
+}  // namespace
+
 hipError_t launch_diff(const DiffParam* d_table, const DiffParam& single, int32_t nparams,
-                       int64_t total_tiles, int32_t* idx, uint16_t* val, int64_t capacity,
-                       int64_t* nnz, int64_t* offsets, void* ws, const WsLayout& L,
-                       hipStream_t stream) {
+                       int64_t total_tiles, void* idx, bool global_idx, uint16_t* val,
+                       int64_t capacity, int64_t* nnz, int64_t* offsets, void* ws,
+                       const WsLayout& L, hipStream_t stream) {
   char* base = static_cast<char*>(ws);
   uint32_t* ndense = reinterpret_cast<uint32_t*>(base + L.ndense);
   uint32_t* counts = reinterpret_cast<uint32_t*>(base + L.counts);
@@ -587,8 +615,9 @@ hipError_t launch_diff(const DiffParam* d_table, const DiffParam& single, int32_
   uint32_t* compact = reinterpret_cast<uint32_t*>(base + L.compact);
   uint32_t* wide = reinterpret_cast<uint32_t*>(base + L.wide);
   // d_table == nullptr: one tensor (nparams == 1, `single`) or an empty list
-  // (nparams == 0, no tiles).
+  // (nparams == 0, no tiles).  Global indices come with a table only.
   const bool many = d_table != nullptr;
+  if (global_idx && !many && total_tiles > 0) return hipErrorInvalidValue;
   const int32_t nchunks = static_cast<int32_t>((total_tiles + kScanChunk - 1) / kScanChunk);
   const unsigned grid = static_cast<unsigned>(total_tiles);  // total_tiles < kMaxTiles
 
@@ -614,26 +643,18 @@ hipError_t launch_diff(const DiffParam* d_table, const DiffParam& single, int32_
     diff_base_kernel<false><<<dim3(1), dim3(kScanBlock), 0, stream>>>(
         nullptr, nparams, total_tiles, nchunks, inpfx, chunk_tot, chunk_base, nnz, offsets);
   if (total_tiles > 0) {
-    // enough placing workgroups to fill the GPU, up to kPlaceTiles tiles each
-    int64_t per_wg = total_tiles / 2048;
-    per_wg = per_wg < 1 ? 1 : (per_wg > kPlaceTiles ? kPlaceTiles : per_wg);
-    const unsigned place_grid = static_cast<unsigned>((total_tiles + per_wg - 1) / per_wg);
-    const int64_t dense_max = many ? dense_grid_limit<true>() : dense_grid_limit<false>();
-    const unsigned dense_grid =
-        static_cast<unsigned>(total_tiles < dense_max ? total_tiles : dense_max);
-    if (many) {
-      diff_place_kernel<true><<<dim3(place_grid), dim3(kDiffBlock), 0, stream>>>(
-          tdesc, total_tiles, nchunks, static_cast<int32_t>(per_wg), inpfx, chunk_base, compact,
-          wide, idx, val, capacity);
-      diff_dense_kernel<true><<<dim3(dense_grid), dim3(kDiffBlock), 0, stream>>>(
-          tdesc, single, dense_list, ndense, inpfx, chunk_base, compact, idx, val, capacity);
-    } else {
-      diff_place_kernel<false><<<dim3(place_grid), dim3(kDiffBlock), 0, stream>>>(
-          nullptr, total_tiles, nchunks, static_cast<int32_t>(per_wg), inpfx, chunk_base, compact,
-          wide, idx, val, capacity);
-      diff_dense_kernel<false><<<dim3(dense_grid), dim3(kDiffBlock), 0, stream>>>(
-          nullptr, single, dense_list, ndense, inpfx, chunk_base, compact, idx, val, capacity);
-    }
+    if (many && global_idx)
+      launch_place<true, int64_t>(tdesc, single, total_tiles, nchunks, inpfx, chunk_base, compact,
+                                  wide, dense_list, ndense, static_cast<int64_t*>(idx), val,
+                                  capacity, stream);
+    else if (many)
+      launch_place<true, int32_t>(tdesc, single, total_tiles, nchunks, inpfx, chunk_base, compact,
+                                  wide, dense_list, ndense, static_cast<int32_t*>(idx), val,
+                                  capacity, stream);
+    else
+      launch_place<false, int32_t>(tdesc, single, total_tiles, nchunks, inpfx, chunk_base, compact,
+                                   wide, dense_list, ndense, static_cast<int32_t*>(idx), val,
+                                   capacity, stream);
   }
   return hipGetLastError();
 }

@@ -55,12 +55,13 @@ constexpr int64_t kDiffTile = int64_t(kDiffBlock) * kVec * kDiffIters;  // 32768
 // work-items.  2^23 tiles are 2.7e11 elements, more than HBM holds twice.
 constexpr int64_t kMaxTiles = int64_t(1) << 23;
 
-// Parameter descriptor as stored in the workspace (32 bytes).
+// Parameter descriptor as stored in the workspace (40 bytes).
 struct DiffParam {
   const uint16_t* old_bits;
   const uint16_t* new_bits;
   int64_t numel;
   int64_t first_tile;
+  int64_t flat_offset;  // added to every index in the sharded form (else 0)
 };
 
 // Per-tile descriptor written by the prepare kernel (32 bytes).
@@ -69,7 +70,7 @@ struct TileDesc {
   const uint16_t* new_bits;
   int32_t e0;                // parameter-local index of that element
   int32_t valid;             // elements of the tile inside the parameter
-  int64_t pad;
+  int64_t flat_offset;       // the parameter's flat offset (sharded form)
 };
 
 // A tile with at most kStageCap changes is staged in LDS (4 bytes per entry)
@@ -113,10 +114,12 @@ WsLayout ws_layout(int64_t max_tiles, int32_t nparams);
 int64_t max_tiles_for(int64_t total_elems, int32_t nparams);
 
 // Launchers return hipSuccess or the launch error.
+// idx is int32_t[capacity] (parameter-local indices) or, with global_idx,
+// int64_t[capacity] holding flat_offset + local index (parameter lists only).
 hipError_t launch_diff(const DiffParam* d_table, const DiffParam& single, int32_t nparams,
-                       int64_t total_tiles, int32_t* idx, uint16_t* val, int64_t capacity,
-                       int64_t* nnz, int64_t* offsets, void* ws, const WsLayout& L,
-                       hipStream_t stream);
+                       int64_t total_tiles, void* idx, bool global_idx, uint16_t* val,
+                       int64_t capacity, int64_t* nnz, int64_t* offsets, void* ws,
+                       const WsLayout& L, hipStream_t stream);
 
 hipError_t launch_apply(const SnapParam* d_table, const SnapParam& single, int32_t nparams,
                         const int64_t* offsets, const int32_t* idx, const uint16_t* val,

@@ -105,13 +105,20 @@ def diff(old: torch.Tensor, new: torch.Tensor, capacity: int | None = None):
 
 
 def diff_many(olds: Sequence[torch.Tensor], news: Sequence[torch.Tensor],
-              capacity: int | None = None):
-    """Batched diff: (idx_cat int32, val_cat bf16, nnz int64[P], offsets int64[P+1]),
-    parameter-local indices concatenated in list order."""
+              capacity: int | None = None, flat_offsets: Sequence[int] | None = None):
+    """Batched diff: (idx_cat, val_cat bf16, nnz int64[P], offsets int64[P+1]),
+    concatenated in list order.  idx_cat holds int32 parameter-local indices,
+    or, when flat_offsets is given (each parameter is a rank's shard of a
+    larger one), int64 global positions flat_offsets[p] + local index."""
     if len(olds) != len(news):
         raise ValueError("olds and news differ in length")
     if not olds:
         raise ValueError("empty parameter list")
+    if flat_offsets is not None:
+        if len(flat_offsets) != len(olds):
+            raise ValueError("flat_offsets and the parameter list differ in length")
+        if any(int(f) < 0 for f in flat_offsets):
+            raise ValueError("flat offsets must be >= 0")
     dev = olds[0].device
     numels = []
     for p, (o, x) in enumerate(zip(olds, news)):
@@ -131,11 +138,19 @@ def diff_many(olds: Sequence[torch.Tensor], news: Sequence[torch.Tensor],
     nums = (ctypes.c_int64 * k)(*numels)
     nnz = torch.empty(k, dtype=torch.int64, device=dev)
     offsets = torch.empty(k + 1, dtype=torch.int64, device=dev)
+    fos = None if flat_offsets is None else (ctypes.c_int64 * k)(*[int(f) for f in flat_offsets])
+    idx_dtype = torch.int32 if fos is None else torch.int64
     while True:
-        idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+        idx = torch.empty(max(cap, 1), dtype=idx_dtype, device=dev)
         val = torch.empty(max(cap, 1), dtype=torch.bfloat16, device=dev)
-        check(lib.delta_diff_many(k, optrs, nptrs, nums, _ptr(idx), _ptr(val), cap, _ptr(nnz),
-                                  _ptr(offsets), _ptr(ws), ws.numel(), _stream(dev)))
+        if fos is None:
+            check(lib.delta_diff_many(k, optrs, nptrs, nums, _ptr(idx), _ptr(val), cap,
+                                      _ptr(nnz), _ptr(offsets), _ptr(ws), ws.numel(),
+                                      _stream(dev)))
+        else:
+            check(lib.delta_diff_many_sharded(k, optrs, nptrs, nums, fos, _ptr(idx), _ptr(val),
+                                              cap, _ptr(nnz), _ptr(offsets), _ptr(ws),
+                                              ws.numel(), _stream(dev)))
         t = int(offsets[k].item())  # the one device->host read
         if t <= cap:
             return idx[:t], val[:t], nnz, offsets

@@ -23,7 +23,10 @@ class DiffPlan:
     """Sender side: delta_diff_many over fixed (old, new) snapshot lists."""
 
     def __init__(self, olds: Sequence[torch.Tensor], news: Sequence[torch.Tensor],
-                 capacity: int):
+                 capacity: int, flat_offsets: Sequence[int] | None = None):
+        """flat_offsets: each parameter is a rank's shard of a larger one,
+        starting at that flat offset; the delta then holds int64 global
+        positions (delta_diff_many_sharded)."""
         if len(olds) != len(news) or not olds:
             raise ValueError("need two equally long, non-empty parameter lists")
         self.device = olds[0].device
@@ -44,17 +47,30 @@ class DiffPlan:
         lib = load()
         dev = self.device
         self.ws = torch.empty(lib.delta_workspace_size(self.total, k), dtype=torch.uint8, device=dev)
-        self.idx = torch.empty(max(self.capacity, 1), dtype=torch.int32, device=dev)
+        if flat_offsets is not None and (len(flat_offsets) != k or
+                                         any(int(f) < 0 for f in flat_offsets)):
+            raise ValueError("need one flat offset >= 0 per parameter")
+        self._fos = None if flat_offsets is None else (ctypes.c_int64 * k)(*map(int, flat_offsets))
+        self.idx = torch.empty(max(self.capacity, 1),
+                               dtype=torch.int32 if self._fos is None else torch.int64, device=dev)
         self.val = torch.empty(max(self.capacity, 1), dtype=torch.bfloat16, device=dev)
         self.nnz = torch.empty(k, dtype=torch.int64, device=dev)
         self.offsets = torch.empty(k + 1, dtype=torch.int64, device=dev)
 
     def run(self):
         """Enqueue the diff on the current stream; returns without syncing."""
-        check(load().delta_diff_many(self.nparams, self._optrs, self._nptrs, self._nums,
-                                     _ptr(self.idx), _ptr(self.val), self.capacity,
-                                     _ptr(self.nnz), _ptr(self.offsets), _ptr(self.ws),
-                                     self.ws.numel(), _stream(self.device)))
+        lib = load()
+        if self._fos is None:
+            check(lib.delta_diff_many(self.nparams, self._optrs, self._nptrs, self._nums,
+                                      _ptr(self.idx), _ptr(self.val), self.capacity,
+                                      _ptr(self.nnz), _ptr(self.offsets), _ptr(self.ws),
+                                      self.ws.numel(), _stream(self.device)))
+        else:
+            check(lib.delta_diff_many_sharded(self.nparams, self._optrs, self._nptrs, self._nums,
+                                              self._fos, _ptr(self.idx), _ptr(self.val),
+                                              self.capacity, _ptr(self.nnz), _ptr(self.offsets),
+                                              _ptr(self.ws), self.ws.numel(),
+                                              _stream(self.device)))
 
     def changed(self) -> int:
         """True total count of the last run (one device-to-host read)."""

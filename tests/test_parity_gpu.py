@@ -148,6 +148,82 @@ def test_diff_tile_kinds_capacity(sbd, oracle_mod, cut):
     assert bool((idx[cut:] == -7).all()) and bool((val[cut:] == -7).all())
 
 
+@pytest.mark.parametrize("pad", [0, 3])
+def test_diff_many_sharded_matches_oracle(sbd, oracle_mod, pad):
+    """Global int64 positions: every tile kind, offsets past 2^31, unaligned."""
+    old, new = tile_kinds_case(31 + pad)
+    olds = [old[:TILE * 3], old, old[5:TILE + 9], old[:0], old[TILE:]]
+    news = [new[:TILE * 3], new, new[5:TILE + 9], new[:0], new[TILE:]]
+    offs = [0, (1 << 31) + 7, 5 * (1 << 33) + 3, 123, 1 << 40]
+    ri, rv, rn, ro = oracle_mod.shard_delta_many(olds, news, offs)
+    gi, gv, gn, go = sbd.diff_many([gpu_bits(o, pad) for o in olds],
+                                   [gpu_bits(x, pad) for x in news], flat_offsets=offs)
+    assert gi.dtype == torch.int64
+    assert np.array_equal(gn.cpu().numpy(), rn)
+    assert np.array_equal(go.cpu().numpy(), ro)
+    assert np.array_equal(gi.cpu().numpy(), ri)
+    assert np.array_equal(np_bits(gv), rv)
+
+
+@pytest.mark.parametrize("world", [1, 3, 8])
+def test_sharded_ranks_concatenate_to_full_delta(sbd, oracle_mod, world):
+    """Each rank diffs its Shard(0) rows of three parameters on the GPU; in
+    rank order the global positions are the whole parameters' deltas."""
+    rng = np.random.default_rng(world)
+    shapes = [(1003, 64), (4096, 40), (7, 3, 11)]
+    fulls = []
+    for sh in shapes:
+        o, x = rand_case(int(rng.integers(1 << 20)), int(np.prod(sh)), 0.04, special=False)
+        fulls.append((o, x))
+    got = {p: ([], []) for p in range(len(shapes))}
+    for rank in range(world):
+        lo, ln, offs = [], [], []
+        for p, sh in enumerate(shapes):
+            first, count = sbd.shard0_piece(sh[0], world, rank)
+            inner = int(np.prod(sh[1:]))
+            lo.append(gpu_bits(fulls[p][0][first * inner:(first + count) * inner]))
+            ln.append(gpu_bits(fulls[p][1][first * inner:(first + count) * inner]))
+            offs.append(sbd.flat_offset(sh, first))
+        gi, gv, gn, go = sbd.diff_many(lo, ln, flat_offsets=offs)
+        o_h = go.cpu().numpy()
+        for p in range(len(shapes)):
+            got[p][0].append(gi[o_h[p]:o_h[p + 1]].cpu().numpy())
+            got[p][1].append(np_bits(gv[o_h[p]:o_h[p + 1]]))
+    for p, (o, x) in enumerate(fulls):
+        ri, rv = oracle_mod.diff(o, x)
+        assert np.array_equal(np.concatenate(got[p][0]), ri.astype(np.int64))
+        assert np.array_equal(np.concatenate(got[p][1]), rv)
+
+
+def test_diff_many_sharded_capacity(sbd, oracle_mod):
+    from sparse_bf16_delta_amd import _abi
+    from sparse_bf16_delta_amd.ops import _ptr, _stream
+    import ctypes
+
+    old, new = tile_kinds_case(41)
+    ri, rv, rn, ro = oracle_mod.shard_delta_many([old], [new], [1 << 35])
+    cut = 1024 + 1023 + 500
+    lib = _abi.load()
+    o, x = gpu_bits(old), gpu_bits(new)
+    guard = 2048
+    idx = torch.full((cut + guard,), -7, dtype=torch.int64, device="cuda")
+    val = torch.full((cut + guard,), -7, dtype=torch.int16, device="cuda")
+    nnz = torch.zeros(1, dtype=torch.int64, device="cuda")
+    offsets = torch.zeros(2, dtype=torch.int64, device="cuda")
+    ws = torch.empty(lib.delta_workspace_size(old.size, 1), dtype=torch.uint8, device="cuda")
+    ptrs_o = (ctypes.c_void_p * 1)(o.data_ptr())
+    ptrs_n = (ctypes.c_void_p * 1)(x.data_ptr())
+    nums = (ctypes.c_int64 * 1)(old.size)
+    fos = (ctypes.c_int64 * 1)(1 << 35)
+    _abi.check(lib.delta_diff_many_sharded(1, ptrs_o, ptrs_n, nums, fos, _ptr(idx), _ptr(val),
+                                           cut, _ptr(nnz), _ptr(offsets), _ptr(ws), ws.numel(),
+                                           _stream(o.device)))
+    assert int(offsets[1].item()) == ri.size
+    assert np.array_equal(idx[:cut].cpu().numpy(), ri[:cut])
+    assert np.array_equal(np_bits(val[:cut]), rv[:cut])
+    assert bool((idx[cut:] == -7).all()) and bool((val[cut:] == -7).all())
+
+
 def test_diff_capacity_protocol(sbd, oracle_mod):
     """Entries past `capacity` are never written; nnz still reports the truth."""
     from sparse_bf16_delta_amd import _abi

@@ -1,0 +1,67 @@
+"""Host side of the sharded diff: the Shard(0) placement helpers, checked
+against torch's own shard size/offset routine and numpy's row-major index,
+and the argument checks of delta_diff_many_sharded (no GPU needed: every
+rejected call returns before anything is enqueued)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from sparse_bf16_delta_amd import _abi
+from sparse_bf16_delta_amd.sharding import flat_offset, shard0_piece
+
+
+@pytest.mark.parametrize("rows", [0, 1, 7, 10, 64, 1003, 32000])
+@pytest.mark.parametrize("world", [1, 2, 3, 8, 16])
+def test_shard0_piece_is_torch_shard0(rows, world):
+    from torch.distributed.tensor.placement_types import Shard
+
+    covered = 0
+    for rank in range(world):
+        size, start = Shard.local_shard_size_and_offset(rows, world, rank)
+        assert shard0_piece(rows, world, rank) == (start, size)
+        covered += size
+    assert covered == rows
+
+
+def test_flat_offset_is_row_major_index():
+    for shape in [(10, 3), (7, 4, 5), (32000, 4096), (5,)]:
+        for row in range(0, shape[0], max(1, shape[0] // 7)):
+            want = int(np.ravel_multi_index((row,) + (0,) * (len(shape) - 1), shape))
+            assert flat_offset(shape, row) == want
+    assert flat_offset((128256, 16384), 128256 - 1) == (128256 - 1) * 16384  # past 2^31
+
+
+def test_bad_geometry_raises():
+    with pytest.raises(ValueError):
+        shard0_piece(10, 0, 0)
+    with pytest.raises(ValueError):
+        shard0_piece(10, 4, 4)
+    with pytest.raises(ValueError):
+        flat_offset((10, 3), 11)
+
+
+def test_sharded_abi_rejects_bad_offsets():
+    lib = _abi.load()
+    one = ctypes.c_void_p(16)
+    ptrs = (ctypes.c_void_p * 1)(16)
+    nums = (ctypes.c_int64 * 1)(100)
+    neg = (ctypes.c_int64 * 1)(-1)
+    big = (ctypes.c_int64 * 1)((1 << 63) - 50)
+    ok = (ctypes.c_int64 * 1)(5)
+    args = dict(idx=one, val=one, cap=10, nnz=one, off=one, ws=one, wsb=1 << 40)
+
+    def call(fos):
+        return lib.delta_diff_many_sharded(1, ptrs, ptrs, nums, fos, args["idx"], args["val"],
+                                           args["cap"], args["nnz"], args["off"], args["ws"],
+                                           args["wsb"], None)
+
+    assert call(None) == _abi.DELTA_E_INVALID
+    assert "flat_offsets is null" in lib.delta_last_error().decode()
+    assert call(neg) == _abi.DELTA_E_INVALID
+    assert "< 0" in lib.delta_last_error().decode()
+    assert call(big) == _abi.DELTA_E_RANGE
+    assert "overflows int64" in lib.delta_last_error().decode()
+    # a valid offset passes validation and then fails on the too-small workspace
+    args["wsb"] = 1
+    assert call(ok) == _abi.DELTA_E_WORKSPACE
