@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU-time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shards", type=int, default=0,
+                    help="W > 0: time delta_diff_many_sharded for each rank of a W-way Shard(0) "
+                         "split of the list, one rank after another (table on stderr)")
     return ap.parse_args()
 
 
@@ -120,6 +123,9 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     if args.config == "c4":
         density_sweep(args, props)
+        return
+    if args.shards > 0:
+        sharded_run(args, props)
         return
     cfg = workloads.CONFIGS[args.config]
     lr = args.lr if args.lr is not None else (1e-6 if cfg.key == "c3" else cfg.lrs[0])
@@ -293,6 +299,97 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, cfg, olds, news, dplan, nnz_total)
     print(json.dumps(result), flush=True)
+
+
+def sharded_run(args, props):
+    """Every rank of a W-way Shard(0) split of the list diffs its pieces with
+    delta_diff_many_sharded (int64 global positions), one rank after another
+    on this GPU; the ranks' deltas, concatenated per parameter in rank order,
+    must equal the unsharded delta."""
+    import torch
+
+    import sparse_bf16_delta_amd as sbd
+    from sparse_bf16_delta_amd.plan import DiffPlan
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    cfg = workloads.CONFIGS[args.config]
+    lr = args.lr if args.lr is not None else (1e-6 if cfg.key == "c3" else cfg.lrs[0])
+    mode = args.mode or cfg.mode
+    numels = cfg.numels
+    n_model = sum(numels)
+    offs, n_alloc = workloads.flat_layout(numels)
+    old = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
+    new = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
+    for t, (o, n) in enumerate(zip(offs, numels)):
+        workloads.fill_step_pair_(old[o:o + n], new[o:o + n], *workloads.seeds(cfg.number, t),
+                                  lr, mode)
+    shapes = [shape for _, shape in cfg.params]
+    world = args.shards
+    log(f"[bench] {cfg.key}: {len(shapes)} tensors, {n_model:,} elements, split over {world} "
+        f"ranks by rows")
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    full = DiffPlan([old[o:o + n] for o, n in zip(offs, numels)],
+                    [new[o:o + n] for o, n in zip(offs, numels)], n_model // 8 + 65536)
+    t_full = timed(full.run)
+    nnz_total = full.changed()
+    f_off = full.offsets.cpu().tolist()
+    rows, pieces = [], []
+    for rank in range(world):
+        lo, ln, fo, nel = [], [], [], []
+        for (o, n), shape in zip(zip(offs, numels), shapes):
+            first, count = sbd.shard0_piece(shape[0], world, rank)
+            inner = n // shape[0]
+            a, b = o + first * inner, o + (first + count) * inner
+            lo.append(old[a:b])
+            ln.append(new[a:b])
+            fo.append(sbd.flat_offset(shape, first))
+            nel.append(b - a)
+        plan = DiffPlan(lo, ln, sum(nel) // 8 + 65536, flat_offsets=fo)
+        t = timed(plan.run)
+        k = plan.changed()
+        rows.append({"rank": rank, "elements": sum(nel), "changed": k, "ms": round(t, 4),
+                     "frac": round((4 * sum(nel) + 10 * k) / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+        pieces.append((plan.idx[:k].clone(), plan.val[:k].clone(), plan.offsets.cpu().tolist()))
+        log(f"[bench] rank {rank}: {sum(nel):,} elements, {k:,} changed, {t:.3f} ms, "
+            f"{100 * rows[-1]['frac']:.1f} % of peak (4n + 10 nnz)")
+    # the ranks' deltas, in rank order per parameter, are the unsharded delta
+    same = True
+    for p in range(len(shapes)):
+        gi = torch.cat([pi[pi_off[p]:pi_off[p + 1]] for pi, _, pi_off in pieces])
+        gv = torch.cat([pv[pi_off[p]:pi_off[p + 1]] for _, pv, pi_off in pieces])
+        fi = full.idx[f_off[p]:f_off[p + 1]].long()
+        fv = full.val[f_off[p]:f_off[p + 1]]
+        same &= torch.equal(gi, fi) and torch.equal(gv.view(torch.int16), fv.view(torch.int16))
+    t_sum = sum(r["ms"] for r in rows)
+    log(f"[bench] unsharded diff_many {t_full:.3f} ms; all ranks' sharded diffs {t_sum:.3f} ms; "
+        f"concatenation identical: {same}")
+    if not same:
+        print("bench.py: sharded deltas do not concatenate to the unsharded delta", file=sys.stderr)
+        sys.exit(1)
+    print(json.dumps({
+        "metric": "sharded diff: per-rank delta_diff_many_sharded time for a Shard(0) split",
+        "value": None, "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": False, "dtype": "u16", "data": "synthetic",
+        "config": {"workload": f"{cfg.title}: {len(shapes)} tensors, {n_model} elements, "
+                               f"{mode} step lr {lr:g}, {world}-way Shard(0) split"},
+        "unsharded_ms": round(t_full, 4), "sharded_sum_ms": round(t_sum, 4), "changed": nnz_total,
+        "ranks": rows, "identical": same,
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None)},
+    }), flush=True)
 
 
 def density_sweep(args, props):
