@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU-time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--receiver", action="store_true",
+                    help="time the receiver with the delta and the XOR mask in pinned host "
+                         "memory: copy only, copy then apply, and the streamed pipeline")
     ap.add_argument("--shards", type=int, default=0,
                     help="W > 0: time delta_diff_many_sharded for each rank of a W-way Shard(0) "
                          "split of the list, one rank after another (table on stderr)")
@@ -126,6 +129,9 @@ def main():
         return
     if args.shards > 0:
         sharded_run(args, props)
+        return
+    if args.receiver:
+        receiver_run(args, props)
         return
     cfg = workloads.CONFIGS[args.config]
     lr = args.lr if args.lr is not None else (1e-6 if cfg.key == "c3" else cfg.lrs[0])
@@ -299,6 +305,135 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, cfg, olds, news, dplan, nnz_total)
     print(json.dumps(result), flush=True)
+
+
+def receiver_run(args, props):
+    """The receiver's side with its input in pinned host memory, as the
+    network leaves it: the sparse delta (idx, val, offsets) and the XOR mask.
+    Times, per mode: the host-to-device copy alone, copy then apply on one
+    stream, and the streamed pipeline (chunks of parameters or elements,
+    copies overlapping applies).  Every variant's result is checked."""
+    import torch
+
+    import sparse_bf16_delta_amd as sbd
+    from sparse_bf16_delta_amd.plan import ApplyPlan, DiffPlan, StreamedApplyPlan
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    cfg = workloads.CONFIGS[args.config]
+    lr = args.lr if args.lr is not None else (1e-6 if cfg.key == "c3" else cfg.lrs[0])
+    mode = args.mode or cfg.mode
+    numels = cfg.numels
+    n_model = sum(numels)
+    offs, n_alloc = workloads.flat_layout(numels)
+    old = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
+    new = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
+    for t, (o, n) in enumerate(zip(offs, numels)):
+        workloads.fill_step_pair_(old[o:o + n], new[o:o + n], *workloads.seeds(cfg.number, t),
+                                  lr, mode)
+    olds = [old[o:o + n] for o, n in zip(offs, numels)]
+    news = [new[o:o + n] for o, n in zip(offs, numels)]
+    snap = old.clone()
+    snaps = [snap[o:o + n] for o, n in zip(offs, numels)]
+    dplan = DiffPlan(olds, news, n_model // 8 + 65536)
+    dplan.run()
+    nnz = dplan.changed()
+    t0 = time.perf_counter()
+    h_idx = dplan.idx[:nnz].cpu().pin_memory()
+    h_val = dplan.val[:nnz].cpu().pin_memory()
+    h_off = dplan.offsets.cpu().pin_memory()
+    mask = sbd.xor_mask(old, new)
+    h_mask = mask.cpu().pin_memory()
+    del mask
+    log(f"[bench] receiver, {cfg.key}: {nnz:,} changed; delta {6 * nnz / 1e9:.3f} GB and mask "
+        f"{2 * n_alloc / 1e9:.2f} GB pinned on the host in {time.perf_counter() - t0:.1f} s")
+    k = len(numels)
+    nchunks = 8
+    bounds = sorted(set([round(i * k / nchunks) for i in range(nchunks + 1)]))
+    d_idx = torch.empty_like(dplan.idx[:nnz])
+    d_val = torch.empty_like(dplan.val[:nnz])
+    d_off = torch.empty_like(dplan.offsets)
+    d_mask = torch.empty(n_alloc, dtype=h_mask.dtype, device=dev)  # same dtype: a bit copy
+    aplan = ApplyPlan(snaps)
+    reps = max(args.steps, 5)
+
+    def timed(fn, reset):
+        """Median wall time of `reps` runs (each from the same start state):
+        host-side copies and stream hand-offs make single runs noisy."""
+        fn()
+        torch.cuda.synchronize()
+        samples = []
+        for _ in range(reps):
+            reset()
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            samples.append(time.perf_counter() - t)
+        return 1e3 * sorted(samples)[len(samples) // 2]
+
+    def reset():
+        snap.copy_(old)
+
+    def copy_delta():
+        d_idx.copy_(h_idx, non_blocking=True)
+        d_val.copy_(h_val, non_blocking=True)
+        d_off.copy_(h_off, non_blocking=True)
+
+    def serial_sparse():
+        copy_delta()
+        aplan.run(d_idx, d_val, d_off, nnz)
+
+    offs_h = h_off.tolist()
+    splan = StreamedApplyPlan(snaps, bounds,
+                              max(offs_h[hi] - offs_h[lo] for lo, hi in zip(bounds, bounds[1:])))
+
+    def streamed_sparse():
+        splan.run(h_idx, h_val, h_off)
+
+    def copy_mask():
+        d_mask.copy_(h_mask, non_blocking=True)
+
+    def serial_xor():
+        copy_mask()
+        sbd.xor_apply_(snap, d_mask)
+
+    chunk = 1 << 27
+
+    def streamed_xor():
+        sbd.xor_apply_streamed_(snap, h_mask, chunk_elems=chunk)
+
+    rows = {}
+    for name, fn, check in (("sparse copy", copy_delta, None),
+                            ("sparse copy+apply", serial_sparse, new),
+                            ("sparse streamed", streamed_sparse, new),
+                            ("xor copy", copy_mask, None),
+                            ("xor copy+apply", serial_xor, new),
+                            ("xor streamed", streamed_xor, new)):
+        ms = timed(fn, reset)
+        ok = True
+        if check is not None:
+            ok = torch.equal(snap.view(torch.int16), check.view(torch.int16))
+        b = 6 * nnz if name.startswith("sparse") else 2 * n_alloc
+        rows[name] = {"ms": round(ms, 3), "host_gbs": round(b / (ms * 1e-3) / 1e9, 2),
+                      "identical": ok}
+        log(f"[bench] {name:18s} {ms:9.3f} ms  {b / (ms * 1e-3) / 1e9:7.2f} GB/s from the host"
+            f"{'' if ok else '  MISMATCH'}")
+        if not ok:
+            print("bench.py: receiver result mismatch", file=sys.stderr)
+            sys.exit(1)
+    print(json.dumps({
+        "metric": "receiver with host-resident input: copy, copy+apply and streamed times "
+                  "(median of steps runs)",
+        "value": None, "unit": "ms", "n_gpus": 1, "steps": reps, "warmup": 1,
+        "higher_is_better": False, "dtype": "u16", "data": "synthetic",
+        "config": {"workload": f"{cfg.title}: {k} tensors, {n_model} elements, {mode} step lr "
+                               f"{lr:g}; {len(bounds) - 1} parameter chunks, XOR chunks of "
+                               f"{chunk} elements"},
+        "changed": nnz, "rows": rows,
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None)},
+    }), flush=True)
 
 
 def sharded_run(args, props):

@@ -222,6 +222,83 @@ delta_status xor_mask(const uint16_t *old_bits, const uint16_t *new_bits, uint16
 delta_status xor_apply(uint16_t *snapshot, const uint16_t *mask, int64_t n, void *stream);
 
 /*
+ * The streamed receiver.  [TRL] section 4.3 (vLLM side): the receiver applies
+ * each incoming delta into its resident bf16 snapshot; [XOR] third paragraph:
+ * the receiver overlaps getting the next mask with applying the current one.
+ * Here a delta or mask that already sits in host memory (where the network
+ * put it) is copied to the GPU chunk by chunk -- for example one layer at a
+ * time -- through two staging slots, and each chunk's apply overlaps the
+ * next chunk's copy.  The result is exactly that of delta_apply_many /
+ * xor_apply over the whole delta.  Host buffers should be pinned
+ * (hipHostMalloc); pageable ones work but their copies do not overlap.
+ * Each chunk costs two host-to-device copies (idx, val) plus a fixed
+ * overhead, so a few large chunks stream better than many small ones.
+ * `copy_stream` and `apply_stream` are hipStream_t as void*; they should be
+ * distinct, non-blocking streams for the copies to overlap.  Both calls
+ * return after the last apply has completed (the snapshots are updated and
+ * every host buffer may be reused); a copy or apply error is reported as
+ * DELTA_E_HIP.
+ */
+
+/* One chunk of a delta in host memory: parameters [first_param,
+ * first_param + nparams) of the receiver's list, with the concatenated
+ * parameter-local idx/val of those parameters and their running offsets
+ * (nparams + 1 entries, offsets[0] == 0, non-decreasing), all in host
+ * memory -- the layout delta_diff_many writes, cut at parameter bounds. */
+typedef struct {
+    int32_t first_param;
+    int32_t nparams;
+    const int32_t *idx;
+    const uint16_t *val;
+    const int64_t *offsets;
+} delta_host_chunk;
+
+/*
+ * delta_streamed_staging_size -- device bytes of the staging buffer for a
+ * receiver list of `nparams` snapshots and `nchunks` chunks of at most
+ * `max_chunk_params` parameters and `max_chunk_nnz` entries each: the
+ * snapshot table, every chunk's offsets, and two slots for idx/val.  0 for
+ * negative arguments.
+ */
+size_t delta_streamed_staging_size(int32_t nparams, int32_t nchunks, int32_t max_chunk_params,
+                                   int64_t max_chunk_nnz);
+
+/*
+ * delta_apply_streamed -- apply a chunked host delta to resident snapshots.
+ *  nparams, snap_ptrs, numels  the receiver's list, as delta_apply_many
+ *                      (host arrays of device pointers and sizes).
+ *  chunks              (host) nchunks chunk descriptors, applied in order.
+ *  staging             device buffer of at least delta_streamed_staging_size
+ *                      bytes for the largest chunk.
+ * Index contract per parameter as delta_apply.
+ * Errors: DELTA_E_INVALID (chunk outside the list, offsets not starting at 0
+ * or decreasing, null pointers), DELTA_E_RANGE (numel > 2^31-1),
+ * DELTA_E_WORKSPACE (staging too small), DELTA_E_HIP.
+ */
+delta_status delta_apply_streamed(int32_t nparams, uint16_t *const *snap_ptrs,
+                                  const int64_t *numels, int32_t nchunks,
+                                  const delta_host_chunk *chunks, void *staging,
+                                  size_t staging_bytes, void *copy_stream, void *apply_stream);
+
+/*
+ * xor_streamed_staging_size -- device bytes of the staging buffer of
+ * xor_apply_streamed for chunks of `chunk_elems` elements (0 if <= 0).
+ */
+size_t xor_streamed_staging_size(int64_t chunk_elems);
+
+/*
+ * xor_apply_streamed -- snapshot ^= mask with the n-element mask in host
+ * memory, copied and applied `chunk_elems` elements at a time.
+ *  snapshot            n uint16 on the device, updated in place.
+ *  mask_host           (host) n uint16.
+ * Errors: DELTA_E_INVALID (n < 0, chunk_elems <= 0, null pointers),
+ * DELTA_E_WORKSPACE, DELTA_E_HIP.
+ */
+delta_status xor_apply_streamed(uint16_t *snapshot, const uint16_t *mask_host, int64_t n,
+                                int64_t chunk_elems, void *staging, size_t staging_bytes,
+                                void *copy_stream, void *apply_stream);
+
+/*
  * delta_last_error -- message for the calling thread's last non-OK status
  * (empty string if none).  The pointer stays valid until the next call on
  * the same thread.

@@ -12,12 +12,14 @@ from ._abi import DeltaError, DeltaRangeError, load  # noqa: F401
 from .ops import (  # noqa: F401
     apply_,
     apply_many_,
+    apply_streamed_,
     default_capacity,
     diff,
     diff_many,
     workspace,
     workspace_size,
     xor_apply_,
+    xor_apply_streamed_,
     xor_mask,
 )
 from .sharding import flat_offset, shard0_piece  # noqa: F401
@@ -25,5 +27,5 @@ from .sharding import flat_offset, shard0_piece  # noqa: F401
 __all__ = [
     "DeltaError", "DeltaRangeError", "load", "diff", "diff_many", "apply_", "apply_many_",
     "xor_mask", "xor_apply_", "workspace", "workspace_size", "default_capacity",
-    "shard0_piece", "flat_offset",
+    "shard0_piece", "flat_offset", "apply_streamed_", "xor_apply_streamed_",
 ]

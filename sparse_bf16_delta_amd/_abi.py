@@ -32,6 +32,13 @@ STATUS_NAMES = {
     DELTA_E_HIP: "DELTA_E_HIP",
 }
 
+class HostChunk(ctypes.Structure):
+    """delta_host_chunk of include/sbd.h."""
+    _fields_ = [("first_param", ctypes.c_int32), ("nparams", ctypes.c_int32),
+                ("idx", ctypes.c_void_p), ("val", ctypes.c_void_p),
+                ("offsets", ctypes.c_void_p)]
+
+
 # name -> (restype, argtypes); mirrors include/sbd.h
 _i64, _i32, _sz, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
 _st = ctypes.c_int
@@ -43,6 +50,10 @@ SIGNATURES = {
                                       _sz, _vp]),
     "delta_apply": (_st, [_vp, _i64, _vp, _vp, _i64, _vp, _vp]),
     "delta_apply_many": (_st, [_i32, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "delta_streamed_staging_size": (_sz, [_i32, _i32, _i32, _i64]),
+    "delta_apply_streamed": (_st, [_i32, _vp, _vp, _i32, _vp, _vp, _sz, _vp, _vp]),
+    "xor_streamed_staging_size": (_sz, [_i64]),
+    "xor_apply_streamed": (_st, [_vp, _vp, _i64, _i64, _vp, _sz, _vp, _vp]),
     "xor_mask": (_st, [_vp, _vp, _vp, _i64, _vp]),
     "xor_apply": (_st, [_vp, _vp, _i64, _vp]),
     "delta_last_error": (ctypes.c_char_p, []),

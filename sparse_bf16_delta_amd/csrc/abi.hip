@@ -255,6 +255,41 @@ delta_status delta_apply_many(int32_t nparams, uint16_t* const* snap_ptrs, const
                     "delta_apply_many launch");
 }
 
+size_t delta_streamed_staging_size(int32_t nparams, int32_t nchunks, int32_t max_chunk_params,
+                                   int64_t max_chunk_nnz) {
+  if (nparams < 0 || nchunks < 0 || max_chunk_params < 0 || max_chunk_nnz < 0) return 0;
+  return sbd::streamed_staging_size(nparams, nchunks, max_chunk_params, max_chunk_nnz);
+}
+
+delta_status delta_apply_streamed(int32_t nparams, uint16_t* const* snap_ptrs,
+                                  const int64_t* numels, int32_t nchunks,
+                                  const delta_host_chunk* chunks, void* staging,
+                                  size_t staging_bytes, void* copy_stream, void* apply_stream) {
+  std::string err;
+  const delta_status st = sbd::apply_streamed_impl(nparams, snap_ptrs, numels, nchunks, chunks,
+                                                   staging, staging_bytes, copy_stream,
+                                                   apply_stream, err);
+  if (st != DELTA_OK) return fail(st, "%s", err.c_str());
+  g_error.clear();
+  return DELTA_OK;
+}
+
+size_t xor_streamed_staging_size(int64_t chunk_elems) {
+  return chunk_elems <= 0 ? 0 : sbd::xor_streamed_staging_size(chunk_elems);
+}
+
+delta_status xor_apply_streamed(uint16_t* snapshot, const uint16_t* mask_host, int64_t n,
+                                int64_t chunk_elems, void* staging, size_t staging_bytes,
+                                void* copy_stream, void* apply_stream) {
+  std::string err;
+  const delta_status st = sbd::xor_apply_streamed_impl(snapshot, mask_host, n, chunk_elems,
+                                                       staging, staging_bytes, copy_stream,
+                                                       apply_stream, err);
+  if (st != DELTA_OK) return fail(st, "%s", err.c_str());
+  g_error.clear();
+  return DELTA_OK;
+}
+
 delta_status xor_mask(const uint16_t* old_bits, const uint16_t* new_bits, uint16_t* mask,
                       int64_t n, void* stream) {
   if (n < 0) return fail(DELTA_E_INVALID, "xor_mask: n=%lld < 0", (long long)n);

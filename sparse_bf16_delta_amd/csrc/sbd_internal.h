@@ -6,6 +6,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
+#include "sbd.h"
+
 namespace sbd {
 
 // A pointer loaded from memory (or built from an integer) is generic to the
@@ -124,6 +128,19 @@ hipError_t launch_diff(const DiffParam* d_table, const DiffParam& single, int32_
 hipError_t launch_apply(const SnapParam* d_table, const SnapParam& single, int32_t nparams,
                         const int64_t* offsets, const int32_t* idx, const uint16_t* val,
                         int64_t max_nnz, int64_t* violations, hipStream_t stream);
+
+// The streamed receiver (stream.hip); on failure `err` receives the message.
+size_t streamed_staging_size(int32_t nparams, int32_t nchunks, int32_t max_chunk_params,
+                             int64_t max_chunk_nnz);
+size_t xor_streamed_staging_size(int64_t chunk_elems);
+delta_status apply_streamed_impl(int32_t nparams, uint16_t* const* snap_ptrs,
+                                 const int64_t* numels, int32_t nchunks,
+                                 const delta_host_chunk* chunks, void* staging,
+                                 size_t staging_bytes, void* copy_stream, void* apply_stream,
+                                 std::string& err);
+delta_status xor_apply_streamed_impl(uint16_t* snapshot, const uint16_t* mask_host, int64_t n,
+                                     int64_t chunk_elems, void* staging, size_t staging_bytes,
+                                     void* copy_stream, void* apply_stream, std::string& err);
 
 hipError_t launch_xor_mask(const uint16_t* a, const uint16_t* b, uint16_t* out, int64_t n,
                            hipStream_t stream);

@@ -11,6 +11,8 @@ memory and the current stream only.  Names mirror the sources' callables:
   apply_many_(snaps, idx, val, offsets)
   xor_mask(old, new)              -- XOR-mask mode (humans& summary)
   xor_apply_(snap, mask)
+  apply_streamed_(snaps, ...)     -- receiver: apply a host-resident delta
+  xor_apply_streamed_(snap, mask) -- chunk by chunk, copies overlapping applies
 
 Bit patterns travel as bfloat16 tensors (int16/uint16 views are accepted too);
 indices are int32, counts and offsets int64, all on the same device.
@@ -22,7 +24,7 @@ from typing import Sequence
 
 import torch
 
-from ._abi import DeltaError, DeltaRangeError, check, load
+from ._abi import DeltaError, DeltaRangeError, HostChunk, check, load
 
 INT32_MAX = (1 << 31) - 1
 _BIT_DTYPES = (torch.bfloat16, torch.int16, torch.uint16)
@@ -215,6 +217,106 @@ def apply_many_(snaps: Sequence[torch.Tensor], idx: torch.Tensor, val: torch.Ten
                                _stream(dev)))
     _raise_on_violations(v)
     return snaps
+
+
+_stream_pairs: dict = {}
+
+
+def _receiver_streams(dev: torch.device):
+    """Two streams of the default priority for the streamed receiver (one for
+    copies, one for applies), made once per device."""
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    if key not in _stream_pairs:
+        _stream_pairs[key] = (torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev))
+    return _stream_pairs[key]
+
+
+def _host_bits(t, what: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cpu" or not t.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous host tensor")
+    if t.dtype not in _BIT_DTYPES:
+        raise ValueError(f"{what}: unsupported dtype {t.dtype}; expected bfloat16 bits")
+    return t
+
+
+def apply_streamed_(snaps: Sequence[torch.Tensor], idx: torch.Tensor, val: torch.Tensor,
+                    offsets: torch.Tensor, bounds: Sequence[int]):
+    """Apply a delta held in host memory -- idx int32, val bf16 bits, offsets
+    int64[P+1], as diff_many writes them -- to the device snapshots `snaps`,
+    in chunks of parameters bounds[c] .. bounds[c+1] (e.g. one layer each):
+    each chunk's host-to-device copy overlaps the previous chunk's apply.
+    Host tensors should be pinned.  Returns after the snapshots are updated."""
+    if not snaps:
+        raise ValueError("empty parameter list")
+    dev = snaps[0].device
+    for p, s in enumerate(snaps):
+        _bits(s, f"snaps[{p}]")
+        if s.device != dev:
+            raise ValueError(f"snaps[{p}] on another device")
+        _range(s.numel(), f"parameter {p}")
+    k = len(snaps)
+    if (not isinstance(idx, torch.Tensor) or idx.device.type != "cpu" or idx.dtype != torch.int32
+            or not idx.is_contiguous()):
+        raise ValueError("idx must be a contiguous host int32 tensor")
+    _host_bits(val, "val")
+    if (not isinstance(offsets, torch.Tensor) or offsets.device.type != "cpu" or
+            offsets.dtype != torch.int64 or offsets.numel() != k + 1):
+        raise ValueError("offsets must be a host int64 tensor of nparams + 1 entries")
+    b = [int(x) for x in bounds]
+    if not b or b[0] != 0 or b[-1] != k or any(x > y for x, y in zip(b, b[1:])):
+        raise ValueError("bounds must run from 0 to nparams without decreasing")
+    off = offsets.tolist()
+    if off[0] != 0 or any(x > y for x, y in zip(off, off[1:])) or off[-1] > idx.numel():
+        raise ValueError("offsets must start at 0, not decrease and stay within idx")
+    # every chunk's offsets relative to its first entry, in one host buffer
+    starts, flat = [], []
+    for lo, hi in zip(b, b[1:]):
+        starts.append(len(flat))
+        flat.extend(x - off[lo] for x in off[lo:hi + 1])
+    rel = torch.tensor(flat, dtype=torch.int64)
+    chunks = (HostChunk * max(len(b) - 1, 1))()
+    for c, (lo, hi) in enumerate(zip(b, b[1:])):
+        chunks[c] = HostChunk(lo, hi - lo, idx.data_ptr() + 4 * off[lo],
+                              val.data_ptr() + 2 * off[lo], rel.data_ptr() + 8 * starts[c])
+    lib = load()
+    max_p = max(hi - lo for lo, hi in zip(b, b[1:]))
+    max_n = max(off[hi] - off[lo] for lo, hi in zip(b, b[1:]))
+    staging = workspace(lib.delta_streamed_staging_size(k, len(b) - 1, max_p, max_n), dev)
+    sptrs = (ctypes.c_void_p * k)(*[s.data_ptr() for s in snaps])
+    nums = (ctypes.c_int64 * k)(*[s.numel() for s in snaps])
+    cs, as_ = _receiver_streams(dev)
+    # the streams start after everything already queued on the current stream
+    cur = torch.cuda.current_stream(dev)
+    cs.wait_stream(cur)
+    as_.wait_stream(cur)
+    check(lib.delta_apply_streamed(k, sptrs, nums, len(b) - 1, chunks, _ptr(staging),
+                                   staging.numel(), ctypes.c_void_p(cs.cuda_stream),
+                                   ctypes.c_void_p(as_.cuda_stream)))
+    del rel
+    return snaps
+
+
+def xor_apply_streamed_(snap: torch.Tensor, mask: torch.Tensor, chunk_elems: int = 1 << 27):
+    """snap ^= mask with `mask` in host memory (should be pinned), copied and
+    applied chunk_elems elements at a time.  Returns after snap is updated."""
+    _bits(snap, "snapshot")
+    _host_bits(mask, "mask")
+    if mask.numel() != snap.numel():
+        raise ValueError("snapshot and mask must have the same numel")
+    if chunk_elems <= 0:
+        raise ValueError("chunk_elems must be positive")
+    dev = snap.device
+    lib = load()
+    staging = workspace(lib.xor_streamed_staging_size(int(chunk_elems)), dev)
+    cs, as_ = _receiver_streams(dev)
+    cur = torch.cuda.current_stream(dev)
+    cs.wait_stream(cur)
+    as_.wait_stream(cur)
+    check(lib.xor_apply_streamed(_ptr(snap), ctypes.c_void_p(mask.data_ptr()), snap.numel(),
+                                 int(chunk_elems), _ptr(staging), staging.numel(),
+                                 ctypes.c_void_p(cs.cuda_stream),
+                                 ctypes.c_void_p(as_.cuda_stream)))
+    return snap
 
 
 def xor_mask(old: torch.Tensor, new: torch.Tensor, out: torch.Tensor | None = None):

@@ -15,7 +15,7 @@ from typing import Sequence
 
 import torch
 
-from ._abi import DeltaError, check, load
+from ._abi import DeltaError, HostChunk, check, load
 from .ops import _bits, _ptr, _range, _stream
 
 
@@ -115,3 +115,72 @@ class ApplyPlan:
                                       _ptr(offsets), m,
                                       _ptr(violations) if violations is not None else None,
                                       _ptr(self.ws), self.ws.numel(), _stream(self.device)))
+
+
+class StreamedApplyPlan:
+    """Receiver side with the delta in host memory: delta_apply_streamed over
+    fixed resident snapshots and fixed chunk bounds (parameters
+    bounds[c] .. bounds[c+1], e.g. groups of layers).  The snapshot table,
+    staging buffer and the two streams are made once; a step builds only the
+    chunk table.  A few large chunks stream best: every chunk costs two
+    host-to-device copies plus a fixed overhead."""
+
+    def __init__(self, snaps: Sequence[torch.Tensor], bounds: Sequence[int],
+                 max_chunk_nnz: int):
+        from .ops import _receiver_streams
+
+        if not snaps:
+            raise ValueError("empty parameter list")
+        self.device = snaps[0].device
+        for p, s in enumerate(snaps):
+            _bits(s, f"snaps[{p}]")
+            if s.device != self.device:
+                raise ValueError(f"snaps[{p}] on another device")
+            _range(s.numel(), f"parameter {p}")
+        self.nparams = k = len(snaps)
+        b = [int(x) for x in bounds]
+        if not b or b[0] != 0 or b[-1] != k or any(x > y for x, y in zip(b, b[1:])):
+            raise ValueError("bounds must run from 0 to nparams without decreasing")
+        self.bounds = b
+        self.nchunks = len(b) - 1
+        self.max_chunk_nnz = int(max_chunk_nnz)
+        self._keep = list(snaps)
+        self._sptrs = (ctypes.c_void_p * k)(*[s.data_ptr() for s in snaps])
+        self._nums = (ctypes.c_int64 * k)(*[s.numel() for s in snaps])
+        max_p = max(hi - lo for lo, hi in zip(b, b[1:]))
+        self.staging = torch.empty(
+            load().delta_streamed_staging_size(k, self.nchunks, max_p, self.max_chunk_nnz),
+            dtype=torch.uint8, device=self.device)
+        self._chunks = (HostChunk * max(self.nchunks, 1))()
+        self._streams = _receiver_streams(self.device)
+
+    def run(self, idx: torch.Tensor, val: torch.Tensor, offsets: torch.Tensor):
+        """Apply a host delta (int32 idx, bf16-bit val, int64 offsets[nparams+1]
+        as diff_many writes them; pinned for the copies to overlap).  Returns
+        after the snapshots are updated."""
+        if (idx.device.type != "cpu" or val.device.type != "cpu" or offsets.device.type != "cpu"
+                or idx.dtype != torch.int32 or offsets.dtype != torch.int64
+                or offsets.numel() != self.nparams + 1):
+            raise ValueError("idx int32, val and offsets int64[nparams+1] must be host tensors")
+        off = offsets.tolist()
+        b = self.bounds
+        rel = torch.empty(self.nparams + self.nchunks, dtype=torch.int64)
+        r = rel.numpy()
+        pos = 0
+        for c, (lo, hi) in enumerate(zip(b, b[1:])):
+            if off[hi] - off[lo] > self.max_chunk_nnz:
+                raise DeltaError(3, f"chunk {c} holds {off[hi] - off[lo]} entries, more than "
+                                    f"the plan's {self.max_chunk_nnz}")
+            r[pos:pos + hi - lo + 1] = [x - off[lo] for x in off[lo:hi + 1]]
+            self._chunks[c] = HostChunk(lo, hi - lo, idx.data_ptr() + 4 * off[lo],
+                                        val.data_ptr() + 2 * off[lo],
+                                        rel.data_ptr() + 8 * pos)
+            pos += hi - lo + 1
+        cs, as_ = self._streams
+        cur = torch.cuda.current_stream(self.device)
+        cs.wait_stream(cur)
+        as_.wait_stream(cur)
+        check(load().delta_apply_streamed(self.nparams, self._sptrs, self._nums, self.nchunks,
+                                          self._chunks, _ptr(self.staging), self.staging.numel(),
+                                          ctypes.c_void_p(cs.cuda_stream),
+                                          ctypes.c_void_p(as_.cuda_stream)))

@@ -65,3 +65,37 @@ def test_sharded_abi_rejects_bad_offsets():
     # a valid offset passes validation and then fails on the too-small workspace
     args["wsb"] = 1
     assert call(ok) == _abi.DELTA_E_WORKSPACE
+
+
+def test_streamed_abi_rejects_bad_chunks():
+    """Every check of delta_apply_streamed fires before any GPU call."""
+    lib = _abi.load()
+    snaps = (ctypes.c_void_p * 3)(16, 32, 48)
+    nums = (ctypes.c_int64 * 3)(10, 20, 30)
+    idx = (ctypes.c_int32 * 4)(1, 2, 3, 4)
+    val = (ctypes.c_uint16 * 4)(1, 2, 3, 4)
+    good = (ctypes.c_int64 * 3)(0, 2, 4)
+    not0 = (ctypes.c_int64 * 3)(1, 2, 4)
+    dec = (ctypes.c_int64 * 3)(0, 3, 2)
+
+    def chunk(first, count, offs):
+        return _abi.HostChunk(first, count, ctypes.addressof(idx), ctypes.addressof(val),
+                              ctypes.addressof(offs))
+
+    def call(chs, staging_bytes=1 << 40):
+        arr = (_abi.HostChunk * len(chs))(*chs)
+        return lib.delta_apply_streamed(3, snaps, nums, len(chs), arr, ctypes.c_void_p(256),
+                                        staging_bytes, None, None)
+
+    assert call([chunk(2, 2, good)]) == _abi.DELTA_E_INVALID  # beyond the list
+    assert "outside the list" in lib.delta_last_error().decode()
+    assert call([chunk(0, 2, not0)]) == _abi.DELTA_E_INVALID
+    assert "not from 0" in lib.delta_last_error().decode()
+    assert call([chunk(0, 2, dec)]) == _abi.DELTA_E_INVALID
+    assert "decrease" in lib.delta_last_error().decode()
+    assert call([chunk(0, 2, good)], staging_bytes=16) == _abi.DELTA_E_WORKSPACE
+    assert lib.xor_apply_streamed(None, None, 10, 0, None, 0, None, None) == _abi.DELTA_E_INVALID
+    assert lib.xor_apply_streamed(ctypes.c_void_p(16), ctypes.c_void_p(16), 100, 64,
+                                  ctypes.c_void_p(256), 8, None, None) == _abi.DELTA_E_WORKSPACE
+    assert lib.delta_streamed_staging_size(-1, 1, 0, 0) == 0
+    assert lib.xor_streamed_staging_size(0) == 0
