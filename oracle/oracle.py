@@ -38,6 +38,16 @@ def _load():
     lib.oracle_diff_many.restype = ctypes.c_int
     lib.oracle_shard_delta_many.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, vp, vp]
     lib.oracle_shard_delta_many.restype = ctypes.c_int
+    lib.oracle_wire_width.argtypes = [i64]
+    lib.oracle_wire_width.restype = ctypes.c_int
+    lib.oracle_wire_encode.argtypes = [i32, vp, vp, vp, vp, vp]
+    lib.oracle_wire_encode.restype = i64
+    lib.oracle_wire_decode.argtypes = [i32, vp, vp, vp, vp, vp]
+    lib.oracle_wire_decode.restype = ctypes.c_int
+    lib.oracle_hash_bytes.argtypes = [vp, i64]
+    lib.oracle_hash_bytes.restype = ctypes.c_uint64
+    lib.oracle_hash_bf16.argtypes = [vp, i64]
+    lib.oracle_hash_bf16.restype = ctypes.c_uint64
     lib.oracle_apply.argtypes = [vp, i64, vp, vp, i64]
     lib.oracle_apply.restype = ctypes.c_int
     lib.oracle_xor_mask.argtypes = [vp, vp, vp, i64]
@@ -216,3 +226,50 @@ def touched_lines(idx, line_bytes=128, base_byte_offset=0) -> int:
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     return int(_load().oracle_touched_lines(_ptr(idx), idx.size, int(line_bytes),
                                             int(base_byte_offset)))
+
+
+def wire_width(numel: int) -> int:
+    return int(_load().oracle_wire_width(int(numel)))
+
+
+def wire_encode(idx, offsets, numels):
+    """Positions byte block of a batched delta: (positions uint8, pos_offsets int64[P+1])."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+    numels = np.ascontiguousarray(numels, dtype=np.int64)
+    k = numels.size
+    if offsets.size != k + 1:
+        raise ValueError("offsets must have nparams + 1 entries")
+    positions = np.empty(max(4 * idx.size, 1), dtype=np.uint8)
+    pos_offsets = np.zeros(k + 1, dtype=np.int64)
+    m = _load().oracle_wire_encode(k, _ptr(numels), _ptr(idx), _ptr(offsets), _ptr(positions),
+                                   _ptr(pos_offsets))
+    if m < 0:
+        raise ValueError("oracle_wire_encode rejected its arguments")
+    return positions[:m].copy(), pos_offsets
+
+
+def wire_decode(positions, pos_offsets, offsets, numels):
+    positions = np.ascontiguousarray(positions, dtype=np.uint8)
+    pos_offsets = np.ascontiguousarray(pos_offsets, dtype=np.int64)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+    numels = np.ascontiguousarray(numels, dtype=np.int64)
+    idx = np.empty(max(int(offsets[-1]), 1), dtype=np.int32)
+    _load().oracle_wire_decode(numels.size, _ptr(numels), _ptr(positions), _ptr(pos_offsets),
+                               _ptr(offsets), _ptr(idx))
+    return idx[:int(offsets[-1])].copy()
+
+
+def hash_bytes(b) -> int:
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    return int(_load().oracle_hash_bytes(_ptr(b), b.size))
+
+
+def hash_bf16(bits) -> int:
+    bits = _u16(bits)
+    return int(_load().oracle_hash_bf16(_ptr(bits), bits.size))
+
+
+def wire_checksum(positions, values_bits) -> int:
+    """The flush checksum as the pages define it, on unbounded integers."""
+    return hash_bytes(positions) ^ (hash_bf16(values_bits) << 1)

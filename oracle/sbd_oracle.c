@@ -21,6 +21,7 @@
  */
 #include <stdint.h>
 #include <stddef.h>
+#include <string.h>
 #include <math.h>
 
 #define ORACLE_INT32_MAX 2147483647LL
@@ -321,4 +322,110 @@ int64_t oracle_touched_lines(const int32_t *idx, int64_t nnz, int64_t line_bytes
         }
     }
     return g;
+}
+
+/*
+ * Wire encoding of a batched delta ([VERL] encode.py: `DeltaParam`,
+ * `DeltaFlush`, `checksum`).
+ *
+ * oracle_wire_width -- bytes per position of a parameter: the pages give a
+ * width of 2 or 4 bytes per parameter; the reading taken is the narrowest
+ * that holds every parameter-local index, i.e. 2 when numel <= 65536.
+ */
+int oracle_wire_width(int64_t numel)
+{
+    return numel <= 65536 ? 2 : 4;
+}
+
+/*
+ * oracle_wire_encode -- the positions byte block: parameter by parameter in
+ * list order, each parameter-local index of the delta written little-endian
+ * with that parameter's width.  pos_offsets (nparams+1 entries) receives
+ * each parameter's start in the block (`pos_start`; the next entry is its
+ * `pos_end`).  Returns the block's size in bytes, or -1 on bad arguments.
+ *
+ * Pins: the bytes equal numpy's per-segment astype('<u2' / '<u4') bytes;
+ * oracle_wire_decode inverts it exactly.
+ */
+int64_t oracle_wire_encode(int32_t nparams, const int64_t *numels, const int32_t *idx,
+                           const int64_t *offsets, uint8_t *positions, int64_t *pos_offsets)
+{
+    int32_t p;
+    int64_t j, at = 0;
+    if (nparams < 0)
+        return -1;
+    for (p = 0; p < nparams; ++p) {
+        int w = oracle_wire_width(numels[p]);
+        pos_offsets[p] = at;
+        for (j = offsets[p]; j < offsets[p + 1]; ++j) {
+            uint32_t v = (uint32_t)idx[j];
+            int b;
+            for (b = 0; b < w; ++b)
+                positions[at + b] = (uint8_t)(v >> (8 * b));
+            at += w;
+        }
+    }
+    pos_offsets[nparams] = at;
+    return at;
+}
+
+/*
+ * oracle_wire_decode -- back from the byte block to int32 parameter-local
+ * indices (the layout oracle_diff_many writes).  Returns 0.
+ */
+int oracle_wire_decode(int32_t nparams, const int64_t *numels, const uint8_t *positions,
+                       const int64_t *pos_offsets, const int64_t *offsets, int32_t *idx)
+{
+    int32_t p;
+    int64_t j;
+    for (p = 0; p < nparams; ++p) {
+        int w = oracle_wire_width(numels[p]);
+        int64_t at = pos_offsets[p];
+        for (j = offsets[p]; j < offsets[p + 1]; ++j) {
+            uint32_t v = 0;
+            int b;
+            for (b = 0; b < w; ++b)
+                v |= (uint32_t)positions[at + b] << (8 * b);
+            idx[j] = (int32_t)v;
+            at += w;
+        }
+    }
+    return 0;
+}
+
+/*
+ * oracle_hash_bytes / oracle_hash_bf16 -- the two halves of the flush
+ * checksum ([VERL] encode.py `checksum`): torch.hash_tensor's XOR reduction
+ * of the elements widened to 64 bits -- bytes zero-extended; bf16 values
+ * widened to IEEE double (through float, as C converts) and taken as their
+ * bit patterns.  The checksum itself is hash_bytes ^ (hash_bf16 << 1) as an
+ * unbounded integer (the pages compute it on Python ints).
+ *
+ * Pins: equal to torch.hash_tensor on the same tensors, for every one of the
+ * 65536 bf16 patterns and for random arrays.
+ */
+uint64_t oracle_hash_bytes(const uint8_t *bytes, int64_t n)
+{
+    int64_t i;
+    uint64_t h = 0;
+    for (i = 0; i < n; ++i)
+        h ^= (uint64_t)bytes[i];
+    return h;
+}
+
+uint64_t oracle_hash_bf16(const uint16_t *bits, int64_t n)
+{
+    int64_t i;
+    uint64_t h = 0;
+    for (i = 0; i < n; ++i) {
+        uint32_t u = (uint32_t)bits[i] << 16;
+        float f;
+        double d;
+        uint64_t b;
+        memcpy(&f, &u, sizeof f);
+        d = (double)f;
+        memcpy(&b, &d, sizeof b);
+        h ^= b;
+    }
+    return h;
 }

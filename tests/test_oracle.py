@@ -444,3 +444,75 @@ def test_shard_delta_rejects_negative_offset(oracle_mod):
     a = np.zeros(4, dtype=np.uint16)
     with pytest.raises(ValueError):
         oracle_mod.shard_delta_many([a], [a], [-1])
+
+
+# ----------------------------------------------------------------------------
+# wire encoding (VERL encode.py: DeltaParam pos_width, DeltaFlush, checksum)
+# ----------------------------------------------------------------------------
+
+
+def _wire_case(seed):
+    rng = np.random.default_rng(seed)
+    numels = [5, 65536, 65537, 100_000, 1, 0, 3000, 65535]
+    olds, news = zip(*[rand_bits(rng, n, 0.3) for n in numels])
+    ri, rv, rn, ro = oracle_diff_many_np(olds, news)
+    return numels, ri, rv, ro
+
+
+def oracle_diff_many_np(olds, news):
+    """The batched delta written with numpy alone (no oracle)."""
+    idx, val, nnz = [], [], []
+    for o, x in zip(olds, news):
+        d = np.flatnonzero(o != x)
+        idx.append(d.astype(np.int32))
+        val.append(x[d])
+        nnz.append(d.size)
+    offsets = np.concatenate([[0], np.cumsum(nnz)]).astype(np.int64)
+    return np.concatenate(idx), np.concatenate(val), np.array(nnz), offsets
+
+
+def test_wire_width_reading(oracle_mod):
+    assert [oracle_mod.wire_width(n) for n in (0, 1, 65535, 65536, 65537, 1 << 31)] == \
+        [2, 2, 2, 2, 4, 4]
+
+
+def test_wire_encode_matches_numpy_bytes(oracle_mod):
+    numels, ri, rv, ro = _wire_case(1)
+    pos, po = oracle_mod.wire_encode(ri, ro, numels)
+    want, starts = [], [0]
+    for p, n in enumerate(numels):
+        seg = ri[ro[p]:ro[p + 1]]
+        b = seg.astype("<u2" if n <= 65536 else "<u4").tobytes()
+        assert seg.size == 0 or int(seg.max()) < n
+        want.append(np.frombuffer(b, dtype=np.uint8))
+        starts.append(starts[-1] + len(b))
+    assert np.array_equal(pos, np.concatenate(want))
+    assert po.tolist() == starts
+    assert np.array_equal(oracle_mod.wire_decode(pos, po, ro, numels), ri)
+
+
+def test_hash_bf16_matches_torch_all_patterns(oracle_mod):
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    t = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
+    for lo in range(0, 1 << 16, 4096):  # blocks, so one wrong pattern shows
+        want = int(torch.hash_tensor(t[lo:lo + 4096]).item())
+        assert oracle_mod.hash_bf16(bits[lo:lo + 4096]) == want, hex(lo)
+    for b in (0x7F81, 0xFFC1, 0x0001, 0x8000, 0x7F80):  # single patterns: sNaN, qNaN, sub, -0, inf
+        one = torch.tensor([b], dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+        assert oracle_mod.hash_bf16(np.array([b], dtype=np.uint16)) == int(torch.hash_tensor(one).item())
+
+
+def test_hash_bytes_and_checksum_match_torch(oracle_mod):
+    numels, ri, rv, ro = _wire_case(2)
+    pos, po = oracle_mod.wire_encode(ri, ro, numels)
+    tp = torch.from_numpy(pos.copy())
+    tv = torch.from_numpy(rv.view(np.int16).copy()).view(torch.bfloat16)
+    p = int(torch.hash_tensor(tp).item()) if tp.numel() else 0
+    v = int(torch.hash_tensor(tv).item()) if tv.numel() else 0
+    assert oracle_mod.hash_bytes(pos) == p
+    assert oracle_mod.hash_bf16(rv) == v
+    assert oracle_mod.wire_checksum(pos, rv) == p ^ (v << 1)
+    # a flipped bit anywhere changes it
+    pos2 = pos.copy()
+    pos2[len(pos2) // 2] ^= 4
+    assert oracle_mod.wire_checksum(pos2, rv) != oracle_mod.wire_checksum(pos, rv)
