@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU-time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--wire", action="store_true",
+                    help="time the wire encoding of the list's delta: positions block encode, "
+                         "decode and the flush hashes")
     ap.add_argument("--receiver", action="store_true",
                     help="time the receiver with the delta and the XOR mask in pinned host "
                          "memory: copy only, copy then apply, and the streamed pipeline")
@@ -132,6 +135,9 @@ def main():
         return
     if args.receiver:
         receiver_run(args, props)
+        return
+    if args.wire:
+        wire_run(args, props)
         return
     cfg = workloads.CONFIGS[args.config]
     lr = args.lr if args.lr is not None else (1e-6 if cfg.key == "c3" else cfg.lrs[0])
@@ -305,6 +311,101 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, cfg, olds, news, dplan, nnz_total)
     print(json.dumps(result), flush=True)
+
+
+def wire_run(args, props):
+    """Encode the list's delta into the flush's positions block, decode it
+    back, and hash positions and values; checked, then timed with HIP events."""
+    import torch
+
+    import sparse_bf16_delta_amd as sbd
+    from sparse_bf16_delta_amd.plan import DiffPlan
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    cfg = workloads.CONFIGS[args.config]
+    lr = args.lr if args.lr is not None else (1e-6 if cfg.key == "c3" else cfg.lrs[0])
+    mode = args.mode or cfg.mode
+    numels = cfg.numels
+    n_model = sum(numels)
+    offs, n_alloc = workloads.flat_layout(numels)
+    old = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
+    new = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
+    for t, (o, n) in enumerate(zip(offs, numels)):
+        workloads.fill_step_pair_(old[o:o + n], new[o:o + n], *workloads.seeds(cfg.number, t),
+                                  lr, mode)
+    dplan = DiffPlan([old[o:o + n] for o, n in zip(offs, numels)],
+                     [new[o:o + n] for o, n in zip(offs, numels)], n_model // 8 + 65536)
+    dplan.run()
+    nnz = dplan.changed()
+    idx, val, offsets = dplan.idx[:nnz], dplan.val[:nnz], dplan.offsets
+    pos, pos_off = sbd.wire_encode(idx, offsets, numels)
+    back = sbd.wire_decode(pos, pos_off, offsets, numels)
+    ok = torch.equal(back, idx)
+    checksum = sbd.wire_checksum(pos, val)
+    log(f"[bench] wire, {cfg.key}: {nnz:,} changed; positions block {pos.numel():,} bytes "
+        f"({pos.numel() / max(nnz, 1):.3f} per entry); round trip identical: {ok}; "
+        f"checksum {checksum:#x}")
+    if not ok:
+        print("bench.py: wire decode does not invert encode", file=sys.stderr)
+        sys.exit(1)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    from sparse_bf16_delta_amd import _abi
+    import ctypes
+    lib = _abi.load()
+    k = len(numels)
+    nums = (ctypes.c_int64 * k)(*numels)
+    ws = torch.empty(lib.delta_workspace_size(0, k), dtype=torch.uint8, device=dev)
+    po2 = torch.empty_like(pos_off)
+    out = torch.empty_like(idx)
+    hashes = torch.empty(2, dtype=torch.int64, device=dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def enc():
+        _abi.check(lib.delta_wire_encode(k, nums, idx.data_ptr(), offsets.data_ptr(), nnz,
+                                         pos.data_ptr(), pos.numel(), po2.data_ptr(),
+                                         ws.data_ptr(), ws.numel(), sh))
+
+    def dec():
+        _abi.check(lib.delta_wire_decode(k, nums, pos.data_ptr(), pos_off.data_ptr(),
+                                         offsets.data_ptr(), nnz, out.data_ptr(), ws.data_ptr(),
+                                         ws.numel(), sh))
+
+    def hsh():
+        _abi.check(lib.delta_wire_hash(pos.data_ptr(), pos.numel(), val.data_ptr(), nnz,
+                                       hashes.data_ptr(), sh))
+
+    rows = {}
+    for name, fn, b in (("encode", enc, 4 * nnz + pos.numel()),
+                        ("decode", dec, pos.numel() + 4 * nnz),
+                        ("hash", hsh, pos.numel() + 2 * nnz)):
+        ms = timed(fn)
+        rows[name] = {"ms": round(ms, 4), "bytes": b,
+                      "frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] {name:7s} {ms:8.3f} ms  {b / (ms * 1e-3) / 1e9:8.1f} GB/s "
+            f"({100 * rows[name]['frac']:.1f} % of peak)")
+    print(json.dumps({
+        "metric": "wire encoding of the delta: encode, decode and hash times",
+        "value": None, "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": False, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": f"{cfg.title}: {k} tensors, {n_model} elements, {mode} step lr "
+                               f"{lr:g}"},
+        "changed": nnz, "positions_bytes": pos.numel(), "rows": rows,
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None)},
+    }), flush=True)
 
 
 def receiver_run(args, props):

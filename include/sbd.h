@@ -299,6 +299,56 @@ delta_status xor_apply_streamed(uint16_t *snapshot, const uint16_t *mask_host, i
                                 void *copy_stream, void *apply_stream);
 
 /*
+ * Wire encoding.  [VERL] encode.py: a flush carries the positions of all its
+ * parameters as one byte block -- each parameter's positions written with a
+ * width of 2 or 4 bytes (here: 2 when the parameter has at most 65536
+ * elements, so every local index fits; little-endian), with each parameter's
+ * start and end in the block (`DeltaParam.pos_start/pos_end`) -- and a
+ * checksum computed before sending and after receiving:
+ * hash(positions) ^ (hash(values) << 1), where hash is torch.hash_tensor's
+ * XOR of the elements widened to 64 bits (bytes zero-extended; bf16 values
+ * widened to IEEE double, NaNs quiet, taken as bits).  The combination is
+ * left to the caller (it exceeds 64 bits).
+ */
+
+/*
+ * delta_wire_encode -- positions byte block of a delta_diff_many result.
+ *  numels              (host) the parameters' sizes (they fix the widths).
+ *  idx, offsets        device, as delta_diff_many wrote them; entries
+ *                      j < min(offsets[nparams], max_entries) are encoded.
+ *  positions           device bytes, room for `positions_capacity`: a
+ *                      position is written only if all its bytes fit, so
+ *                      nothing past the capacity is touched and the block
+ *                      is exact up to the last whole position.
+ *  pos_offsets         device int64[nparams+1]: each parameter's start in the
+ *                      block; pos_offsets[nparams] is the block's full size.
+ *  ws, ws_bytes        at least delta_workspace_size(0, nparams).
+ * Errors: DELTA_E_INVALID, DELTA_E_RANGE (numel > 2^31-1), DELTA_E_WORKSPACE,
+ * DELTA_E_HIP.
+ */
+delta_status delta_wire_encode(int32_t nparams, const int64_t *numels, const int32_t *idx,
+                               const int64_t *offsets, int64_t max_entries, uint8_t *positions,
+                               int64_t positions_capacity, int64_t *pos_offsets, void *ws,
+                               size_t ws_bytes, void *stream);
+
+/*
+ * delta_wire_decode -- inverse of delta_wire_encode: int32 parameter-local
+ * indices (the delta_diff_many layout) for entries j < min(offsets[nparams],
+ * max_entries), from the byte block and the device pos_offsets and offsets.
+ */
+delta_status delta_wire_decode(int32_t nparams, const int64_t *numels, const uint8_t *positions,
+                               const int64_t *pos_offsets, const int64_t *offsets,
+                               int64_t max_entries, int32_t *idx, void *ws, size_t ws_bytes,
+                               void *stream);
+
+/*
+ * delta_wire_hash -- hashes[0] = hash of the npos position bytes, hashes[1] =
+ * hash of the nval bf16 values (device uint64[2], overwritten).
+ */
+delta_status delta_wire_hash(const uint8_t *positions, int64_t npos, const uint16_t *values,
+                             int64_t nval, uint64_t *hashes, void *stream);
+
+/*
  * delta_last_error -- message for the calling thread's last non-OK status
  * (empty string if none).  The pointer stays valid until the next call on
  * the same thread.

@@ -21,6 +21,10 @@ from .ops import (  # noqa: F401
     xor_apply_,
     xor_apply_streamed_,
     xor_mask,
+    wire_checksum,
+    wire_decode,
+    wire_encode,
+    wire_hashes,
 )
 from .sharding import flat_offset, shard0_piece  # noqa: F401
 
@@ -28,4 +32,5 @@ __all__ = [
     "DeltaError", "DeltaRangeError", "load", "diff", "diff_many", "apply_", "apply_many_",
     "xor_mask", "xor_apply_", "workspace", "workspace_size", "default_capacity",
     "shard0_piece", "flat_offset", "apply_streamed_", "xor_apply_streamed_",
+    "wire_encode", "wire_decode", "wire_hashes", "wire_checksum",
 ]

@@ -54,6 +54,9 @@ SIGNATURES = {
     "delta_apply_streamed": (_st, [_i32, _vp, _vp, _i32, _vp, _vp, _sz, _vp, _vp]),
     "xor_streamed_staging_size": (_sz, [_i64]),
     "xor_apply_streamed": (_st, [_vp, _vp, _i64, _i64, _vp, _sz, _vp, _vp]),
+    "delta_wire_encode": (_st, [_i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "delta_wire_decode": (_st, [_i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "delta_wire_hash": (_st, [_vp, _i64, _vp, _i64, _vp, _vp]),
     "xor_mask": (_st, [_vp, _vp, _vp, _i64, _vp]),
     "xor_apply": (_st, [_vp, _vp, _i64, _vp]),
     "delta_last_error": (ctypes.c_char_p, []),

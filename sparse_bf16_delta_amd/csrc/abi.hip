@@ -290,6 +290,89 @@ delta_status xor_apply_streamed(uint16_t* snapshot, const uint16_t* mask_host, i
   return DELTA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Per-parameter position widths into the workspace's table region.
+delta_status upload_widths(const char* fn, int32_t nparams, const int64_t* numels, void* ws,
+                           size_t ws_bytes, hipStream_t s, int32_t** d_widths) {
+  if (nparams < 0) return fail(DELTA_E_INVALID, "%s: nparams=%d < 0", fn, nparams);
+  if (nparams > 0 && numels == nullptr) return fail(DELTA_E_INVALID, "%s: numels is null", fn);
+  std::vector<int32_t> widths(static_cast<size_t>(nparams > 0 ? nparams : 1), 2);
+  for (int32_t p = 0; p < nparams; ++p) {
+    if (numels[p] < 0 || numels[p] > kInt32Max)
+      return fail(numels[p] < 0 ? DELTA_E_INVALID : DELTA_E_RANGE,
+                  "%s: numels[%d]=%lld outside [0, 2^31-1]", fn, p, (long long)numels[p]);
+    widths[p] = numels[p] <= 65536 ? 2 : 4;
+  }
+  const sbd::WsLayout L = sbd::ws_layout(sbd::max_tiles_for(0, nparams), nparams);
+  if (ws == nullptr || ws_bytes < L.total)
+    return fail(DELTA_E_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, L.total);
+  *d_widths = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.table);
+  const hipError_t e = hipMemcpyAsync(*d_widths, widths.data(), sizeof(int32_t) * widths.size(),
+                                      hipMemcpyHostToDevice, s);
+  return e == hipSuccess ? DELTA_OK : hip_status(e, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+delta_status delta_wire_encode(int32_t nparams, const int64_t* numels, const int32_t* idx,
+                               const int64_t* offsets, int64_t max_entries, uint8_t* positions,
+                               int64_t positions_capacity, int64_t* pos_offsets, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (max_entries < 0 || positions_capacity < 0)
+    return fail(DELTA_E_INVALID, "delta_wire_encode: negative size");
+  if (offsets == nullptr || pos_offsets == nullptr)
+    return fail(DELTA_E_INVALID, "delta_wire_encode: null offsets");
+  if (max_entries > 0 && idx == nullptr)
+    return fail(DELTA_E_INVALID, "delta_wire_encode: null idx");
+  if (positions_capacity > 0 && positions == nullptr)
+    return fail(DELTA_E_INVALID, "delta_wire_encode: null positions");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* d_widths = nullptr;
+  const delta_status st =
+      upload_widths("delta_wire_encode", nparams, numels, ws, ws_bytes, s, &d_widths);
+  if (st != DELTA_OK) return st;
+  g_error.clear();
+  return hip_status(sbd::launch_wire_encode(nparams, d_widths, idx, offsets, max_entries,
+                                            positions, positions_capacity, pos_offsets, s),
+                    "delta_wire_encode launch");
+}
+
+delta_status delta_wire_decode(int32_t nparams, const int64_t* numels, const uint8_t* positions,
+                               const int64_t* pos_offsets, const int64_t* offsets,
+                               int64_t max_entries, int32_t* idx, void* ws, size_t ws_bytes,
+                               void* stream) {
+  if (max_entries < 0) return fail(DELTA_E_INVALID, "delta_wire_decode: max_entries < 0");
+  if (offsets == nullptr || pos_offsets == nullptr)
+    return fail(DELTA_E_INVALID, "delta_wire_decode: null offsets");
+  if (max_entries > 0 && (idx == nullptr || positions == nullptr))
+    return fail(DELTA_E_INVALID, "delta_wire_decode: null idx or positions");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* d_widths = nullptr;
+  const delta_status st =
+      upload_widths("delta_wire_decode", nparams, numels, ws, ws_bytes, s, &d_widths);
+  if (st != DELTA_OK) return st;
+  g_error.clear();
+  return hip_status(sbd::launch_wire_decode(nparams, d_widths, positions, pos_offsets, offsets,
+                                            max_entries, idx, s),
+                    "delta_wire_decode launch");
+}
+
+delta_status delta_wire_hash(const uint8_t* positions, int64_t npos, const uint16_t* values,
+                             int64_t nval, uint64_t* hashes, void* stream) {
+  if (npos < 0 || nval < 0) return fail(DELTA_E_INVALID, "delta_wire_hash: negative size");
+  if (hashes == nullptr || (npos > 0 && positions == nullptr) || (nval > 0 && values == nullptr))
+    return fail(DELTA_E_INVALID, "delta_wire_hash: null pointer");
+  g_error.clear();
+  return hip_status(sbd::launch_wire_hash(positions, npos, values, nval, hashes,
+                                          static_cast<hipStream_t>(stream)),
+                    "delta_wire_hash launch");
+}
+
 delta_status xor_mask(const uint16_t* old_bits, const uint16_t* new_bits, uint16_t* mask,
                       int64_t n, void* stream) {
   if (n < 0) return fail(DELTA_E_INVALID, "xor_mask: n=%lld < 0", (long long)n);

@@ -82,18 +82,8 @@ __device__ __forceinline__ void apply_chunk(
       const int64_t t = offsets[nparams];
       total = t < max_nnz ? t : max_nnz;
       if (j0 < total) {
-        // Largest p with offsets[p] <= j0 -- the non-empty parameter holding
-        // j0 -- by a 64-way search in wave 0: each step probes 64 evenly
-        // spaced offsets at once (two steps for up to 4096 parameters).
         const int lane = threadIdx.x;
-        int32_t lo = 0, hi = nparams;  // offsets[lo] <= j0 holds throughout
-        while (hi - lo > 1) {
-          const int32_t step = (hi - lo + 63) / 64;
-          const int32_t probe = lo + lane * step;
-          const uint64_t ok = __ballot(probe < hi && offsets[probe] <= j0);
-          lo += (63 - __builtin_clzll(ok)) * step;
-          hi = lo + step < hi ? lo + step : hi;
-        }
+        const int32_t lo = find_param_wave0(offsets, nparams, j0);
         if (lane == 0) {
           sh.p0 = lo;
           const int64_t end = j0 + kApplyChunk < total ? j0 + kApplyChunk : total;

@@ -96,6 +96,24 @@ struct SnapParam {
   int64_t numel;
 };
 
+// Called by the 64 lanes of wave 0 only: the largest p in [0, nparams) with
+// offsets[p] <= j -- the non-empty parameter holding entry j of a
+// concatenated delta -- by a 64-way search (each step probes 64 evenly
+// spaced offsets at once; two steps for up to 4096 parameters).
+__device__ __forceinline__ int32_t find_param_wave0(const int64_t* __restrict__ offsets,
+                                                    int32_t nparams, int64_t j) {
+  const int lane = threadIdx.x & 63;
+  int32_t lo = 0, hi = nparams;  // offsets[lo] <= j holds throughout
+  while (hi - lo > 1) {
+    const int32_t step = (hi - lo + 63) / 64;
+    const int32_t probe = lo + lane * step;
+    const uint64_t ok = __ballot(probe < hi && offsets[probe] <= j);
+    lo += (63 - __builtin_clzll(ok)) * step;
+    hi = lo + step < hi ? lo + step : hi;
+  }
+  return lo;
+}
+
 // Workspace layout (all offsets 256-byte aligned): a 256-byte header, then
 // per tile a count, an in-chunk prefix, a dense-list entry, a descriptor, a
 // compact and a wide slot (20 KB), per chunk a total and a base, and the
@@ -141,6 +159,17 @@ delta_status apply_streamed_impl(int32_t nparams, uint16_t* const* snap_ptrs,
 delta_status xor_apply_streamed_impl(uint16_t* snapshot, const uint16_t* mask_host, int64_t n,
                                      int64_t chunk_elems, void* staging, size_t staging_bytes,
                                      void* copy_stream, void* apply_stream, std::string& err);
+
+// Wire encoding (wire.hip): widths are per parameter, in device memory.
+hipError_t launch_wire_encode(int32_t nparams, const int32_t* widths, const int32_t* idx,
+                              const int64_t* offsets, int64_t max_entries, uint8_t* positions,
+                              int64_t positions_capacity, int64_t* pos_offsets,
+                              hipStream_t stream);
+hipError_t launch_wire_decode(int32_t nparams, const int32_t* widths, const uint8_t* positions,
+                              const int64_t* pos_offsets, const int64_t* offsets,
+                              int64_t max_entries, int32_t* idx, hipStream_t stream);
+hipError_t launch_wire_hash(const uint8_t* positions, int64_t npos, const uint16_t* values,
+                            int64_t nval, uint64_t* hashes, hipStream_t stream);
 
 hipError_t launch_xor_mask(const uint16_t* a, const uint16_t* b, uint16_t* out, int64_t n,
                            hipStream_t stream);

@@ -13,6 +13,8 @@ memory and the current stream only.  Names mirror the sources' callables:
   xor_apply_(snap, mask)
   apply_streamed_(snaps, ...)     -- receiver: apply a host-resident delta
   xor_apply_streamed_(snap, mask) -- chunk by chunk, copies overlapping applies
+  wire_encode / wire_decode / wire_checksum -- the flush's positions block
+                                     and checksum (verl review, encode.py)
 
 Bit patterns travel as bfloat16 tensors (int16/uint16 views are accepted too);
 indices are int32, counts and offsets int64, all on the same device.
@@ -317,6 +319,64 @@ def xor_apply_streamed_(snap: torch.Tensor, mask: torch.Tensor, chunk_elems: int
                                  ctypes.c_void_p(cs.cuda_stream),
                                  ctypes.c_void_p(as_.cuda_stream)))
     return snap
+
+
+def wire_width(numel: int) -> int:
+    """Bytes per position of a parameter in the wire encoding."""
+    return 2 if int(numel) <= 65536 else 4
+
+
+def wire_encode(idx: torch.Tensor, offsets: torch.Tensor, numels: Sequence[int]):
+    """Positions byte block of a diff_many result: (positions uint8, pos_offsets
+    int64[P+1]) on the device; one device-to-host read of the offsets sizes it."""
+    k = len(numels)
+    dev = idx.device
+    if idx.dtype != torch.int32 or offsets.dtype != torch.int64 or offsets.numel() != k + 1:
+        raise ValueError("idx must be int32 and offsets int64[nparams+1]")
+    off = offsets.cpu().tolist()
+    size = sum((off[p + 1] - off[p]) * wire_width(n) for p, n in enumerate(numels))
+    positions = torch.empty(max(size, 1), dtype=torch.uint8, device=dev)
+    pos_offsets = torch.empty(k + 1, dtype=torch.int64, device=dev)
+    lib = load()
+    ws = workspace(lib.delta_workspace_size(0, k), dev)
+    nums = (ctypes.c_int64 * max(k, 1))(*[int(n) for n in numels])
+    check(lib.delta_wire_encode(k, nums, _ptr(idx), _ptr(offsets), min(off[-1], idx.numel()),
+                                _ptr(positions), size, _ptr(pos_offsets), _ptr(ws), ws.numel(),
+                                _stream(dev)))
+    return positions[:size], pos_offsets
+
+
+def wire_decode(positions: torch.Tensor, pos_offsets: torch.Tensor, offsets: torch.Tensor,
+                numels: Sequence[int]) -> torch.Tensor:
+    """int32 parameter-local indices back from a positions block."""
+    k = len(numels)
+    dev = positions.device
+    total = int(offsets[k].item())
+    idx = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
+    lib = load()
+    ws = workspace(lib.delta_workspace_size(0, k), dev)
+    nums = (ctypes.c_int64 * max(k, 1))(*[int(n) for n in numels])
+    check(lib.delta_wire_decode(k, nums, _ptr(positions), _ptr(pos_offsets), _ptr(offsets),
+                                total, _ptr(idx), _ptr(ws), ws.numel(), _stream(dev)))
+    return idx[:total]
+
+
+def wire_hashes(positions: torch.Tensor, values: torch.Tensor) -> tuple[int, int]:
+    """(hash of the position bytes, hash of the bf16 values) as unsigned ints."""
+    _bits(values, "values")
+    if positions.dtype != torch.uint8 or positions.device != values.device:
+        raise ValueError("positions must be uint8 on the values' device")
+    h = torch.empty(2, dtype=torch.int64, device=values.device)
+    check(load().delta_wire_hash(_ptr(positions), positions.numel(), _ptr(values),
+                                 values.numel(), _ptr(h), _stream(values.device)))
+    a, b = h.cpu().tolist()
+    return a & (2 ** 64 - 1), b & (2 ** 64 - 1)
+
+
+def wire_checksum(positions: torch.Tensor, values: torch.Tensor) -> int:
+    """The flush checksum: hash(positions) ^ (hash(values) << 1), unbounded."""
+    p, v = wire_hashes(positions, values)
+    return p ^ (v << 1)
 
 
 def xor_mask(old: torch.Tensor, new: torch.Tensor, out: torch.Tensor | None = None):

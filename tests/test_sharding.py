@@ -99,3 +99,20 @@ def test_streamed_abi_rejects_bad_chunks():
                                   ctypes.c_void_p(256), 8, None, None) == _abi.DELTA_E_WORKSPACE
     assert lib.delta_streamed_staging_size(-1, 1, 0, 0) == 0
     assert lib.xor_streamed_staging_size(0) == 0
+
+
+def test_wire_abi_rejects_bad_arguments():
+    lib = _abi.load()
+    one = ctypes.c_void_p(16)
+    nums = (ctypes.c_int64 * 2)(10, -1)
+    assert lib.delta_wire_encode(2, nums, one, one, 5, one, 10, one, one, 1 << 30, None) == \
+        _abi.DELTA_E_INVALID
+    assert "numels[1]" in lib.delta_last_error().decode()
+    big = (ctypes.c_int64 * 1)(1 << 31)
+    assert lib.delta_wire_decode(1, big, one, one, one, 5, one, one, 1 << 30, None) == \
+        _abi.DELTA_E_RANGE
+    ok = (ctypes.c_int64 * 1)(10)
+    assert lib.delta_wire_encode(1, ok, one, one, 5, one, 10, one, one, 1, None) == \
+        _abi.DELTA_E_WORKSPACE
+    assert lib.delta_wire_hash(None, 4, None, 0, one, None) == _abi.DELTA_E_INVALID
+    assert lib.delta_wire_hash(one, -1, one, 0, one, None) == _abi.DELTA_E_INVALID
