@@ -13,6 +13,9 @@ Step 2 turns the receiver snapshot into `new`, step 4 turns it back into
 Default workload: the Llama-7B-shaped list (291 tensors, 6,738,415,616 bf16
 elements), weights N(0, 0.02), bf16-resident step at lr 1e-6 (about 1 %
 changed).  Inputs are generated on the GPU and resident in HBM before timing.
+Other modes: --config c1/c2 (smaller lists), c4 (density sweep), c5 (the
+405B-shaped 10-layer share, streamed layer by layer, in place), --shards W,
+--receiver, --wire.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -77,9 +80,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4"],
+    ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5"],
                     help="c3 (default): the 7B-shaped list; c1, c2: smaller lists; "
-                         "c4: density sweep on one flat 2^28-element tensor (table on stderr)")
+                         "c4: density sweep on one flat 2^28-element tensor (table on stderr); "
+                         "c5: the 405B-shaped 10-layer share, streamed layer by layer")
     ap.add_argument("--lr", type=float, default=None)
     ap.add_argument("--mode", default=None, choices=[None, "fp32_master", "bf16_resident"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -129,6 +133,9 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     if args.config == "c4":
         density_sweep(args, props)
+        return
+    if args.config == "c5":
+        layer_stream_run(args, props)
         return
     if args.shards > 0:
         sharded_run(args, props)
@@ -702,6 +709,162 @@ def density_sweep(args, props):
         "sweep": rows,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None)},
     }), flush=True)
+
+
+def layer_stream_run(args, props):
+    """The 405B-shaped share (10 layers of 7 tensors, 64 GB per snapshot, old
+    and new resident), streamed one layer at a time, each op in place on the
+    resident `old`: xor_mask (old, new) into a one-layer mask, diff_many over
+    the layer's tensors, apply_many into old (old becomes new), xor_apply of
+    the mask (old comes back).  Per-op times are summed over the layers; a
+    step is all ten layers."""
+    import torch
+
+    import sparse_bf16_delta_amd as sbd
+    from sparse_bf16_delta_amd.plan import ApplyPlan, DiffPlan
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    cfg = workloads.CONFIGS["c5"]
+    lr = args.lr if args.lr is not None else cfg.lrs[0]
+    mode = args.mode or cfg.mode
+    numels = cfg.numels
+    n_model = sum(numels)
+    offs, n_alloc = workloads.flat_layout(numels)
+    per = 7
+    layers = len(numels) // per
+    log(f"[bench] device {props.name}, {props.total_memory / 2**30:.0f} GiB")
+    log(f"[bench] workload c5: {layers} layers x {per} tensors, {n_model:,} elements, "
+        f"lr {lr:g}, {mode}")
+    t0 = time.perf_counter()
+    old = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
+    new = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
+    for t, (o, n) in enumerate(zip(offs, numels)):
+        workloads.fill_step_pair_(old[o:o + n], new[o:o + n], *workloads.seeds(cfg.number, t),
+                                  lr, mode)
+    torch.cuda.synchronize()
+    log(f"[bench] generated inputs in {time.perf_counter() - t0:.1f} s")
+    bounds = [offs[per * l] for l in range(layers)] + [n_alloc]
+    region = max(bounds[l + 1] - bounds[l] for l in range(layers))
+    mask = torch.empty(region, dtype=torch.int16, device=dev)
+    L = []
+    for l in range(layers):
+        r0, r1 = bounds[l], bounds[l + 1]
+        ts = range(per * l, per * l + per)
+        lo = [old[offs[t]:offs[t] + numels[t]] for t in ts]
+        ln = [new[offs[t]:offs[t] + numels[t]] for t in ts]
+        n_l = sum(numels[t] for t in ts)
+        cap = n_l // 8 + 65536
+        dp = DiffPlan(lo, ln, cap)
+        dp.run()
+        k = dp.changed()
+        if k > cap:
+            cap = k + 65536
+            dp = DiffPlan(lo, ln, cap)
+            dp.run()
+            k = dp.changed()
+        poff = torch.tensor([offs[t] for t in ts], dtype=torch.int64, device=dev)
+        pos = dp.idx[:k].long() + torch.repeat_interleave(poff, dp.nnz)
+        g128 = int(((pos >> 6)[1:] != (pos >> 6)[:-1]).sum().item()) + 1 if k else 0
+        del pos, poff
+        # checksum of the delta: the restored `old` must give the same one again
+        ck = (int(dp.idx[:k].to(torch.int64).sum().item()),
+              int(dp.val[:k].view(torch.int16).to(torch.int64).sum().item()))
+        L.append({"r0": r0, "r1": r1, "n": n_l, "nnz": k, "g128": g128, "dp": dp,
+                  "ap": ApplyPlan(lo), "cap": cap, "ck": ck, "news": ln})
+    nnz_total = sum(x["nnz"] for x in L)
+    log(f"[bench] changed {nnz_total:,} of {n_model:,} ({nnz_total / n_model:.4%})")
+
+    names = ["delta_diff_many", "delta_apply_many", "xor_mask", "xor_apply"]
+
+    def layer_ops(x, ev=None):
+        a, b = old[x["r0"]:x["r1"]], new[x["r0"]:x["r1"]]
+        m = mask[:x["r1"] - x["r0"]]
+        ops = (lambda: x["dp"].run(),
+               lambda: x["ap"].run(x["dp"].idx, x["dp"].val, x["dp"].offsets, x["cap"]),
+               lambda: sbd.xor_mask(a, b, out=m),
+               lambda: sbd.xor_apply_(a, m))
+        # mask first (old, new), then diff, apply (old -> new), xor_apply (-> old)
+        for i in (2, 0, 1, 3):
+            if ev is not None:
+                ev[2 * i].record(stream)
+            ops[i]()
+            if ev is not None:
+                ev[2 * i + 1].record(stream)
+
+    # one checked pass: after apply the layer equals new, after xor_apply old again
+    for x in L:
+        a, b = old[x["r0"]:x["r1"]], new[x["r0"]:x["r1"]]
+        m = mask[:x["r1"] - x["r0"]]
+        sbd.xor_mask(a, b, out=m)
+        x["ap"].run(x["dp"].idx, x["dp"].val, x["dp"].offsets, x["cap"])
+        if not torch.equal(a.view(torch.int16), b.view(torch.int16)):
+            print("bench.py: c5 apply check failed", file=sys.stderr)
+            sys.exit(1)
+        sbd.xor_apply_(a, m)
+    for _ in range(args.warmup):
+        for x in L:
+            layer_ops(x)
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in L]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        for x, ev in zip(L, evs[k]):
+            layer_ops(x, ev)
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t_start) / args.steps
+    op_ms = [sum(evs[k][l][2 * i].elapsed_time(evs[k][l][2 * i + 1])
+                 for k in range(args.steps) for l in range(layers)) / args.steps
+             for i in range(4)]
+    for x in L:  # the restored old gives the same delta again
+        x["dp"].run()
+        ck = (int(x["dp"].idx[:x["nnz"]].to(torch.int64).sum().item()),
+              int(x["dp"].val[:x["nnz"]].view(torch.int16).to(torch.int64).sum().item()))
+        if x["dp"].changed() != x["nnz"] or ck != x["ck"]:
+            print("bench.py: c5 timed steps changed the result", file=sys.stderr)
+            sys.exit(1)
+    g128 = sum(x["g128"] for x in L)
+    alg = [4 * n_model + 6 * nnz_total, 6 * nnz_total + 256 * g128, 6 * n_alloc,
+           2 * n_alloc + 256 * g128]
+    kernels = []
+    for name, ms, b in zip(names, op_ms, alg):
+        gbs = b / (ms * 1e-3) / 1e9
+        kernels.append({"kernel": name, "ms": round(ms, 3), "launches": layers, "alg_bytes": b,
+                        "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "traffic": None})
+        log(f"[bench] {name:17s} {ms:9.3f} ms per step ({layers} launches)  {gbs:8.1f} GB/s "
+            f"({100 * gbs / HBM_PEAK_GBS:.1f} % of peak)")
+    dom = max(range(4), key=lambda i: op_ms[i])
+    result = {
+        "metric": METRIC,
+        "value": round(2 * n_model / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u16", "data": "synthetic",
+        "config": {"workload": f"{cfg.title}: {len(numels)} tensors, {n_model} bf16 elements, "
+                               f"{mode} step lr {lr:g}, streamed layer by layer",
+                   "tensors": len(numels), "layers": layers, "elements": n_model,
+                   "changed": nnz_total, "density": round(nnz_total / n_model, 6),
+                   "touched_lines_128B": g128,
+                   "step": "per layer: xor_mask, diff_many, apply_many, xor_apply, in place"},
+        "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": kernels[dom]["achieved_gbs"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["frac"],
+                     "traffic": None},
+        "kernels": kernels,
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        x = L[0]
+        result["cpu_baseline"] = cpu_baseline(args, cfg, old_views(old, offs, numels, 0, per),
+                                              x["news"], x["dp"], x["nnz"])
+    print(json.dumps(result), flush=True)
+
+
+def old_views(old, offs, numels, layer, per):
+    return [old[offs[t]:offs[t] + numels[t]] for t in range(per * layer, per * layer + per)]
 
 
 def cpu_baseline(args, cfg, olds, news, dplan, nnz_total):

@@ -53,10 +53,13 @@ typedef enum {
  * `nparams` tensors holding `total_elems` elements in all (an upper bound
  * that holds for any split of the elements).  Pure host function.
  * The workspace holds, per 32768-element tile of the compaction, its change
- * count, its running offset, its descriptor and two staging slots (4 KB and
- * 16 KB) for its compacted entries -- about 0.63 bytes per element -- plus
- * the device copy of the parameter table.  Its contents on entry do not
- * matter and are clobbered.  Returns 0 for negative arguments.
+ * count, its running offset, its descriptor, a 4 KB staging slot and a 16 KB
+ * share of a staging arena for its compacted entries -- about 0.63 bytes per
+ * element -- plus the device copy of the parameter table.  Every function
+ * taking a workspace requires it to start on a 256-byte boundary (device
+ * allocations do) and fails with DELTA_E_WORKSPACE otherwise.  Its contents
+ * on entry do not matter and are clobbered.  Returns 0 for negative
+ * arguments.
  */
 size_t delta_workspace_size(int64_t total_elems, int32_t nparams);
 

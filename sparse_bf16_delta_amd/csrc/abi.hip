@@ -34,6 +34,11 @@ constexpr int64_t kInt32Max = 2147483647LL;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The workspace regions are laid out at 256-byte offsets and written with
+// 16-byte stores, so the workspace itself must start on a 256-byte boundary
+// (every hipMalloc and torch allocation does).
+bool ws_aligned(const void* ws) { return (reinterpret_cast<uintptr_t>(ws) & 255u) == 0; }
+
 }  // namespace
 
 namespace sbd {
@@ -47,7 +52,9 @@ WsLayout ws_layout(int64_t max_tiles, int32_t nparams) {
   const size_t tiles = size_t(max_tiles);
   const size_t chunks = (tiles + size_t(kScanChunk) - 1) / size_t(kScanChunk);
   WsLayout L;
+  const size_t entry = sizeof(DiffParam) > sizeof(SnapParam) ? sizeof(DiffParam) : sizeof(SnapParam);
   L.ndense = 0;
+  L.arena_next = 8;
   L.counts = 256;
   L.inpfx = L.counts + align256(sizeof(uint32_t) * tiles);
   L.chunk_tot = L.inpfx + align256(sizeof(uint32_t) * tiles);
@@ -55,7 +62,7 @@ WsLayout ws_layout(int64_t max_tiles, int32_t nparams) {
   L.dense_list = L.chunk_base + align256(sizeof(uint64_t) * (chunks + 1));
   L.tile_desc = L.dense_list + align256(sizeof(int32_t) * tiles);
   L.table = L.tile_desc + align256(sizeof(TileDesc) * tiles);
-  const size_t entry = sizeof(DiffParam) > sizeof(SnapParam) ? sizeof(DiffParam) : sizeof(SnapParam);
+  L.tile_pos = L.table + align256(entry * size_t(nparams > 0 ? nparams : 1));
   // The slots start a fixed 9472 bytes past a 1 MB boundary of the workspace,
   // whatever the table sizes before them.  Where the 4 KB compact slots fall
   // relative to HBM's channel interleave measurably changes the cost of the
@@ -64,7 +71,7 @@ WsLayout ws_layout(int64_t max_tiles, int32_t nparams) {
   // (the best of those tried; rotating each tile's start in its slot was
   // worse still).
   constexpr size_t kSlotAlign = size_t(1) << 20, kSlotSkew = 9472;
-  L.compact = (L.table + align256(entry * size_t(nparams > 0 ? nparams : 1)) + kSlotAlign - 1) /
+  L.compact = (L.tile_pos + align256(sizeof(uint64_t) * tiles) + kSlotAlign - 1) /
                   kSlotAlign * kSlotAlign + kSlotSkew;
   L.wide = L.compact + sizeof(uint32_t) * size_t(kCompactWords) * tiles;
   L.total = L.wide + sizeof(uint32_t) * size_t(kWideWords) * tiles;
@@ -101,6 +108,8 @@ delta_status delta_diff(const uint16_t* old_bits, const uint16_t* new_bits, int6
   if (ws == nullptr || ws_bytes < L.total)
     return fail(DELTA_E_WORKSPACE, "delta_diff: workspace %zu bytes, need %zu", ws_bytes,
                 L.total);
+  if (!ws_aligned(ws))
+    return fail(DELTA_E_WORKSPACE, "delta_diff: workspace not 256-byte aligned");
   sbd::DiffParam single{old_bits, new_bits, n, 0, 0};
   const int64_t tiles = (n + sbd::kDiffTile - 1) / sbd::kDiffTile;  // < kMaxTiles for n < 2^31
   g_error.clear();
@@ -160,6 +169,7 @@ delta_status diff_many_impl(const char* fn, bool global_idx, int32_t nparams,
   const sbd::WsLayout L = sbd::ws_layout(sbd::max_tiles_for(total, nparams), nparams);
   if (ws == nullptr || ws_bytes < L.total)
     return fail(DELTA_E_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, L.total);
+  if (!ws_aligned(ws)) return fail(DELTA_E_WORKSPACE, "%s: workspace not 256-byte aligned", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
   sbd::DiffParam* d_table = reinterpret_cast<sbd::DiffParam*>(static_cast<char*>(ws) + L.table);
   if (nparams > 0) {
@@ -244,6 +254,8 @@ delta_status delta_apply_many(int32_t nparams, uint16_t* const* snap_ptrs, const
   if (ws == nullptr || ws_bytes < need)
     return fail(DELTA_E_WORKSPACE, "delta_apply_many: workspace %zu bytes, need %zu", ws_bytes,
                 need);
+  if (!ws_aligned(ws))
+    return fail(DELTA_E_WORKSPACE, "delta_apply_many: workspace not 256-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   sbd::SnapParam* d_table = reinterpret_cast<sbd::SnapParam*>(static_cast<char*>(ws) + 256);
   const hipError_t e = hipMemcpyAsync(d_table, table.data(), sizeof(sbd::SnapParam) * table.size(),
@@ -309,6 +321,7 @@ delta_status upload_widths(const char* fn, int32_t nparams, const int64_t* numel
   const sbd::WsLayout L = sbd::ws_layout(sbd::max_tiles_for(0, nparams), nparams);
   if (ws == nullptr || ws_bytes < L.total)
     return fail(DELTA_E_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, L.total);
+  if (!ws_aligned(ws)) return fail(DELTA_E_WORKSPACE, "%s: workspace not 256-byte aligned", fn);
   *d_widths = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.table);
   const hipError_t e = hipMemcpyAsync(*d_widths, widths.data(), sizeof(int32_t) * widths.size(),
                                       hipMemcpyHostToDevice, s);

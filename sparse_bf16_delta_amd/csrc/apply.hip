@@ -19,13 +19,13 @@
 //  * Dense entries: when a workgroup's entries lie in one parameter and span
 //    at most kMergeSpread elements per entry (about 4 % density or more,
 //    where nearly every line is touched and masked writes dominate), the
-//    workgroup instead reads each 128-byte line strictly inside that span,
-//    patches it from the entries (kept sorted in LDS, found by binary
-//    search) and writes it back whole.  The two edge lines, which a
+//    workgroup instead reads the lines strictly inside that span into LDS,
+//    8192 elements at a time, patches them from its entries (held in
+//    registers) and writes them back whole.  The two edge lines, which a
 //    neighbouring workgroup may share, are still written entry by entry.
 //  * Snapshot pointers come from the parameter table in memory; they are
 //    cast to the global address space so the stores are global, not flat.
-//  * The parameter of the workgroup's first entry comes from one binary
+//  * The parameter of the workgroup's first entry comes from one 64-way
 //    search over the device offsets; each lane then walks forward.  The
 //    offsets are read on the GPU, so no host round trip separates diff and
 //    apply.

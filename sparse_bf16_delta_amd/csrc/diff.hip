@@ -19,12 +19,15 @@
 //     group totals are scanned in LDS, giving every change its slot inside
 //     the tile in ascending element order.  A tile with at most 4096 changes
 //     is compacted in LDS as (tile-local index << 16 | new bits) and copied
-//     with 16-byte nontemporal stores into a workspace slot of its own: a
-//     4 KB one for up to 1024 changes, else a 16 KB one.  (A sparse tile's
-//     entries then land close to the previous tile's: at a 16 KB stride the
-//     few KB each tile writes cost measurably more HBM time.)  A denser tile
-//     stores its 4 KB change mask instead.  The tile count goes to a per-tile
-//     array and the workgroup ends.
+//     with 16-byte nontemporal stores: a tile with up to 1024 changes into a
+//     4 KB workspace slot of its own, a tile with more into a staging arena
+//     shared by all tiles, at a position it takes with one atomic add on a
+//     workspace counter (so the arena fills as one dense, ascending write
+//     stream; fixed 16 KB slots, a few KB written in each, cost 1.3 ms more
+//     on the 7B-shaped list at 8 % density, while for sparse tiles the
+//     atomic's latency costs more than the slot saves).  A denser tile
+//     stores its 4 KB change mask in its slot instead.  The tile count goes
+//     to a per-tile array and the workgroup ends.
 //  2. Scan.  One workgroup per 4096 tiles scans their counts (prefix inside
 //     the chunk, chunk total) and lists the dense tiles; one workgroup scans
 //     the chunk totals and writes the per-parameter counts and offsets.
@@ -38,9 +41,10 @@
 // are done, which keeps the next tile's loads from being issued; measured on
 // the 7B-shaped list it cost more than the 8 extra bytes per changed element
 // that the slot round trip adds here.
-// Traffic: the 4n-byte read happens once; a sparse tile adds 4 bytes written
+// Traffic: the 4n-byte read happens once; a staged tile adds 4 bytes written
 // and 4 read per changed element, a dense tile re-reads `new` (2 bytes per
-// element), and the tile count, prefix and descriptor add 40 bytes per tile.
+// element), and the tile count, prefix, position and descriptor add about 60
+// bytes per tile.
 #include "sbd_internal.h"
 
 namespace sbd {
@@ -186,9 +190,17 @@ __device__ __forceinline__ void tile_offsets(const uint32_t (&m)[kDiffIters],
 // For a parameter list: every tile's descriptor (base pointers, first index,
 // length), so a workgroup needs one load, not a parameter search, before its
 // data loads.
+// Clears the staging arena's fill counter before the count kernel (the
+// parameter-list form clears it in the prepare kernel instead).
+__global__ __launch_bounds__(64) void zero_ctr_kernel(unsigned long long* ctr) {
+  if (threadIdx.x == 0) *ctr = 0ull;
+}
+
 __global__ __launch_bounds__(256) void diff_prepare_kernel(const DiffParam* __restrict__ table,
                                                            int32_t nparams, int64_t total_tiles,
-                                                           TileDesc* __restrict__ tdesc) {
+                                                           TileDesc* __restrict__ tdesc,
+                                                           unsigned long long* __restrict__ ctr) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ctr = 0ull;
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   for (int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; t < total_tiles; t += stride) {
     // largest p whose first tile is <= t (skips empty parameters)
@@ -217,8 +229,10 @@ __global__ __launch_bounds__(256) void diff_prepare_kernel(const DiffParam* __re
 template <bool kMany>
 __global__ __launch_bounds__(kDiffBlock) void diff_count_kernel(
     const TileDesc* __restrict__ tdesc, DiffParam single, uint32_t* __restrict__ counts,
-    uint32_t* __restrict__ compact, uint32_t* __restrict__ wide, uint32_t* __restrict__ ndense) {
+    uint32_t* __restrict__ compact, uint32_t* __restrict__ wide, uint32_t* __restrict__ ndense,
+    uint64_t* __restrict__ tile_pos, unsigned long long* __restrict__ ctr) {
   __shared__ __attribute__((aligned(16))) uint32_t s_stage[kStageCap];
+  __shared__ uint64_t s_pos;
   __shared__ uint32_t s_wtot[kGroups];
 
   const int tid = threadIdx.x;
@@ -261,6 +275,12 @@ __global__ __launch_bounds__(kDiffBlock) void diff_count_kernel(
     if (tile == 0) *ndense = 0u;  // the scan kernel, launched next, lists dense tiles
   }
   if (agg <= static_cast<uint32_t>(kStageCap)) {
+    if (tid == 0 && agg > static_cast<uint32_t>(kCompactCap)) {
+      // whole 16-byte quads of the arena, so every tile's run starts aligned
+      const uint64_t p = atomicAdd(ctr, static_cast<unsigned long long>((agg + 3u) / 4u));
+      s_pos = p;
+      tile_pos[tile] = p;
+    }
 #pragma unroll
     for (int j = 0; j < kDiffIters; ++j) {
       const uint32_t mm = m[j];
@@ -283,7 +303,7 @@ __global__ __launch_bounds__(kDiffBlock) void diff_count_kernel(
     // placing kernel); the last one may carry up to three stale LDS words
     // past `agg`, which stay inside the slot and are never read.
     uint32_t* slot = agg <= static_cast<uint32_t>(kCompactCap) ? compact + tile * kCompactWords
-                                                               : wide + tile * kWideWords;
+                                                               : wide + s_pos * 4u;
     for (uint32_t p = static_cast<uint32_t>(tid) * 4u; p < agg; p += kDiffBlock * 4u) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(&s_stage[p]);
       __builtin_nontemporal_store(w, global_ptr(reinterpret_cast<u32x4*>(slot + p)));
@@ -397,8 +417,10 @@ __global__ __launch_bounds__(kDiffBlock) void diff_place_kernel(
     const TileDesc* __restrict__ tdesc, int64_t total_tiles, int32_t nchunks, int32_t tiles_per_wg,
     const uint32_t* __restrict__ inpfx, const uint64_t* __restrict__ chunk_base,
     const uint32_t* __restrict__ compact, const uint32_t* __restrict__ wide,
-    IdxT* __restrict__ idx, uint16_t* __restrict__ val, int64_t capacity) {
+    IdxT* __restrict__ idx, uint16_t* __restrict__ val, int64_t capacity,
+    const uint64_t* __restrict__ tile_pos) {
   static_assert(sizeof(IdxT) == 8 ? kMany : true, "global indices need a parameter table");
+  __shared__ uint64_t s_tpos[kPlaceTiles];
   constexpr int kUnroll = 4;
   __shared__ uint64_t s_off[kPlaceTiles + 1];  // output offset of each tile
   __shared__ IdxT s_first[kPlaceTiles];  // index written for the tile's first element
@@ -413,6 +435,7 @@ __global__ __launch_bounds__(kDiffBlock) void diff_place_kernel(
     const int64_t t = t0 + tid;
     s_off[tid] = t < total_tiles ? chunk_base[t / kScanChunk] + inpfx[t] : chunk_base[nchunks];
     if (tid < nt) {
+      s_tpos[tid] = tile_pos[t];
       if constexpr (kMany) {
         if constexpr (sizeof(IdxT) == 8)
           s_first[tid] = tdesc[t].flat_offset + tdesc[t].e0;
@@ -461,7 +484,7 @@ __global__ __launch_bounds__(kDiffBlock) void diff_place_kernel(
         ok[u] = jj[u] < cap;
         const uint32_t* slot = s_off[k + 1] - s_off[k] <= static_cast<uint64_t>(kCompactCap)
                                    ? compact + (t0 + k) * kCompactWords
-                                   : wide + (t0 + k) * kWideWords;
+                                   : wide + s_tpos[k] * 4u;
         if (ok[u]) w[u] = *global_ptr(slot + p);
       }
     }
@@ -583,7 +606,7 @@ void launch_place(const TileDesc* tdesc, const DiffParam& single, int64_t total_
                   int32_t nchunks, const uint32_t* inpfx, const uint64_t* chunk_base,
                   const uint32_t* compact, const uint32_t* wide, const int32_t* dense_list,
                   const uint32_t* ndense, IdxT* idx, uint16_t* val, int64_t capacity,
-                  hipStream_t stream) {
+                  const uint64_t* tile_pos, hipStream_t stream) {
   // enough placing workgroups to fill the GPU, up to kPlaceTiles tiles each
   int64_t per_wg = total_tiles / 2048;
   per_wg = per_wg < 1 ? 1 : (per_wg > kPlaceTiles ? kPlaceTiles : per_wg);
@@ -593,7 +616,7 @@ void launch_place(const TileDesc* tdesc, const DiffParam& single, int64_t total_
       static_cast<unsigned>(total_tiles < dense_max ? total_tiles : dense_max);
   diff_place_kernel<kMany, IdxT><<<dim3(place_grid), dim3(kDiffBlock), 0, stream>>>(
       tdesc, total_tiles, nchunks, static_cast<int32_t>(per_wg), inpfx, chunk_base, compact, wide,
-      idx, val, capacity);
+      idx, val, capacity, tile_pos);
   diff_dense_kernel<kMany, IdxT><<<dim3(dense_grid), dim3(kDiffBlock), 0, stream>>>(
       tdesc, single, dense_list, ndense, inpfx, chunk_base, compact, idx, val, capacity);
 }
@@ -614,6 +637,8 @@ hipError_t launch_diff(const DiffParam* d_table, const DiffParam& single, int32_
   TileDesc* tdesc = reinterpret_cast<TileDesc*>(base + L.tile_desc);
   uint32_t* compact = reinterpret_cast<uint32_t*>(base + L.compact);
   uint32_t* wide = reinterpret_cast<uint32_t*>(base + L.wide);
+  uint64_t* tile_pos = reinterpret_cast<uint64_t*>(base + L.tile_pos);
+  unsigned long long* ctr = reinterpret_cast<unsigned long long*>(base + L.arena_next);
   // d_table == nullptr: one tensor (nparams == 1, `single`) or an empty list
   // (nparams == 0, no tiles).  Global indices come with a table only.
   const bool many = d_table != nullptr;
@@ -626,12 +651,13 @@ hipError_t launch_diff(const DiffParam* d_table, const DiffParam& single, int32_
       int64_t prep_blocks = (total_tiles + 255) / 256;
       if (prep_blocks > 65536) prep_blocks = 65536;
       diff_prepare_kernel<<<dim3(unsigned(prep_blocks)), dim3(256), 0, stream>>>(
-          d_table, nparams, total_tiles, tdesc);
+          d_table, nparams, total_tiles, tdesc, ctr);
       diff_count_kernel<true><<<dim3(grid), dim3(kDiffBlock), 0, stream>>>(tdesc, single, counts,
-                                                                           compact, wide, ndense);
+                                                                           compact, wide, ndense, tile_pos, ctr);
     } else {
+      zero_ctr_kernel<<<dim3(1), dim3(64), 0, stream>>>(ctr);
       diff_count_kernel<false><<<dim3(grid), dim3(kDiffBlock), 0, stream>>>(nullptr, single,
-                                                                            counts, compact, wide, ndense);
+                                                                            counts, compact, wide, ndense, tile_pos, ctr);
     }
     diff_scan_chunks_kernel<<<dim3(unsigned(nchunks)), dim3(kScanBlock), 0, stream>>>(
         counts, total_tiles, inpfx, chunk_tot, dense_list, ndense);
@@ -646,15 +672,15 @@ hipError_t launch_diff(const DiffParam* d_table, const DiffParam& single, int32_
     if (many && global_idx)
       launch_place<true, int64_t>(tdesc, single, total_tiles, nchunks, inpfx, chunk_base, compact,
                                   wide, dense_list, ndense, static_cast<int64_t*>(idx), val,
-                                  capacity, stream);
+                                  capacity, tile_pos, stream);
     else if (many)
       launch_place<true, int32_t>(tdesc, single, total_tiles, nchunks, inpfx, chunk_base, compact,
                                   wide, dense_list, ndense, static_cast<int32_t*>(idx), val,
-                                  capacity, stream);
+                                  capacity, tile_pos, stream);
     else
       launch_place<false, int32_t>(tdesc, single, total_tiles, nchunks, inpfx, chunk_base, compact,
                                    wide, dense_list, ndense, static_cast<int32_t*>(idx), val,
-                                   capacity, stream);
+                                   capacity, tile_pos, stream);
   }
   return hipGetLastError();
 }

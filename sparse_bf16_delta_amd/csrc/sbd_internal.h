@@ -78,13 +78,15 @@ struct TileDesc {
 };
 
 // A tile with at most kStageCap changes is staged in LDS (4 bytes per entry)
-// and then copied to a workspace slot: a compact 4 KB slot when it has at
-// most kCompactCap changes, else a wide 16 KB one.  A denser tile stores its
-// change mask (one byte per 16-byte chunk, 8 per lane) in its compact slot.
+// and then copied out: into its own compact 4 KB slot when it has at most
+// kCompactCap changes, else into the shared staging arena (kWideWords words
+// per tile reserved in all, filled in whole 16-byte quads from a counter).
+// A denser tile stores its change mask (one byte per 16-byte chunk, 8 per
+// lane) in its compact slot.
 constexpr int kStageCap = 4096;
 constexpr int kCompactCap = 1024;
 constexpr int64_t kCompactWords = kCompactCap;  // uint32 per compact slot
-constexpr int64_t kWideWords = kStageCap;       // uint32 per wide slot
+constexpr int64_t kWideWords = kStageCap;       // arena uint32 reserved per tile
 // Tile counts are scanned in chunks of kScanChunk tiles, four per lane.
 constexpr int kScanBlock = 1024;
 constexpr int64_t kScanChunk = int64_t(kScanBlock) * 4;
@@ -114,12 +116,14 @@ __device__ __forceinline__ int32_t find_param_wave0(const int64_t* __restrict__ 
   return lo;
 }
 
-// Workspace layout (all offsets 256-byte aligned): a 256-byte header, then
-// per tile a count, an in-chunk prefix, a dense-list entry, a descriptor, a
-// compact and a wide slot (20 KB), per chunk a total and a base, and the
-// parameter table.
+// Workspace layout (all offsets 256-byte aligned): a 256-byte header (the
+// dense-tile count and the arena fill counter), then per tile a count, an
+// in-chunk prefix, a dense-list entry, a descriptor, an arena position, a
+// compact slot and its share of the arena (20 KB), per chunk a total and a
+// base, and the parameter table.
 struct WsLayout {
   size_t ndense;      // uint32: number of dense tiles
+  size_t arena_next;  // uint64: arena quads handed out so far
   size_t counts;      // uint32 per tile: changed elements
   size_t inpfx;       // uint32 per tile: exclusive prefix inside its chunk
   size_t chunk_tot;   // uint32 per chunk
@@ -128,7 +132,8 @@ struct WsLayout {
   size_t tile_desc;   // TileDesc per tile
   size_t table;       // DiffParam / SnapParam per parameter
   size_t compact;     // kCompactWords uint32 per tile
-  size_t wide;        // kWideWords uint32 per tile
+  size_t wide;        // the staging arena: kWideWords uint32 per tile
+  size_t tile_pos;    // uint64 per tile: its first arena quad
   size_t total;
 };
 

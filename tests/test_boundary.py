@@ -108,6 +108,16 @@ def test_argument_errors_return_before_any_launch():
                                 None) == _abi.DELTA_E_WORKSPACE
     assert lib.delta_apply_many(2, ptrs, ok2, one, one, None, 5, None, one, 1 << 20,
                                 None) == _abi.DELTA_E_INVALID
+    # a workspace that is large enough but not 256-byte aligned
+    odd = ctypes.c_void_p(256 + 16)
+    assert lib.delta_diff(one, one, 10, one, one, 5, one, odd, 1 << 40, None) == _abi.DELTA_E_WORKSPACE
+    assert "256-byte" in _err(lib)
+    assert lib.delta_diff_many(2, ptrs, ptrs, ok2, one, one, 10, one, one, odd, 1 << 40,
+                               None) == _abi.DELTA_E_WORKSPACE
+    assert "256-byte" in _err(lib)
+    assert lib.delta_apply_many(2, ptrs, ok2, one, one, one, 5, None, odd, 1 << 40,
+                                None) == _abi.DELTA_E_WORKSPACE
+    assert "256-byte" in _err(lib)
     assert lib.xor_mask(one, None, one, 5, None) == _abi.DELTA_E_INVALID
     assert lib.xor_mask(one, one, one, -5, None) == _abi.DELTA_E_INVALID
     assert lib.xor_apply(None, one, 5, None) == _abi.DELTA_E_INVALID

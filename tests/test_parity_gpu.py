@@ -122,6 +122,41 @@ def test_diff_tile_kinds(sbd, oracle_mod, pad):
     assert np.array_equal(np_bits(gv2), rv2)
 
 
+@pytest.mark.parametrize("seed", [41, 42])
+def test_diff_arena_mixed_tiles_repeated(sbd, oracle_mod, seed):
+    """Hundreds of tiles whose counts fall on both sides of every staging
+    limit, so many tiles share the staging arena in whatever order they
+    finish; two different inputs through one workspace in a row (the arena
+    counter starts afresh each call), as one tensor and as a list."""
+    from sparse_bf16_delta_amd.plan import DiffPlan
+
+    rng = np.random.default_rng(seed)
+    ntiles = 300
+    counts = rng.choice([0, 5, 600, 1024, 1025, 2000, 3500, 4096, 4097, 9000], size=ntiles)
+    cases = [tile_kinds_case(seed, counts=list(counts), last_valid=TILE),
+             tile_kinds_case(seed + 100, counts=list(rng.permutation(counts)), last_valid=TILE)]
+    n = ntiles * TILE
+    for old, new in cases:  # calls on one stream share the cached workspace
+        ri, rv = oracle_mod.diff(old, new)
+        gi, gv = sbd.diff(gpu_bits(old), gpu_bits(new))
+        assert np.array_equal(gi.cpu().numpy(), ri)
+        assert np.array_equal(np_bits(gv), rv)
+    # the list form: parameters of uneven sizes cut across tiles, one plan run twice
+    cuts = [0, 5 * TILE + 77, 40 * TILE, 41 * TILE + 3, 200 * TILE + 1000, n]
+    for old, new in cases:
+        olds = [gpu_bits(old[a:b]) for a, b in zip(cuts, cuts[1:])]
+        news = [gpu_bits(new[a:b]) for a, b in zip(cuts, cuts[1:])]
+        plan = DiffPlan(olds, news, capacity=n // 4)
+        for _ in range(2):
+            plan.run()
+            idx, val, nnz, offsets = plan.result()
+            ri2, rv2, rn2, ro2 = oracle_mod.diff_many([old[a:b] for a, b in zip(cuts, cuts[1:])],
+                                                      [new[a:b] for a, b in zip(cuts, cuts[1:])])
+            assert np.array_equal(offsets.cpu().numpy(), ro2)
+            assert np.array_equal(idx.cpu().numpy(), ri2)
+            assert np.array_equal(np_bits(val), rv2)
+
+
 @pytest.mark.parametrize("cut", [1024 + 1023 + 1, 1 + 1023 + 1024 + 1025 + 4095 + 7,
                                  sum(TILE_COUNTS[:8]) + 100, sum(TILE_COUNTS) - 1])
 def test_diff_tile_kinds_capacity(sbd, oracle_mod, cut):
