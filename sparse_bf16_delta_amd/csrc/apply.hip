@@ -10,19 +10,32 @@
 //  * Each workgroup owns 2048 consecutive entries; a lane loads 8 of them as
 //    two 16-byte idx loads and one 16-byte val load, so the delta is read
 //    once, coalesced.
-//  * Sparse entries (the usual case, about 1 % of a tensor) are scattered
-//    with 2-byte stores.  Indices within a parameter ascend, so stores to
-//    the same 128-byte line come close together and merge in L2; HBM then
-//    sees masked partial writes of the touched sectors and no reads of the
-//    snapshot.  (Reading and rewriting whole 64-byte segments instead moved
-//    three times the bytes and measured no faster at 1 % density.)
-//  * Dense entries: when a workgroup's entries lie in one parameter and span
-//    at most kMergeSpread elements per entry (about 4 % density or more,
-//    where nearly every line is touched and masked writes dominate), the
-//    workgroup instead reads the lines strictly inside that span into LDS,
-//    8192 elements at a time, patches them from its entries (held in
-//    registers) and writes them back whole.  The two edge lines, which a
-//    neighbouring workgroup may share, are still written entry by entry.
+//  * The memory system handles a 2-byte store to a line of HBM as a masked
+//    write of its 32-byte sector; a sector written whole, or better a 64-byte
+//    segment, costs it less.  So a workgroup whose entries are well formed
+//    (one parameter, all in range, strictly ascending) may rewrite the
+//    segments strictly inside its span whole.  A "segment" is an aligned
+//    64-byte unit of memory (32 bf16), whatever the snapshot's alignment.
+//    How depends on the entries per element of span:
+//      - sparse (more than kMergeSpread elements per entry, about 4 %
+//        density or less), and only when the whole delta has at least
+//        kSegMinTotal entries: the workgroup lists the segments its entries
+//        touch (a scan in LDS); four lanes read, patch and write back each
+//        listed segment, 16 bytes each, nontemporal.  A smaller delta keeps
+//        2-byte stores: its touched segments fit in or near the 256 MB
+//        memory-side cache, which absorbs masked stores (measured at
+//        2^28-2^30 elements and 0.3-1 % density: 1-3x faster than the
+//        rewrite); at the 79 million entries of a 7B-shaped step the rewrite
+//        is 8 % faster;
+//      - dense (kMergeMinSpread to kMergeSpread elements per entry, about
+//        4 % to 33 %): nearly every segment is touched, so the workgroup
+//        reads its whole span into LDS in 8192-element windows, patches it
+//        from its entries (held in registers) and writes it back;
+//      - denser still (runs that cover whole segments): 2-byte stores, which
+//        already merge into full lines in L2 without reading the snapshot.
+//    The first and the last touched segment, which a neighbouring workgroup
+//    may share, are always written with 2-byte stores, as is every entry of
+//    a workgroup that breaks the precondition or spans parameters.
 //  * Snapshot pointers come from the parameter table in memory; they are
 //    cast to the global address space so the stores are global, not flat.
 //  * The parameter of the workgroup's first entry comes from one 64-way
@@ -31,7 +44,9 @@
 //    apply.
 //  * An index outside [0, numel) is skipped, never written.  With unsorted
 //    or repeated indices the values at those entries' positions are
-//    unspecified; every other position keeps its value.
+//    unspecified; every other position keeps its value (a rewritten segment
+//    is written back with the values read from it, and lies inside the
+//    snapshot).
 #include "sbd_internal.h"
 
 namespace sbd {
@@ -40,17 +55,28 @@ namespace {
 constexpr int kApplyBlock = 256;
 constexpr int kApplyWaves = kApplyBlock / 64;
 constexpr int kApplyPer = 8;
-constexpr int64_t kApplyChunk = int64_t(kApplyBlock) * kApplyPer;
-// A workgroup merges whole lines when its in-range entries span between
-// kMergeMinSpread and kMergeSpread elements per entry (about 4 % to 33 %
-// density): then most lines are touched but few are covered whole.  Denser
-// entries cover whole lines, which the scatter's stores already merge into
-// full writes in L2 without reading the snapshot.
+constexpr int kApplyChunk = kApplyBlock * kApplyPer;  // 2048 entries per workgroup
+// Elements of span per entry that choose between the ways of writing a
+// well-formed workgroup's interior segments (see above).
 constexpr int64_t kMergeSpread = 24;
 constexpr int64_t kMergeMinSpread = 3;
-constexpr int kLineElems = 64;       // bf16 per 128-byte line
-constexpr int kMergeWindow = 8192;   // snapshot elements patched in LDS at a time
-static_assert(kMergeWindow % kLineElems == 0, "windows hold whole lines");
+constexpr int kSegElems = 32;                        // bf16 per 64-byte segment
+constexpr int kSegLanes = kSegElems / kVec;          // 4 lanes x 16 bytes per segment
+constexpr int kSegGroups = kApplyBlock / kSegLanes;  // segments per workgroup pass
+constexpr int kSegUnroll = 4;                        // segments in flight per lane
+// Fewest delta entries for which sparse workgroups rewrite whole segments.
+constexpr int64_t kSegMinTotal = int64_t(1) << 25;
+constexpr int kMergeWindow = 8192;  // snapshot elements patched in LDS at a time
+static_assert(kMergeWindow % kSegElems == 0, "windows hold whole segments");
+
+enum ApplyMode : int { kScatter = 0, kWindows = 1, kSegments = 2 };
+
+// The touched-segment list of a sparse workgroup (16 KB, the window's size).
+struct SegList {
+  uint32_t pos[kApplyChunk];    // per entry: its index plus the segment shift
+  uint16_t val[kApplyChunk];    // per entry: its value
+  uint16_t first[kApplyChunk];  // the first entry of each listed segment
+};
 
 struct ApplyShared {
   int64_t total;
@@ -61,16 +87,34 @@ struct ApplyShared {
   uint32_t wcnt[kApplyWaves];
   int32_t wfirst[kApplyWaves];  // first and last entry of each wave, for the order check
   int32_t wlast[kApplyWaves];
-  __attribute__((aligned(16))) uint16_t win[kMergeWindow];  // snapshot window being patched
+  uint32_t wsegs[kApplyWaves];  // listed segments per wave
+  uint32_t last_first;          // the first entry in the last touched segment
+  union {
+    __attribute__((aligned(16))) uint16_t win[kMergeWindow];  // snapshot window being patched
+    __attribute__((aligned(16))) SegList sl;
+  };
 };
 
 __global__ __launch_bounds__(64) void zero_i64_kernel(int64_t* p) {
   if (threadIdx.x == 0) *p = 0;
 }
 
+// Element `k` (0..7) of a 16-byte vector of bf16 set to `v`.
+__device__ __forceinline__ void set_elem(u32x4& x, uint32_t k, uint32_t v) {
+  const uint32_t s = (k & 1u) * 16u;
+  const uint32_t keep = ~(0xFFFFu << s), put = v << s;
+  const uint32_t q = k >> 1;
+  x.x = q == 0u ? (x.x & keep) | put : x.x;
+  x.y = q == 1u ? (x.y & keep) | put : x.y;
+  x.z = q == 2u ? (x.z & keep) | put : x.z;
+  x.w = q == 3u ? (x.w & keep) | put : x.w;
+}
+
 // Applies entries [j0, j0 + kApplyChunk) of the delta.  Every lane of the
 // workgroup reaches the end (the violation count is a wave reduction).
-template <bool kMany>
+// kSegOK: the segment rewrite is compiled in (the launch's capacity allows a
+// delta of kSegMinTotal entries); without it the kernel needs fewer registers.
+template <bool kMany, bool kSegOK>
 __device__ __forceinline__ void apply_chunk(
     int64_t j0, const SnapParam* __restrict__ table, const SnapParam& single, int32_t nparams,
     const int64_t* __restrict__ offsets, const int32_t* __restrict__ idx,
@@ -98,9 +142,12 @@ __device__ __forceinline__ void apply_chunk(
   __syncthreads();
   const int64_t total = sh.total;
   if (j0 >= total) return;  // uniform over the workgroup
-  const int64_t n_entries = total - j0 < kApplyChunk ? total - j0 : kApplyChunk;
+  const int n_entries = total - j0 < kApplyChunk ? int(total - j0) : kApplyChunk;
 
-  const int64_t jt = j0 + int64_t(threadIdx.x) * kApplyPer;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int e0 = int(threadIdx.x) * kApplyPer;  // the lane's first entry in the chunk
+  const int64_t jt = j0 + e0;
   int64_t bad = 0;
   int32_t iv[kApplyPer];
   uint16_t vv[kApplyPer];
@@ -134,25 +181,24 @@ __device__ __forceinline__ void apply_chunk(
     }
   }
 
-  // ---- merge or scatter (uniform over the workgroup) ------------------------
-  // Merge when the chunk lies in one 16-byte-aligned snapshot, all its
-  // entries are in range and strictly ascending, and they are dense; then the
-  // lines strictly between the first and the last touched line,
-  // [lo_end, hi_start), are rewritten whole.  A chunk that breaks the
-  // precondition always takes the entry-by-entry path.
-  bool merge = false;
-  uint32_t lo_end = 0, hi_start = 0;
+  // ---- choose how to write (uniform over the workgroup) --------------------
+  // Segments are numbered from the 64-byte segment holding the snapshot's
+  // element 0, which sits `shift` elements into it: element i is in segment
+  // (i + shift) / 32.  For a well-formed chunk the segments strictly between
+  // the first and the last touched one hold the elements [lo_end, hi_start).
+  int mode = kScatter;
+  uint32_t shift = 0, ufirst = 0, ulast = 0, lo_end = 0, hi_start = 0;
   SnapParam dm = single;
   if (sh.one_param) {
     if constexpr (kMany) dm = table[sh.p0];
-    if ((reinterpret_cast<uintptr_t>(dm.snap) & 15u) == 0) {
+    shift = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dm.snap) & 63u) >> 1;
+    if ((reinterpret_cast<uintptr_t>(dm.snap) & 1u) == 0) {
       uint32_t umin = 0xFFFFFFFFu, umax = 0u, cnt = 0u;
       bool sorted = true, any = false;
       int32_t first = 0, last = 0;
 #pragma unroll
       for (int r = 0; r < kApplyPer; ++r) {
-        const int64_t e = int64_t(threadIdx.x) * kApplyPer + r;
-        if (e < n_entries) {
+        if (e0 + r < n_entries) {
           const uint32_t i = static_cast<uint32_t>(iv[r]);
           if (static_cast<uint64_t>(i) < static_cast<uint64_t>(dm.numel)) {
             umin = i < umin ? i : umin;
@@ -166,7 +212,6 @@ __device__ __forceinline__ void apply_chunk(
         }
       }
       // ascending across neighbouring lanes of the wave
-      const int lane = threadIdx.x & 63;
       const int32_t prev_last = __shfl_up(last, 1, 64);
       const int prev_any = __shfl_up(any ? 1 : 0, 1, 64);
       if (lane > 0 && prev_any && any && !(first > prev_last)) sorted = false;
@@ -179,7 +224,6 @@ __device__ __forceinline__ void apply_chunk(
         umax = b > umax ? b : umax;
         cnt += static_cast<uint32_t>(__shfl_xor(static_cast<int>(cnt), o, 64));
       }
-      const int wave = threadIdx.x >> 6;
       if (lane == 0) {
         sh.wmin[wave] = umin;
         sh.wmax[wave] = umax;
@@ -198,22 +242,29 @@ __device__ __forceinline__ void apply_chunk(
         if (sh.wcnt[w] == 0xFFFFFFFFu) well_formed = false;
         gcnt += sh.wcnt[w];
         // ascending across the boundary between waves w - 1 and w
-        const int64_t e = int64_t(w) * 64 * kApplyPer;
-        if (w > 0 && e < n_entries && !(sh.wfirst[w] > sh.wlast[w - 1])) well_formed = false;
+        if (w > 0 && w * 64 * kApplyPer < n_entries && !(sh.wfirst[w] > sh.wlast[w - 1]))
+          well_formed = false;
       }
       well_formed = well_formed && gcnt == static_cast<uint32_t>(n_entries);  // all in range
       if (well_formed && gcnt > 0u) {
-        const uint32_t first_line = gmin / kLineElems, last_line = gmax / kLineElems;
+        // indices are below 2^31, so these stay within 32 bits
+        ufirst = (gmin + shift) / kSegElems;
+        ulast = (gmax + shift) / kSegElems;
         const int64_t span = int64_t(gmax - gmin) + 1;
-        merge = last_line >= first_line + 2u && span <= kMergeSpread * int64_t(gcnt) &&
-                span >= kMergeMinSpread * int64_t(gcnt);
-        lo_end = (first_line + 1u) * kLineElems;
-        hi_start = last_line * kLineElems;
+        if (ulast >= ufirst + 2u) {
+          if (span > kMergeSpread * int64_t(gcnt)) {
+            if (kSegOK && total >= kSegMinTotal) mode = kSegments;
+          } else if (span >= kMergeMinSpread * int64_t(gcnt)) {
+            mode = kWindows;
+          }
+        }
+        lo_end = (ufirst + 1u) * kSegElems - shift;
+        hi_start = ulast * kSegElems - shift;
       }
     }
   }
 
-  // ---- entry by entry: every entry, or only the edge lines' when merging ---
+  // ---- entry by entry: every entry, or only the edge segments' ------------
   if (jt < total) {
     int32_t p = 0;
     SnapParam d = single;
@@ -252,8 +303,8 @@ __device__ __forceinline__ void apply_chunk(
         }
         const uint32_t i = static_cast<uint32_t>(iv[r]);
         const bool in_range = static_cast<uint64_t>(i) < static_cast<uint64_t>(d.numel);
-        const bool merged = merge && i >= lo_end && i < hi_start;
-        if (in_range && !merged) *global_ptr(d.snap + i) = vv[r];
+        const bool interior = mode != kScatter && i >= lo_end && i < hi_start;
+        if (in_range && !interior) *global_ptr(d.snap + i) = vv[r];
         if (violations != nullptr) {
           bad += (!in_range || (have_prev && iv[r] <= prev)) ? 1 : 0;
           prev = iv[r];
@@ -263,9 +314,107 @@ __device__ __forceinline__ void apply_chunk(
     }
   }
 
-  // ---- line merge: window by window, read whole lines into LDS, patch them
+  // ---- sparse: list the touched interior segments, then rewrite each -----
+  if constexpr (kSegOK) {
+    if (mode == kSegments) {
+      // The 64-byte-aligned address of segment 0.
+      const uintptr_t seg0 = reinterpret_cast<uintptr_t>(dm.snap) - 2u * shift;
+      // The entry before the lane's first one: the previous lane's last, or
+      // for a wave's lane 0 the previous wave's last (entry 0 needs none).
+      int32_t before = __shfl_up(iv[kApplyPer - 1], 1, 64);
+      if (lane == 0) before = wave > 0 ? sh.wlast[wave - 1] : 0;
+      uint32_t pu = (static_cast<uint32_t>(before) + shift) / kSegElems;
+      uint32_t leads = 0u, nlead = 0u;
+#pragma unroll
+      for (int r = 0; r < kApplyPer; ++r) {
+        const int e = e0 + r;
+        const uint32_t u = (static_cast<uint32_t>(iv[r]) + shift) / kSegElems;
+        const bool lead = e < n_entries && (e == 0 || u != pu);
+        pu = u;
+        if (lead && u > ufirst && u < ulast) {
+          leads |= 1u << r;
+          ++nlead;
+        }
+        if (lead && u == ulast) sh.last_first = uint32_t(e);
+      }
+      // the lane's entries, as 16-byte LDS stores
+#pragma unroll
+      for (int h = 0; h < kApplyPer; h += 4) {
+        u32x4 w;
+        w.x = static_cast<uint32_t>(iv[h + 0]) + shift;
+        w.y = static_cast<uint32_t>(iv[h + 1]) + shift;
+        w.z = static_cast<uint32_t>(iv[h + 2]) + shift;
+        w.w = static_cast<uint32_t>(iv[h + 3]) + shift;
+        *reinterpret_cast<u32x4*>(&sh.sl.pos[e0 + h]) = w;
+      }
+      {
+        u32x4 w;
+        w.x = uint32_t(vv[0]) | (uint32_t(vv[1]) << 16);
+        w.y = uint32_t(vv[2]) | (uint32_t(vv[3]) << 16);
+        w.z = uint32_t(vv[4]) | (uint32_t(vv[5]) << 16);
+        w.w = uint32_t(vv[6]) | (uint32_t(vv[7]) << 16);
+        *reinterpret_cast<u32x4*>(&sh.sl.val[e0]) = w;
+      }
+      // slots in the list: a workgroup scan of the lanes' leader counts
+      uint32_t incl = nlead;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = static_cast<uint32_t>(__shfl_up(static_cast<int>(incl), o, 64));
+        if (lane >= o) incl += t;
+      }
+      if (lane == 63) sh.wsegs[wave] = incl;
+      __syncthreads();
+      uint32_t slot = incl - nlead, ns = 0u;
+#pragma unroll
+      for (int w = 0; w < kApplyWaves; ++w) {
+        slot += w < wave ? sh.wsegs[w] : 0u;
+        ns += sh.wsegs[w];
+      }
+#pragma unroll
+      for (int r = 0; r < kApplyPer; ++r) {
+        if ((leads >> r) & 1u) {
+          sh.sl.first[slot] = static_cast<uint16_t>(e0 + r);
+          ++slot;
+        }
+      }
+      __syncthreads();
+      // four lanes per listed segment: read it, patch it, write it back
+      const uint32_t g = threadIdx.x / kSegLanes;
+      const uint32_t sub = threadIdx.x % kSegLanes;
+      const uint32_t last_first = sh.last_first;
+      for (uint32_t s0 = 0; s0 < ns; s0 += kSegGroups * kSegUnroll) {
+        u32x4 x[kSegUnroll];
+#pragma unroll
+        for (int k = 0; k < kSegUnroll; ++k) {
+          const uint32_t s = s0 + k * kSegGroups + g;
+          if (s < ns) {
+            const uint32_t u = sh.sl.pos[sh.sl.first[s]] / kSegElems;
+            const uintptr_t a = seg0 + uintptr_t(u) * 64u + sub * 16u;
+            x[k] = __builtin_nontemporal_load(global_ptr(reinterpret_cast<const u32x4*>(a)));
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < kSegUnroll; ++k) {
+          const uint32_t s = s0 + k * kSegGroups + g;
+          if (s < ns) {
+            const uint32_t eb = sh.sl.first[s];
+            const uint32_t ee = s + 1u < ns ? uint32_t(sh.sl.first[s + 1u]) : last_first;
+            for (uint32_t e = eb; e < ee; ++e) {
+              const uint32_t off = sh.sl.pos[e] % kSegElems;
+              if (off / kVec == sub) set_elem(x[k], off % kVec, sh.sl.val[e]);
+            }
+            const uint32_t u = sh.sl.pos[eb] / kSegElems;
+            const uintptr_t a = seg0 + uintptr_t(u) * 64u + sub * 16u;
+            __builtin_nontemporal_store(x[k], global_ptr(reinterpret_cast<u32x4*>(a)));
+          }
+        }
+      }
+    }
+  }
+
+  // ---- dense: window by window, read whole segments into LDS, patch them
   // from the lanes' entries, write them back whole ---------------------------
-  if (merge) {
+  if (mode == kWindows) {
     for (uint32_t w0 = lo_end; w0 < hi_start; w0 += kMergeWindow) {
       const uint32_t w1 = hi_start - w0 < uint32_t(kMergeWindow) ? hi_start : w0 + kMergeWindow;
       for (uint32_t c = threadIdx.x; c < (w1 - w0) / kVec; c += kApplyBlock) {
@@ -276,8 +425,7 @@ __device__ __forceinline__ void apply_chunk(
 #pragma unroll
       for (int r = 0; r < kApplyPer; ++r) {
         const uint32_t i = static_cast<uint32_t>(iv[r]);
-        if (int64_t(threadIdx.x) * kApplyPer + r < n_entries && i >= w0 && i < w1)
-          sh.win[i - w0] = vv[r];
+        if (e0 + r < n_entries && i >= w0 && i < w1) sh.win[i - w0] = vv[r];
       }
       __syncthreads();
       for (uint32_t c = threadIdx.x; c < (w1 - w0) / kVec; c += kApplyBlock) {
@@ -290,13 +438,13 @@ __device__ __forceinline__ void apply_chunk(
   if (violations != nullptr) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) bad += __shfl_xor(bad, o, 64);
-    if ((threadIdx.x & 63) == 0 && bad != 0)
+    if (lane == 0 && bad != 0)
       atomicAdd(reinterpret_cast<unsigned long long*>(violations),
                 static_cast<unsigned long long>(bad));
   }
 }
 
-template <bool kMany>
+template <bool kMany, bool kSegOK>
 __global__ __launch_bounds__(kApplyBlock) void apply_kernel(
     const SnapParam* __restrict__ table, SnapParam single, int32_t nparams,
     const int64_t* __restrict__ offsets, const int32_t* __restrict__ idx,
@@ -304,10 +452,19 @@ __global__ __launch_bounds__(kApplyBlock) void apply_kernel(
   __shared__ ApplyShared sh;
   const int64_t nchunks = (max_nnz + kApplyChunk - 1) / kApplyChunk;
   for (int64_t chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {
-    apply_chunk<kMany>(chunk * kApplyChunk, table, single, nparams, offsets, idx, val, max_nnz,
-                       violations, sh);
+    apply_chunk<kMany, kSegOK>(chunk * kApplyChunk, table, single, nparams, offsets, idx, val,
+                               max_nnz, violations, sh);
     __syncthreads();  // the shared state is rewritten by the next chunk
   }
+}
+
+template <bool kMany, bool kSegOK>
+void launch_apply_kernel(unsigned blocks, const SnapParam* d_table, const SnapParam& single,
+                         int32_t nparams, const int64_t* offsets, const int32_t* idx,
+                         const uint16_t* val, int64_t max_nnz, int64_t* violations,
+                         hipStream_t stream) {
+  apply_kernel<kMany, kSegOK><<<dim3(blocks), dim3(kApplyBlock), 0, stream>>>(
+      d_table, single, nparams, offsets, idx, val, max_nnz, violations);
 }
 
 }  // namespace
@@ -319,12 +476,25 @@ hipError_t launch_apply(const SnapParam* d_table, const SnapParam& single, int32
   if (max_nnz > 0) {
     int64_t blocks = (max_nnz + kApplyChunk - 1) / kApplyChunk;
     if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
-    if (d_table != nullptr)
-      apply_kernel<true><<<dim3(unsigned(blocks)), dim3(kApplyBlock), 0, stream>>>(
-          d_table, single, nparams, offsets, idx, val, max_nnz, violations);
-    else
-      apply_kernel<false><<<dim3(unsigned(blocks)), dim3(kApplyBlock), 0, stream>>>(
-          nullptr, single, 1, nullptr, idx, val, max_nnz, violations);
+    const unsigned b = unsigned(blocks);
+    // the segment rewrite needs a delta of kSegMinTotal entries, which only a
+    // capacity that large can hold
+    const bool seg = max_nnz >= kSegMinTotal;
+    if (d_table != nullptr) {
+      if (seg)
+        launch_apply_kernel<true, true>(b, d_table, single, nparams, offsets, idx, val, max_nnz,
+                                        violations, stream);
+      else
+        launch_apply_kernel<true, false>(b, d_table, single, nparams, offsets, idx, val, max_nnz,
+                                         violations, stream);
+    } else {
+      if (seg)
+        launch_apply_kernel<false, true>(b, nullptr, single, 1, nullptr, idx, val, max_nnz,
+                                         violations, stream);
+      else
+        launch_apply_kernel<false, false>(b, nullptr, single, 1, nullptr, idx, val, max_nnz,
+                                          violations, stream);
+    }
   }
   return hipGetLastError();
 }

@@ -403,9 +403,9 @@ def test_apply_unsorted_is_flagged_and_stays_inside(sbd):
 @pytest.mark.parametrize("frac", [0.02, 0.05, 0.1, 0.3])
 @pytest.mark.parametrize("pad", [0, 1, 8])
 def test_apply_dense_runs_and_boundaries(sbd, oracle_mod, frac, pad):
-    """Densities around the line-merge threshold, on a snapshot that is 16-byte
-    aligned (merge allowed), 2-byte aligned (scatter only) or offset by 16
-    bytes (lines not on 128-byte boundaries); chunk edges share lines."""
+    """Densities around the merge threshold, on a snapshot that is aligned or
+    offset by 1 or 8 elements (64-byte segments then start inside the
+    snapshot's first one); chunk edges share segments."""
     n = 9 * 2048 * 40 + 77
     old, new = rand_case(int(frac * 100) + pad, n, frac, special=False)
     ri, rv = oracle_mod.diff(old, new)
@@ -413,6 +413,104 @@ def test_apply_dense_runs_and_boundaries(sbd, oracle_mod, frac, pad):
     sbd.apply_(snap, torch.from_numpy(ri).cuda(),
                torch.from_numpy(rv.view(np.int16)).cuda().view(torch.bfloat16))
     assert np.array_equal(np_bits(snap), new)
+
+
+# The segment rewrite of sparse workgroups runs only for deltas of at least
+# 2^25 entries (below that, masked stores are cheaper): these cases are that
+# large, so they check properties that hold at any size -- the result equals
+# `new` -- with the delta taken by torch's own comparison, not by diff.
+SEG_N = (1 << 30) + 12345
+
+
+def _torch_delta(old_bits, new_bits):
+    idx = torch.nonzero(old_bits != new_bits).reshape(-1).to(torch.int32)
+    return idx, new_bits[idx.long()].view(torch.bfloat16)
+
+
+def _sparse_pair(n, seed, percent=3.5):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    old = torch.randint(-(1 << 15), 1 << 15, (n,), dtype=torch.int16, device="cuda", generator=g)
+    pick = torch.randint(0, 1000, (n,), dtype=torch.int16, device="cuda", generator=g)
+    new = torch.where(pick < int(percent * 10), old ^ 0x1, old)
+    del pick
+    return old, new
+
+
+@pytest.mark.parametrize("pad", [0, 3])
+def test_apply_segment_rewrite_large(sbd, pad):
+    """About 37.6 million entries at 3.5 % (span per entry above the merge
+    threshold): sparse workgroups rewrite whole 64-byte segments; the
+    snapshot starts `pad` elements into its allocation, with guard elements
+    after it."""
+    n = SEG_N
+    old, new = _sparse_pair(n, 7 + pad)
+    idx, val = _torch_delta(old, new)
+    assert idx.numel() >= (1 << 25)
+    buf = torch.full((pad + n + 64,), 7, dtype=torch.int16, device="cuda")
+    buf[pad:pad + n] = old
+    snap = buf[pad:pad + n].view(torch.bfloat16)
+    sbd.apply_(snap, idx, val, check_indices=True)
+    assert torch.equal(buf[pad:pad + n], new)
+    assert bool((buf[:pad] == 7).all()) and bool((buf[pad + n:] == 7).all())
+    sbd.apply_(snap, *_torch_delta(new, old))  # and back
+    assert torch.equal(buf[pad:pad + n], old)
+
+
+def test_apply_many_segment_rewrite_unaligned_params(sbd):
+    """A list packed back to back at odd element offsets (each parameter's
+    segments start at a different shift, edge segments shared with the
+    neighbours), more than 2^25 entries in all."""
+    sizes = [(1 << 29) + 7, 5, (1 << 28) + 3, 1000, (1 << 29) - 11]
+    total = sum(sizes)
+    old, new = _sparse_pair(total, 21)
+    buf = torch.full((1 + total + 64,), 7, dtype=torch.int16, device="cuda")
+    buf[1:1 + total] = old
+    views, idxs, vals, counts, pos = [], [], [], [], 0
+    for n in sizes:
+        views.append(buf[1 + pos:1 + pos + n].view(torch.bfloat16))
+        i, v = _torch_delta(old[pos:pos + n], new[pos:pos + n])
+        idxs.append(i)
+        vals.append(v)
+        counts.append(i.numel())
+        pos += n
+    offsets = torch.tensor([0] + list(np.cumsum(counts)), dtype=torch.int64, device="cuda")
+    assert int(offsets[-1]) >= (1 << 25)
+    sbd.apply_many_(views, torch.cat(idxs), torch.cat(vals), offsets, check_indices=True)
+    assert torch.equal(buf[1:1 + total], new)
+    assert int(buf[0]) == 7 and bool((buf[1 + total:] == 7).all())
+
+
+def test_apply_segment_rewrite_with_broken_precondition(sbd):
+    """A large delta with an unsorted pair, a repeated index and an
+    out-of-range entry in three workgroups' chunks: they are counted, those
+    chunks are written entry by entry, every other position ends as in
+    `new` (or keeps its old value where its entry was replaced), and nothing
+    outside the snapshot changes."""
+    n = SEG_N
+    old, new = _sparse_pair(n, 33)
+    idx, val = _torch_delta(old, new)
+    k0, k1, k2 = 5_000_000, 12_000_000, 30_000_000
+    orig1, orig2 = int(idx[k1]), int(idx[k2])
+    idx2, val2 = idx.clone(), val.view(torch.int16).clone()
+    idx2[[k0, k0 + 1]] = idx2[[k0 + 1, k0]]
+    val2[[k0, k0 + 1]] = val2[[k0 + 1, k0]]
+    idx2[k1] = idx2[k1 - 1]
+    idx2[k2] = n + 5
+    buf = torch.full((n + 64,), 7, dtype=torch.int16, device="cuda")
+    buf[:n] = old
+    with pytest.raises(sbd.DeltaError, match="delta entries"):
+        sbd.apply_(buf[:n].view(torch.bfloat16), idx2, val2.view(torch.bfloat16),
+                   check_indices=True)
+    want = new.clone()
+    want[orig1] = old[orig1]   # its entry now names another position
+    want[orig2] = old[orig2]   # its entry is out of range
+    dup = int(idx2[k1])
+    got_dup = int(buf[dup])
+    assert got_dup in (int(val2[k1 - 1]), int(val2[k1]))
+    want[dup] = got_dup
+    assert torch.equal(buf[:n], want)
+    assert bool((buf[n:] == 7).all())
 
 
 def test_apply_merge_with_broken_precondition_stays_inside(sbd):
