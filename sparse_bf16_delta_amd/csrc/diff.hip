@@ -299,9 +299,10 @@ __global__ __launch_bounds__(kDiffBlock) void diff_count_kernel(
       }
     }
     __syncthreads();
-    // 16-byte copies with the nontemporal hint (the slot is read once, by the
-    // placing kernel); the last one may carry up to three stale LDS words
-    // past `agg`, which stay inside the slot and are never read.
+    // 16-byte copies with the nontemporal hint (the entries are read once, by
+    // the placing kernel); the last one may carry up to three stale LDS words
+    // past `agg`, which stay inside the slot or the tile's arena quads and are
+    // never read.
     uint32_t* slot = agg <= static_cast<uint32_t>(kCompactCap) ? compact + tile * kCompactWords
                                                                : wide + s_pos * 4u;
     for (uint32_t p = static_cast<uint32_t>(tid) * 4u; p < agg; p += kDiffBlock * 4u) {
@@ -408,10 +409,11 @@ __global__ __launch_bounds__(kScanBlock) void diff_base_kernel(
   }
 }
 
-// Phase 3a: copy the staged entries of `tiles_per_wg` consecutive tiles to
-// their final positions.  Consecutive tiles have consecutive outputs, so the
-// staged tiles' entries are walked as one flat run (dense tiles, written by
-// diff_dense_kernel, and empty ones are left out of it).
+// Phase 3a: copy the staged entries of `tiles_per_wg` consecutive tiles, from
+// each tile's slot or arena position, to their final positions.  Consecutive
+// tiles have consecutive outputs, so the staged tiles' entries are walked as
+// one flat run (dense tiles, written by diff_dense_kernel, and empty ones are
+// left out of it).
 template <bool kMany, typename IdxT>
 __global__ __launch_bounds__(kDiffBlock) void diff_place_kernel(
     const TileDesc* __restrict__ tdesc, int64_t total_tiles, int32_t nchunks, int32_t tiles_per_wg,

@@ -53,10 +53,11 @@ def test_workspace_size():
     b = lib.delta_workspace_size(1 << 30, 1)
     c = lib.delta_workspace_size(1 << 30, 300)
     assert 0 < a < b < c
-    # per 32768-element tile: two staging slots (4 KB + 16 KB), count, prefix,
-    # dense-list entry and a 32-byte descriptor; each extra parameter may add
-    # a partial tile and a 32-byte table entry
-    per_tile = 4096 + 16384 + 4 + 4 + 4 + 32
+    # per 32768-element tile: a 4 KB staging slot and 16 KB of staging arena,
+    # count, prefix, dense-list entry, a 32-byte descriptor and an 8-byte arena
+    # position; each extra parameter may add a partial tile and a 32-byte
+    # table entry
+    per_tile = 4096 + 16384 + 4 + 4 + 4 + 32 + 8
     tiles = (1 << 30) // 32768
     assert b >= per_tile * tiles
     # no more than the layout needs: the slots start past a 1 MB boundary

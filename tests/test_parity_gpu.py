@@ -101,7 +101,7 @@ def tile_kinds_case(seed, counts=TILE_COUNTS, last_valid=5000):
 
 @pytest.mark.parametrize("pad", [0, 3])
 def test_diff_tile_kinds(sbd, oracle_mod, pad):
-    """Every staging path -- compact slot, wide slot, dense re-read -- and their
+    """Every staging path -- compact slot, shared arena, dense re-read -- and their
     limits, aligned and unaligned, as one tensor and as a parameter list."""
     old, new = tile_kinds_case(11 + pad)
     ri, rv = oracle_mod.diff(old, new)
