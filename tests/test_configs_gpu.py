@@ -197,3 +197,43 @@ def test_llama405b_share_xor_path(sbd, llama405b_share):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16))
             sbd.xor_apply_(a, mask)
             del mask
+
+
+def test_largest_tensor_int32_index_range(sbd, oracle_mod):
+    """One tensor of 2^31 - 1 elements, the most the int32 index contract
+    allows, about 2 % changed (the last and first elements among them): the
+    count equals torch's count of differing bit patterns, the indices ascend
+    strictly and the values are new's, apply (sparse workgroups rewriting
+    whole segments) turns old into new, XOR round-trips, and the oracle
+    agrees exactly on the first and last million elements."""
+    n = (1 << 31) - 1
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    old = torch.randint(-(1 << 15), 1 << 15, (n,), dtype=torch.int16, device="cuda", generator=g)
+    pick = torch.randint(0, 1000, (n,), dtype=torch.int16, device="cuda", generator=g) < 20
+    pick[0] = True
+    pick[n - 1] = True
+    new = torch.where(pick, old ^ 0x1, old)
+    want_count = int(pick.sum().item())
+    del pick
+    idx, val = sbd.diff(old.view(torch.bfloat16), new.view(torch.bfloat16))
+    assert idx.numel() == want_count
+    assert int(idx[0]) == 0 and int(idx[-1]) == n - 1
+    assert bool((idx[1:] > idx[:-1]).all())
+    assert torch.equal(val.view(torch.int16), new[idx.long()])
+    w = 1 << 20
+    for a in (0, n - w):
+        lo = int(torch.searchsorted(idx, torch.tensor([a], dtype=torch.int32, device="cuda")))
+        hi = int(torch.searchsorted(idx, torch.tensor([a + w], dtype=torch.int32, device="cuda")))
+        ri, rv = oracle_mod.diff(bits(old[a:a + w]), bits(new[a:a + w]))
+        assert np.array_equal(idx[lo:hi].cpu().numpy() - a, ri)
+        assert np.array_equal(bits(val[lo:hi]), rv)
+    snap = old.clone()
+    assert idx.numel() >= (1 << 25)  # large enough for the segment rewrite
+    sbd.apply_(snap.view(torch.bfloat16), idx, val, check_indices=True)
+    assert torch.equal(snap, new)
+    del idx, val
+    mask = sbd.xor_mask(old.view(torch.bfloat16), new.view(torch.bfloat16))
+    assert int((mask.view(torch.int16) != 0).sum().item()) == want_count
+    sbd.xor_apply_(snap.view(torch.bfloat16), mask)
+    assert torch.equal(snap, old)
