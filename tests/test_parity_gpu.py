@@ -592,6 +592,36 @@ def test_apply_many_adjacent_unaligned_params(sbd, oracle_mod, frac):
     assert np.array_equal(np_bits(buf), np.concatenate(want))
 
 
+@pytest.mark.parametrize("frac", [0.01, 0.3])
+def test_many_thousands_of_parameters(sbd, oracle_mod, frac):
+    """20,000 parameters, mostly tiny or empty with a few spanning several
+    tiles, back to back in one buffer: past the 4096 that one step of the
+    parameter search covers.  diff_many and apply_many against the oracle."""
+    rng = np.random.default_rng(int(frac * 1000) + 5)
+    k = 20_000
+    kind = rng.random(k)
+    sizes = np.where(kind < 0.05, 0,
+                     np.where(kind < 0.80, rng.integers(1, 300, k),
+                              np.where(kind < 0.995, rng.integers(300, 5000, k),
+                                       rng.integers(TILE, 3 * TILE, k)))).astype(np.int64)
+    total = int(sizes.sum())
+    old, new = rand_case(int(frac * 100) + 9, total, frac)
+    bounds = np.concatenate([[0], np.cumsum(sizes)])
+    olds = [old[a:b] for a, b in zip(bounds[:-1], bounds[1:])]
+    news = [new[a:b] for a, b in zip(bounds[:-1], bounds[1:])]
+    ri, rv, rn, ro = oracle_mod.diff_many(olds, news)
+    g_old, g_new = gpu_bits(old, 1), gpu_bits(new, 1)
+    vo = [g_old[a:b] for a, b in zip(bounds[:-1], bounds[1:])]
+    vn = [g_new[a:b] for a, b in zip(bounds[:-1], bounds[1:])]
+    gi, gv, gn, go = sbd.diff_many(vo, vn)
+    assert np.array_equal(gn.cpu().numpy(), rn)
+    assert np.array_equal(go.cpu().numpy(), ro)
+    assert np.array_equal(gi.cpu().numpy(), ri)
+    assert np.array_equal(np_bits(gv), rv)
+    sbd.apply_many_(vo, gi, gv, go, check_indices=True)
+    assert np.array_equal(np_bits(g_old), new)
+
+
 def test_diff_many_then_apply_many_without_host_sync(sbd):
     """The receiver can follow the sender on one stream: apply_many reads the
     device offsets written by diff_many; the result equals `new` bitwise."""
