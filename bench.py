@@ -95,6 +95,8 @@ def parse():
     ap.add_argument("--receiver", action="store_true",
                     help="time the receiver with the delta and the XOR mask in pinned host "
                          "memory: copy only, copy then apply, and the streamed pipeline")
+    ap.add_argument("--chunks", type=int, default=8,
+                    help="--receiver: parameter chunks of the streamed sparse receiver")
     ap.add_argument("--shards", type=int, default=0,
                     help="W > 0: time delta_diff_many_sharded for each rank of a W-way Shard(0) "
                          "split of the list, one rank after another (table on stderr)")
@@ -419,8 +421,10 @@ def receiver_run(args, props):
     """The receiver's side with its input in pinned host memory, as the
     network leaves it: the sparse delta (idx, val, offsets) and the XOR mask.
     Times, per mode: the host-to-device copy alone, copy then apply on one
-    stream, and the streamed pipeline (chunks of parameters or elements,
-    copies overlapping applies).  Every variant's result is checked."""
+    stream, the streamed pipeline (chunks of parameters or elements, copies
+    overlapping applies), and for the delta the host-direct apply (the
+    kernel reads the pinned delta itself).  Every variant's result is
+    checked."""
     import torch
 
     import sparse_bf16_delta_amd as sbd
@@ -457,7 +461,7 @@ def receiver_run(args, props):
     log(f"[bench] receiver, {cfg.key}: {nnz:,} changed; delta {6 * nnz / 1e9:.3f} GB and mask "
         f"{2 * n_alloc / 1e9:.2f} GB pinned on the host in {time.perf_counter() - t0:.1f} s")
     k = len(numels)
-    nchunks = 8
+    nchunks = max(1, min(args.chunks, k))
     bounds = sorted(set([round(i * k / nchunks) for i in range(nchunks + 1)]))
     d_idx = torch.empty_like(dplan.idx[:nnz])
     d_val = torch.empty_like(dplan.val[:nnz])
@@ -500,6 +504,9 @@ def receiver_run(args, props):
     def streamed_sparse():
         splan.run(h_idx, h_val, h_off)
 
+    def host_direct_sparse():
+        sbd.apply_many_host_(snaps, h_idx, h_val, h_off)
+
     def copy_mask():
         d_mask.copy_(h_mask, non_blocking=True)
 
@@ -516,6 +523,7 @@ def receiver_run(args, props):
     for name, fn, check in (("sparse copy", copy_delta, None),
                             ("sparse copy+apply", serial_sparse, new),
                             ("sparse streamed", streamed_sparse, new),
+                            ("sparse host-direct", host_direct_sparse, new),
                             ("xor copy", copy_mask, None),
                             ("xor copy+apply", serial_xor, new),
                             ("xor streamed", streamed_xor, new)):

@@ -284,6 +284,34 @@ delta_status delta_apply_streamed(int32_t nparams, uint16_t *const *snap_ptrs,
                                   size_t staging_bytes, void *copy_stream, void *apply_stream);
 
 /*
+ * delta_apply_many_host -- delta_apply_many with the delta in pinned host
+ * memory, read by the apply kernel itself over the host link: no staging
+ * buffer and no copy engine, so the transfer and the apply proceed together.
+ * [TRL] section 4.3: the receiver applies the downloaded delta into its
+ * resident snapshot; here the delta never needs a device copy of its own.
+ *  nparams, snap_ptrs, numels  the receiver's list, as delta_apply_many.
+ *  idx_host, val_host  (host) the concatenated delta, in pinned host memory
+ *                      the runtime maps for the GPU (hipHostMalloc, torch's
+ *                      pin_memory); both ends of each array are checked
+ *                      before anything is launched, and any other host memory
+ *                      is rejected with DELTA_E_INVALID.
+ *  offsets_host        (host) int64[nparams+1]: offsets[0] == 0,
+ *                      non-decreasing; copied to the workspace with the table.
+ *  max_nnz             entries j < min(offsets[nparams], max_nnz) are applied.
+ *  violations          optional device int64[1], as in delta_apply.
+ *  ws, ws_bytes        at least delta_workspace_size(0, nparams) bytes.
+ * The call only enqueues the apply: idx_host and val_host must stay valid and
+ * unchanged until the stream has passed it.  Index contract as delta_apply.
+ * Errors: DELTA_E_INVALID (null or unpinned buffers, bad offsets),
+ * DELTA_E_RANGE (numel > 2^31-1), DELTA_E_WORKSPACE, DELTA_E_HIP.
+ */
+delta_status delta_apply_many_host(int32_t nparams, uint16_t *const *snap_ptrs,
+                                   const int64_t *numels, const int32_t *idx_host,
+                                   const uint16_t *val_host, const int64_t *offsets_host,
+                                   int64_t max_nnz, int64_t *violations, void *ws,
+                                   size_t ws_bytes, void *stream);
+
+/*
  * xor_streamed_staging_size -- device bytes of the staging buffer of
  * xor_apply_streamed for chunks of `chunk_elems` elements (0 if <= 0).
  */

@@ -12,6 +12,7 @@ from ._abi import DeltaError, DeltaRangeError, load  # noqa: F401
 from .ops import (  # noqa: F401
     apply_,
     apply_many_,
+    apply_many_host_,
     apply_streamed_,
     default_capacity,
     diff,
@@ -31,6 +32,6 @@ from .sharding import flat_offset, shard0_piece  # noqa: F401
 __all__ = [
     "DeltaError", "DeltaRangeError", "load", "diff", "diff_many", "apply_", "apply_many_",
     "xor_mask", "xor_apply_", "workspace", "workspace_size", "default_capacity",
-    "shard0_piece", "flat_offset", "apply_streamed_", "xor_apply_streamed_",
+    "shard0_piece", "flat_offset", "apply_streamed_", "xor_apply_streamed_", "apply_many_host_",
     "wire_encode", "wire_decode", "wire_hashes", "wire_checksum",
 ]

@@ -52,6 +52,7 @@ SIGNATURES = {
     "delta_apply_many": (_st, [_i32, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "delta_streamed_staging_size": (_sz, [_i32, _i32, _i32, _i64]),
     "delta_apply_streamed": (_st, [_i32, _vp, _vp, _i32, _vp, _vp, _sz, _vp, _vp]),
+    "delta_apply_many_host": (_st, [_i32, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "xor_streamed_staging_size": (_sz, [_i64]),
     "xor_apply_streamed": (_st, [_vp, _vp, _i64, _i64, _vp, _sz, _vp, _vp]),
     "delta_wire_encode": (_st, [_i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _sz, _vp]),

@@ -286,6 +286,20 @@ delta_status delta_apply_streamed(int32_t nparams, uint16_t* const* snap_ptrs,
   return DELTA_OK;
 }
 
+delta_status delta_apply_many_host(int32_t nparams, uint16_t* const* snap_ptrs,
+                                   const int64_t* numels, const int32_t* idx_host,
+                                   const uint16_t* val_host, const int64_t* offsets_host,
+                                   int64_t max_nnz, int64_t* violations, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  std::string err;
+  const delta_status st =
+      sbd::apply_host_impl(nparams, snap_ptrs, numels, idx_host, val_host, offsets_host, max_nnz,
+                           violations, ws, ws_bytes, stream, err);
+  if (st != DELTA_OK) return fail(st, "%s", err.c_str());
+  g_error.clear();
+  return DELTA_OK;
+}
+
 size_t xor_streamed_staging_size(int64_t chunk_elems) {
   return chunk_elems <= 0 ? 0 : sbd::xor_streamed_staging_size(chunk_elems);
 }

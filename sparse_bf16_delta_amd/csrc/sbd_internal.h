@@ -161,6 +161,13 @@ delta_status apply_streamed_impl(int32_t nparams, uint16_t* const* snap_ptrs,
                                  const delta_host_chunk* chunks, void* staging,
                                  size_t staging_bytes, void* copy_stream, void* apply_stream,
                                  std::string& err);
+// The host-direct receiver (stream.hip): the apply kernel reads the pinned
+// host delta itself.
+size_t host_apply_workspace_size(int32_t nparams);
+delta_status apply_host_impl(int32_t nparams, uint16_t* const* snap_ptrs, const int64_t* numels,
+                             const int32_t* idx_host, const uint16_t* val_host,
+                             const int64_t* offsets_host, int64_t max_nnz, int64_t* violations,
+                             void* ws, size_t ws_bytes, void* stream, std::string& err);
 delta_status xor_apply_streamed_impl(uint16_t* snapshot, const uint16_t* mask_host, int64_t n,
                                      int64_t chunk_elems, void* staging, size_t staging_bytes,
                                      void* copy_stream, void* apply_stream, std::string& err);

@@ -13,6 +13,8 @@ memory and the current stream only.  Names mirror the sources' callables:
   xor_apply_(snap, mask)
   apply_streamed_(snaps, ...)     -- receiver: apply a host-resident delta
   xor_apply_streamed_(snap, mask) -- chunk by chunk, copies overlapping applies
+  apply_many_host_(snaps, ...)    -- receiver: the apply kernel reads a pinned
+                                     host delta itself (no staging)
   wire_encode / wire_decode / wire_checksum -- the flush's positions block
                                      and checksum (verl review, encode.py)
 
@@ -239,6 +241,51 @@ def _host_bits(t, what: str) -> torch.Tensor:
     if t.dtype not in _BIT_DTYPES:
         raise ValueError(f"{what}: unsupported dtype {t.dtype}; expected bfloat16 bits")
     return t
+
+
+def apply_many_host_(snaps: Sequence[torch.Tensor], idx: torch.Tensor, val: torch.Tensor,
+                     offsets: torch.Tensor, max_nnz: int | None = None, check_indices=False,
+                     wait=True):
+    """apply_many_ with the delta -- idx int32, val bf16 bits, offsets
+    int64[P+1], as diff_many writes them -- in host memory: idx and val must
+    be pinned (pin_memory()), and the apply kernel reads them directly over
+    the host link, with no device copy of the delta.  With wait=True (the
+    default) the call returns once the snapshots are updated; with
+    wait=False it only enqueues, and idx and val must then stay alive and
+    unchanged until the current stream has passed the apply."""
+    if not snaps:
+        raise ValueError("empty parameter list")
+    dev = snaps[0].device
+    for p, s in enumerate(snaps):
+        _bits(s, f"snaps[{p}]")
+        if s.device != dev:
+            raise ValueError(f"snaps[{p}] on another device")
+        _range(s.numel(), f"parameter {p}")
+    k = len(snaps)
+    if (not isinstance(idx, torch.Tensor) or idx.device.type != "cpu" or idx.dtype != torch.int32
+            or not idx.is_contiguous()):
+        raise ValueError("idx must be a contiguous host int32 tensor")
+    _host_bits(val, "val")
+    if idx.numel() != val.numel():
+        raise ValueError("idx and val must have equal length")
+    if not (idx.numel() == 0 or (idx.is_pinned() and val.is_pinned())):
+        raise ValueError("idx and val must be pinned host memory (tensor.pin_memory())")
+    if (not isinstance(offsets, torch.Tensor) or offsets.device.type != "cpu" or
+            offsets.dtype != torch.int64 or offsets.numel() != k + 1 or not offsets.is_contiguous()):
+        raise ValueError("offsets must be a contiguous host int64 tensor of nparams + 1 entries")
+    cap = idx.numel() if max_nnz is None else min(int(max_nnz), idx.numel())
+    lib = load()
+    ws = workspace(lib.delta_workspace_size(0, k), dev)
+    sptrs = (ctypes.c_void_p * k)(*[s.data_ptr() for s in snaps])
+    nums = (ctypes.c_int64 * k)(*[s.numel() for s in snaps])
+    v = _violations(dev, check_indices)
+    check(lib.delta_apply_many_host(k, sptrs, nums, _ptr(idx), _ptr(val), _ptr(offsets), cap,
+                                    _ptr(v) if v is not None else None, _ptr(ws), ws.numel(),
+                                    _stream(dev)))
+    if wait or check_indices:
+        torch.cuda.current_stream(dev).synchronize()
+    _raise_on_violations(v)
+    return snaps
 
 
 def apply_streamed_(snaps: Sequence[torch.Tensor], idx: torch.Tensor, val: torch.Tensor,

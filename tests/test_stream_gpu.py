@@ -136,3 +136,83 @@ def test_streamed_apply_plan_reused_over_steps(sbd, oracle_mod):
     small = StreamedApplyPlan(snaps, bounds, 1)
     with pytest.raises(sbd.DeltaError, match="more than"):
         small.run(*hf)
+
+
+# ---- the host-direct receiver: the apply kernel reads the pinned host delta
+
+@pytest.mark.parametrize("frac", [0.0, 0.01, 0.2, 0.7])
+def test_apply_many_host_matches_oracle(sbd, oracle_mod, frac):
+    """delta_apply_many_host reads idx and val straight from pinned host
+    memory; the snapshots end exactly as the oracle's apply leaves them."""
+    olds, news = [], []
+    for i, n in enumerate(SIZES):
+        o, x = rand_pair(400 + i + int(frac * 1000), n, frac)
+        olds.append(o)
+        news.append(x)
+    ri, rv, rn, ro = oracle_mod.diff_many(olds, news)
+    snaps = [torch.from_numpy(o.view(np.int16)).cuda() for o in olds]
+    # views into larger pinned buffers, starting past their first element
+    h_idx = torch.zeros(ri.size + 5, dtype=torch.int32).pin_memory()[3:3 + ri.size]
+    h_val = torch.zeros(rv.size + 5, dtype=torch.int16).pin_memory()[1:1 + rv.size]
+    h_idx.copy_(torch.from_numpy(ri))
+    h_val.copy_(torch.from_numpy(rv.view(np.int16)))
+    sbd.apply_many_host_(snaps, h_idx, h_val.view(torch.bfloat16), torch.from_numpy(ro),
+                         check_indices=True)
+    for s, x in zip(snaps, news):
+        assert np.array_equal(np_bits(s), x)
+
+
+def test_apply_many_host_from_device_diff_and_back(sbd, oracle_mod):
+    """A sender's diff_many output moved to pinned host memory, applied by the
+    host-direct path, then the reverse delta likewise: back to old."""
+    olds, news = [], []
+    for i, n in enumerate(SIZES):
+        o, x = rand_pair(500 + i, n, 0.05)
+        olds.append(o)
+        news.append(x)
+    g_o = [torch.from_numpy(o.view(np.int16)).cuda() for o in olds]
+    g_n = [torch.from_numpy(x.view(np.int16)).cuda() for x in news]
+    snaps = [t.clone() for t in g_o]
+    for src, dst, want in ((g_o, g_n, news), (g_n, g_o, olds)):
+        gi, gv, gn, go = sbd.diff_many(src, dst)
+        sbd.apply_many_host_(snaps, gi.cpu().pin_memory(), gv.cpu().pin_memory(), go.cpu())
+        for s, w in zip(snaps, want):
+            assert np.array_equal(np_bits(s), w)
+
+
+def test_apply_many_host_rejects_unpinned_and_bad_offsets(sbd):
+    """Pageable host buffers and malformed offsets are refused before any
+    launch; the snapshot is untouched."""
+    from sparse_bf16_delta_amd import _abi
+    from sparse_bf16_delta_amd.ops import _ptr, _stream
+    import ctypes
+
+    snap = torch.arange(1000, dtype=torch.int16, device="cuda")
+    before = snap.clone()
+    idx = torch.tensor([1, 5, 9], dtype=torch.int32)
+    val = torch.tensor([7, 7, 7], dtype=torch.int16)
+    off = torch.tensor([0, 3], dtype=torch.int64)
+    with pytest.raises(ValueError, match="pinned"):
+        sbd.apply_many_host_([snap], idx, val.view(torch.bfloat16), off)
+    lib = _abi.load()
+    ws = torch.empty(lib.delta_workspace_size(0, 1), dtype=torch.uint8, device="cuda")
+    sp = (ctypes.c_void_p * 1)(snap.data_ptr())
+    nums = (ctypes.c_int64 * 1)(1000)
+    # the ABI itself refuses pageable memory (it is not mapped for the GPU)
+    st = lib.delta_apply_many_host(1, sp, nums, _ptr(idx), _ptr(val), _ptr(off), 3, None,
+                                   _ptr(ws), ws.numel(), _stream(snap.device))
+    assert st == _abi.DELTA_E_INVALID and b"pinned" in lib.delta_last_error()
+    p_idx, p_val = idx.pin_memory(), val.pin_memory()
+    # the arrays must hold every entry the offsets name
+    big = torch.tensor([0, 1 << 30], dtype=torch.int64)
+    st = lib.delta_apply_many_host(1, sp, nums, _ptr(p_idx), _ptr(p_val), _ptr(big), 1 << 30,
+                                   None, _ptr(ws), ws.numel(), _stream(snap.device))
+    assert st == _abi.DELTA_E_INVALID
+    bad = torch.tensor([1, 3], dtype=torch.int64)
+    st = lib.delta_apply_many_host(1, sp, nums, _ptr(p_idx), _ptr(p_val), _ptr(bad), 3, None,
+                                   _ptr(ws), ws.numel(), _stream(snap.device))
+    assert st == _abi.DELTA_E_INVALID and b"offsets[0]" in lib.delta_last_error()
+    torch.cuda.synchronize()
+    assert torch.equal(snap, before)
+    sbd.apply_many_host_([snap], p_idx, p_val.view(torch.bfloat16), off)
+    assert [int(snap[i]) for i in (1, 5, 9)] == [7, 7, 7]
