@@ -101,6 +101,35 @@ def test_streamed_abi_rejects_bad_chunks():
     assert lib.xor_streamed_staging_size(0) == 0
 
 
+def test_host_apply_abi_rejects_bad_arguments():
+    """delta_apply_many_host checks its counts, pointers, sizes and offsets
+    before it asks the runtime about the host buffers or launches anything."""
+    lib = _abi.load()
+    snaps = (ctypes.c_void_p * 2)(16, 32)
+    nums = (ctypes.c_int64 * 2)(10, 20)
+    idx = (ctypes.c_int32 * 4)(1, 2, 3, 4)
+    val = (ctypes.c_uint16 * 4)(1, 2, 3, 4)
+    ws = ctypes.c_void_p(256)
+
+    def call(offs, n=2, sp=snaps, nm=nums, max_nnz=4):
+        return lib.delta_apply_many_host(n, sp, nm, ctypes.addressof(idx), ctypes.addressof(val),
+                                         offs, max_nnz, None, ws, 1 << 30, None)
+
+    good = (ctypes.c_int64 * 3)(0, 2, 4)
+    assert call(good, n=-1) == _abi.DELTA_E_INVALID
+    assert call(good, max_nnz=-1) == _abi.DELTA_E_INVALID
+    assert call(None) == _abi.DELTA_E_INVALID
+    assert call(good, sp=None) == _abi.DELTA_E_INVALID
+    assert call(good, nm=(ctypes.c_int64 * 2)(10, -5)) == _abi.DELTA_E_INVALID
+    assert call(good, nm=(ctypes.c_int64 * 2)(10, 1 << 31)) == _abi.DELTA_E_RANGE
+    assert call(good, sp=(ctypes.c_void_p * 2)(16, None)) == _abi.DELTA_E_INVALID
+    assert "null snapshot" in lib.delta_last_error().decode()
+    assert call((ctypes.c_int64 * 3)(1, 2, 4)) == _abi.DELTA_E_INVALID
+    assert "offsets[0]" in lib.delta_last_error().decode()
+    assert call((ctypes.c_int64 * 3)(0, 3, 2)) == _abi.DELTA_E_INVALID
+    assert "decrease" in lib.delta_last_error().decode()
+
+
 def test_wire_abi_rejects_bad_arguments():
     lib = _abi.load()
     one = ctypes.c_void_p(16)
