@@ -13,9 +13,9 @@ Step 2 turns the receiver snapshot into `new`, step 4 turns it back into
 Default workload: the Llama-7B-shaped list (291 tensors, 6,738,415,616 bf16
 elements), weights N(0, 0.02), bf16-resident step at lr 1e-6 (about 1 %
 changed).  Inputs are generated on the GPU and resident in HBM before timing.
-Other modes: --config c1/c2 (smaller lists), c4 (density sweep), c5 (the
-405B-shaped 10-layer share, streamed layer by layer, in place), --shards W,
---receiver, --wire.
+Other modes: --config tensor1m / qwen3_0p6b (smaller lists), sweep256m (the
+density sweep), llama405b_share (the 405B-shaped 10-layer share, streamed
+layer by layer, in place), --shards W, --receiver, --wire.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -80,10 +80,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5"],
-                    help="c3 (default): the 7B-shaped list; c1, c2: smaller lists; "
-                         "c4: density sweep on one flat 2^28-element tensor (table on stderr); "
-                         "c5: the 405B-shaped 10-layer share, streamed layer by layer")
+    ap.add_argument("--config", default="llama7b",
+                    choices=["tensor1m", "qwen3_0p6b", "llama7b", "sweep256m", "llama405b_share"],
+                    help="llama7b (default): the 7B-shaped list; tensor1m, qwen3_0p6b: smaller "
+                         "lists; sweep256m: density sweep on one flat 2^28-element tensor (table "
+                         "on stderr); llama405b_share: the 405B-shaped 10-layer share, streamed "
+                         "layer by layer")
     ap.add_argument("--lr", type=float, default=None)
     ap.add_argument("--mode", default=None, choices=[None, "fp32_master", "bf16_resident"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -133,10 +135,10 @@ def main():
     sbd.load()
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
-    if args.config == "c4":
+    if args.config == "sweep256m":
         density_sweep(args, props)
         return
-    if args.config == "c5":
+    if args.config == "llama405b_share":
         layer_stream_run(args, props)
         return
     if args.shards > 0:
@@ -149,7 +151,7 @@ def main():
         wire_run(args, props)
         return
     cfg = workloads.CONFIGS[args.config]
-    lr = args.lr if args.lr is not None else (1e-6 if cfg.key == "c3" else cfg.lrs[0])
+    lr = args.lr if args.lr is not None else (1e-6 if cfg.key == "llama7b" else cfg.lrs[0])
     mode = args.mode or cfg.mode
     numels = cfg.numels
     n_model = sum(numels)
@@ -164,7 +166,7 @@ def main():
     old = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
     new = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
     for t, (o, n) in enumerate(zip(offs, numels)):
-        sw, su = workloads.seeds(cfg.number, t)
+        sw, su = workloads.seeds(cfg.seed_family, t)
         workloads.fill_step_pair_(old[o:o + n], new[o:o + n], sw, su, lr, mode)
     snap = old.clone()
     mask = torch.empty(n_alloc, dtype=torch.int16, device=dev)
@@ -334,7 +336,7 @@ def wire_run(args, props):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     cfg = workloads.CONFIGS[args.config]
-    lr = args.lr if args.lr is not None else (1e-6 if cfg.key == "c3" else cfg.lrs[0])
+    lr = args.lr if args.lr is not None else (1e-6 if cfg.key == "llama7b" else cfg.lrs[0])
     mode = args.mode or cfg.mode
     numels = cfg.numels
     n_model = sum(numels)
@@ -342,7 +344,7 @@ def wire_run(args, props):
     old = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
     new = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
     for t, (o, n) in enumerate(zip(offs, numels)):
-        workloads.fill_step_pair_(old[o:o + n], new[o:o + n], *workloads.seeds(cfg.number, t),
+        workloads.fill_step_pair_(old[o:o + n], new[o:o + n], *workloads.seeds(cfg.seed_family, t),
                                   lr, mode)
     dplan = DiffPlan([old[o:o + n] for o, n in zip(offs, numels)],
                      [new[o:o + n] for o, n in zip(offs, numels)], n_model // 8 + 65536)
@@ -434,7 +436,7 @@ def receiver_run(args, props):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     cfg = workloads.CONFIGS[args.config]
-    lr = args.lr if args.lr is not None else (1e-6 if cfg.key == "c3" else cfg.lrs[0])
+    lr = args.lr if args.lr is not None else (1e-6 if cfg.key == "llama7b" else cfg.lrs[0])
     mode = args.mode or cfg.mode
     numels = cfg.numels
     n_model = sum(numels)
@@ -442,7 +444,7 @@ def receiver_run(args, props):
     old = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
     new = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
     for t, (o, n) in enumerate(zip(offs, numels)):
-        workloads.fill_step_pair_(old[o:o + n], new[o:o + n], *workloads.seeds(cfg.number, t),
+        workloads.fill_step_pair_(old[o:o + n], new[o:o + n], *workloads.seeds(cfg.seed_family, t),
                                   lr, mode)
     olds = [old[o:o + n] for o, n in zip(offs, numels)]
     news = [new[o:o + n] for o, n in zip(offs, numels)]
@@ -566,7 +568,7 @@ def sharded_run(args, props):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     cfg = workloads.CONFIGS[args.config]
-    lr = args.lr if args.lr is not None else (1e-6 if cfg.key == "c3" else cfg.lrs[0])
+    lr = args.lr if args.lr is not None else (1e-6 if cfg.key == "llama7b" else cfg.lrs[0])
     mode = args.mode or cfg.mode
     numels = cfg.numels
     n_model = sum(numels)
@@ -574,7 +576,7 @@ def sharded_run(args, props):
     old = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
     new = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
     for t, (o, n) in enumerate(zip(offs, numels)):
-        workloads.fill_step_pair_(old[o:o + n], new[o:o + n], *workloads.seeds(cfg.number, t),
+        workloads.fill_step_pair_(old[o:o + n], new[o:o + n], *workloads.seeds(cfg.seed_family, t),
                                   lr, mode)
     shapes = [shape for _, shape in cfg.params]
     world = args.shards
@@ -734,7 +736,7 @@ def layer_stream_run(args, props):
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
-    cfg = workloads.CONFIGS["c5"]
+    cfg = workloads.CONFIGS["llama405b_share"]
     lr = args.lr if args.lr is not None else cfg.lrs[0]
     mode = args.mode or cfg.mode
     numels = cfg.numels
@@ -743,13 +745,13 @@ def layer_stream_run(args, props):
     per = 7
     layers = len(numels) // per
     log(f"[bench] device {props.name}, {props.total_memory / 2**30:.0f} GiB")
-    log(f"[bench] workload c5: {layers} layers x {per} tensors, {n_model:,} elements, "
+    log(f"[bench] workload {cfg.key}: {layers} layers x {per} tensors, {n_model:,} elements, "
         f"lr {lr:g}, {mode}")
     t0 = time.perf_counter()
     old = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
     new = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
     for t, (o, n) in enumerate(zip(offs, numels)):
-        workloads.fill_step_pair_(old[o:o + n], new[o:o + n], *workloads.seeds(cfg.number, t),
+        workloads.fill_step_pair_(old[o:o + n], new[o:o + n], *workloads.seeds(cfg.seed_family, t),
                                   lr, mode)
     torch.cuda.synchronize()
     log(f"[bench] generated inputs in {time.perf_counter() - t0:.1f} s")
@@ -808,7 +810,7 @@ def layer_stream_run(args, props):
         sbd.xor_mask(a, b, out=m)
         x["ap"].run(x["dp"].idx, x["dp"].val, x["dp"].offsets, x["cap"])
         if not torch.equal(a.view(torch.int16), b.view(torch.int16)):
-            print("bench.py: c5 apply check failed", file=sys.stderr)
+            print("bench.py: 405B-share apply check failed", file=sys.stderr)
             sys.exit(1)
         sbd.xor_apply_(a, m)
     for _ in range(args.warmup):
@@ -831,7 +833,7 @@ def layer_stream_run(args, props):
         ck = (int(x["dp"].idx[:x["nnz"]].to(torch.int64).sum().item()),
               int(x["dp"].val[:x["nnz"]].view(torch.int16).to(torch.int64).sum().item()))
         if x["dp"].changed() != x["nnz"] or ck != x["ck"]:
-            print("bench.py: c5 timed steps changed the result", file=sys.stderr)
+            print("bench.py: 405B-share timed steps changed the result", file=sys.stderr)
             sys.exit(1)
     g128 = sum(x["g128"] for x in L)
     alg = [4 * n_model + 6 * nnz_total, 6 * nnz_total + 256 * g128, 6 * n_alloc,

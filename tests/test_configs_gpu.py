@@ -38,7 +38,7 @@ def build_arenas(cfg, lr, mode, dev, params=None):
     old = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
     new = torch.zeros(n_alloc, dtype=torch.bfloat16, device=dev)
     for t, o, n in zip(params, offs, numels):
-        workloads.fill_step_pair_(old[o:o + n], new[o:o + n], *workloads.seeds(cfg.number, t),
+        workloads.fill_step_pair_(old[o:o + n], new[o:o + n], *workloads.seeds(cfg.seed_family, t),
                                   lr, mode)
     olds = [old[o:o + n] for o, n in zip(offs, numels)]
     news = [new[o:o + n] for o, n in zip(offs, numels)]
@@ -72,7 +72,7 @@ def check_whole_list(sbd, oracle_mod, olds, news, capacity):
 
 
 def test_qwen3_0p6b_list_full(sbd, oracle_mod):
-    cfg = workloads.CONFIGS["c2"]
+    cfg = workloads.CONFIGS["qwen3_0p6b"]
     old, new, olds, news, offs, numels = build_arenas(cfg, 3e-6, "fp32_master", "cuda")
     total = check_whole_list(sbd, oracle_mod, olds, news, cfg.total // 4)
     mask = sbd.xor_mask(old, new)
@@ -86,7 +86,7 @@ def test_qwen3_0p6b_list_full(sbd, oracle_mod):
 def test_llama7b_headline_full(sbd, oracle_mod):
     """The benchmark's workload: bf16-resident step at lr 1e-6, every tensor
     compared with the oracle."""
-    cfg = workloads.CONFIGS["c3"]
+    cfg = workloads.CONFIGS["llama7b"]
     old, new, olds, news, offs, numels = build_arenas(cfg, 1e-6, "bf16_resident", "cuda")
     total = check_whole_list(sbd, oracle_mod, olds, news, cfg.total // 8)
     print(f"llama-7B list lr 1e-6 bf16-resident: {total} changed ({total / cfg.total:.4%})")
@@ -100,7 +100,7 @@ def test_llama7b_other_steps(sbd, oracle_mod, lr, mode):
     the oracle on three whole tensors."""
     from sparse_bf16_delta_amd.plan import ApplyPlan, DiffPlan
 
-    cfg = workloads.CONFIGS["c3"]
+    cfg = workloads.CONFIGS["llama7b"]
     old, new, olds, news, offs, numels = build_arenas(cfg, lr, mode, "cuda")
     dp = DiffPlan(olds, news, cfg.total // 4)
     dp.run()
@@ -141,7 +141,7 @@ def test_density_sweep_flat_2p28(sbd, oracle_mod, pattern, di, frac):
 def llama405b_share():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    cfg = workloads.CONFIGS["c5"]
+    cfg = workloads.CONFIGS["llama405b_share"]
     old, new, olds, news, offs, numels = build_arenas(cfg, 3e-6, "fp32_master", "cuda")
     torch.cuda.synchronize()
     yield cfg, old, new, olds, news

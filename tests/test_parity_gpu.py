@@ -685,8 +685,8 @@ def test_xor_mask_may_alias_new(sbd, oracle_mod):
 
 def test_c1_single_tensor_roundtrip(sbd, oracle_mod):
     """1024x1024 bf16, fp32-master step at lr 3e-6: diff, apply, XOR round trip."""
-    cfg = workloads.CONFIGS["c1"]
-    sw, su = workloads.seeds(cfg.number, 0)
+    cfg = workloads.CONFIGS["tensor1m"]
+    sw, su = workloads.seeds(cfg.seed_family, 0)
     old, new = workloads.make_step_pair(1 << 20, sw, su, 3e-6, "fp32_master", device="cuda")
     o_np, n_np = np_bits(old), np_bits(new)
     ri, rv = oracle_mod.diff(o_np, n_np)
@@ -701,7 +701,7 @@ def test_c1_single_tensor_roundtrip(sbd, oracle_mod):
     snap2 = old.clone()
     sbd.xor_apply_(snap2, mask)
     assert torch.equal(snap2.view(torch.int16), new.view(torch.int16))
-    print(f"c1 realized density {ri.size / (1 << 20):.4%}")
+    print(f"1024x1024 tensor: realized density {ri.size / (1 << 20):.4%}")
 
 
 def test_diff_many_empty_list_through_abi(sbd):

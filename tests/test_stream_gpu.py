@@ -71,14 +71,14 @@ def test_apply_streamed_matches_oracle(sbd, oracle_mod, bounds, pinned, frac):
 def test_apply_streamed_tile_kinds_from_device_diff(sbd, oracle_mod):
     """The sender's diff_many output, moved to pinned host memory, streamed
     back into a copy of the old snapshots gives the new ones."""
-    cfg = workloads.CONFIGS["c2"]
+    cfg = workloads.CONFIGS["qwen3_0p6b"]
     params = list(range(0, len(cfg.params), 7))[:40]
     numels = [cfg.numels[t] for t in params]
     offs, n_alloc = workloads.flat_layout(numels)
     old = torch.zeros(n_alloc, dtype=torch.bfloat16, device="cuda")
     new = torch.zeros(n_alloc, dtype=torch.bfloat16, device="cuda")
     for t, o, n in zip(params, offs, numels):
-        workloads.fill_step_pair_(old[o:o + n], new[o:o + n], *workloads.seeds(cfg.number, t),
+        workloads.fill_step_pair_(old[o:o + n], new[o:o + n], *workloads.seeds(cfg.seed_family, t),
                                   3e-6, "fp32_master")
     olds = [old[o:o + n] for o, n in zip(offs, numels)]
     news = [new[o:o + n] for o, n in zip(offs, numels)]

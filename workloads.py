@@ -19,8 +19,8 @@ Density sweep.  A seeded subset of exactly k = round(f*n) elements (uniform
 pattern) or of whole aligned 2048-element (4 KB) runs (clustered pattern) is
 forced to a different bf16 value by toggling the lowest significand bit.
 
-Seeds: tensor t of configuration c uses seed (c << 20) | (t << 1) for w and
-that value | 1 for u.  Generation runs on whatever device the caller names;
+Seeds: tensor t of a workload whose seed family is f uses seed
+(f << 20) | (t << 1) for w and that value | 1 for u.  Generation runs on whatever device the caller names;
 parity never depends on the RNG because both sides receive the same bits.
 """
 from __future__ import annotations
@@ -39,7 +39,7 @@ DENSITIES = (0.00085, 0.01, 0.02, 0.10, 0.50)
 @dataclass(frozen=True)
 class Config:
     key: str
-    number: int
+    seed_family: int         # the f of the seed recipe above
     title: str
     params: tuple            # ((name, shape), ...)
     lrs: tuple
@@ -115,21 +115,21 @@ def _llama_405b_share(layers=10):
 
 
 CONFIGS = {
-    "c1": Config("c1", 1, "single bf16 tensor 1024x1024", (("w", (1024, 1024)),),
+    "tensor1m": Config("tensor1m", 1, "single bf16 tensor 1024x1024", (("w", (1024, 1024)),),
                  (3e-6,), "fp32_master"),
-    "c2": Config("c2", 2, "Qwen3-0.6B-shaped parameter list", _qwen3_0p6b(),
+    "qwen3_0p6b": Config("qwen3_0p6b", 2, "Qwen3-0.6B-shaped parameter list", _qwen3_0p6b(),
                  (3e-6,), "fp32_master"),
-    "c3": Config("c3", 3, "Llama-7B-shaped parameter list", _llama_7b(),
+    "llama7b": Config("llama7b", 3, "Llama-7B-shaped parameter list", _llama_7b(),
                  (1e-6, 3e-6, 1e-5), "bf16_resident"),
-    "c4": Config("c4", 4, "flat 256M-element tensor, density sweep",
+    "sweep256m": Config("sweep256m", 4, "flat 256M-element tensor, density sweep",
                  (("flat", (1 << 28,)),), (), "forced"),
-    "c5": Config("c5", 5, "Llama-3.1-405B-shaped 10-layer share", _llama_405b_share(),
+    "llama405b_share": Config("llama405b_share", 5, "Llama-3.1-405B-shaped 10-layer share", _llama_405b_share(),
                  (3e-6,), "fp32_master"),
 }
 
 
-def seeds(config_number: int, tensor_index: int):
-    s_w = (config_number << 20) | (tensor_index << 1)
+def seeds(seed_family: int, tensor_index: int):
+    s_w = (seed_family << 20) | (tensor_index << 1)
     return s_w, s_w | 1
 
 
