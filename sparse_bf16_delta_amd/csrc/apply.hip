@@ -472,6 +472,7 @@ void launch_apply_kernel(unsigned blocks, const SnapParam* d_table, const SnapPa
 hipError_t launch_apply(const SnapParam* d_table, const SnapParam& single, int32_t nparams,
                         const int64_t* offsets, const int32_t* idx, const uint16_t* val,
                         int64_t max_nnz, int64_t* violations, hipStream_t stream) {
+  clear_stale_error();
   if (violations != nullptr) zero_i64_kernel<<<dim3(1), dim3(64), 0, stream>>>(violations);
   if (max_nnz > 0) {
     int64_t blocks = (max_nnz + kApplyChunk - 1) / kApplyChunk;

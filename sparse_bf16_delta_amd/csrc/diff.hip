@@ -629,6 +629,7 @@ hipError_t launch_diff(const DiffParam* d_table, const DiffParam& single, int32_
                        int64_t total_tiles, void* idx, bool global_idx, uint16_t* val,
                        int64_t capacity, int64_t* nnz, int64_t* offsets, void* ws,
                        const WsLayout& L, hipStream_t stream) {
+  clear_stale_error();
   char* base = static_cast<char*>(ws);
   uint32_t* ndense = reinterpret_cast<uint32_t*>(base + L.ndense);
   uint32_t* counts = reinterpret_cast<uint32_t*>(base + L.counts);
@@ -670,6 +671,9 @@ hipError_t launch_diff(const DiffParam* d_table, const DiffParam& single, int32_
   else
     diff_base_kernel<false><<<dim3(1), dim3(kScanBlock), 0, stream>>>(
         nullptr, nparams, total_tiles, nchunks, inpfx, chunk_tot, chunk_base, nnz, offsets);
+  // checked here: the placing launcher's occupancy query clears the error state if it fails
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (total_tiles > 0) {
     if (many && global_idx)
       launch_place<true, int64_t>(tdesc, single, total_tiles, nchunks, inpfx, chunk_base, compact,

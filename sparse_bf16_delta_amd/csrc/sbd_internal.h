@@ -140,6 +140,11 @@ struct WsLayout {
 WsLayout ws_layout(int64_t max_tiles, int32_t nparams);
 int64_t max_tiles_for(int64_t total_elems, int32_t nparams);
 
+// The runtime keeps one error per thread, set by any failed call, and a
+// launch check reads it.  Every launcher clears it before launching, so a
+// failure left by some earlier, unrelated call is not reported as its own.
+inline void clear_stale_error() { (void)hipGetLastError(); }
+
 // Launchers return hipSuccess or the launch error.
 // idx is int32_t[capacity] (parameter-local indices) or, with global_idx,
 // int64_t[capacity] holding flat_offset + local index (parameter lists only).

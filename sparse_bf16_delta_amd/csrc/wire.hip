@@ -216,6 +216,7 @@ hipError_t launch_wire_encode(int32_t nparams, const int32_t* widths, const int3
                               const int64_t* offsets, int64_t max_entries, uint8_t* positions,
                               int64_t positions_capacity, int64_t* pos_offsets,
                               hipStream_t stream) {
+  clear_stale_error();
   wire_offsets_kernel<<<dim3(1), dim3(kScanThreads), 0, stream>>>(nparams, widths, offsets,
                                                                    pos_offsets);
   if (nparams > 0 && max_entries > 0)
@@ -228,6 +229,7 @@ hipError_t launch_wire_encode(int32_t nparams, const int32_t* widths, const int3
 hipError_t launch_wire_decode(int32_t nparams, const int32_t* widths, const uint8_t* positions,
                               const int64_t* pos_offsets, const int64_t* offsets,
                               int64_t max_entries, int32_t* idx, hipStream_t stream) {
+  clear_stale_error();
   if (nparams > 0 && max_entries > 0)
     wire_code_kernel<true><<<dim3(code_grid(max_entries)), dim3(kWireBlock), 0, stream>>>(
         nparams, widths, offsets, pos_offsets, max_entries, idx,
@@ -237,6 +239,7 @@ hipError_t launch_wire_decode(int32_t nparams, const int32_t* widths, const uint
 
 hipError_t launch_wire_hash(const uint8_t* positions, int64_t npos, const uint16_t* values,
                             int64_t nval, uint64_t* hashes, hipStream_t stream) {
+  clear_stale_error();
   wire_hash_zero_kernel<<<dim3(1), dim3(64), 0, stream>>>(hashes);
   // a bounded grid: every workgroup ends in one atomic per hash on the same
   // two addresses, which serialise

@@ -120,7 +120,8 @@ __global__ __launch_bounds__(kXorBlock) void xor_scalar_kernel(const uint16_t* a
 
 hipError_t launch_xor3(const uint16_t* a, const uint16_t* b, uint16_t* out, int64_t n,
                        hipStream_t stream) {
-  if (n <= 0) return hipGetLastError();
+  clear_stale_error();
+  if (n <= 0) return hipSuccess;
   const bool aligned = ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
                          reinterpret_cast<uintptr_t>(out)) & 15u) == 0;
   if (aligned) {
@@ -150,7 +151,8 @@ hipError_t launch_xor_mask(const uint16_t* a, const uint16_t* b, uint16_t* out, 
 
 hipError_t launch_xor_apply(uint16_t* snap, const uint16_t* mask, int64_t n,
                             hipStream_t stream) {
-  if (n <= 0) return hipGetLastError();
+  clear_stale_error();
+  if (n <= 0) return hipSuccess;
   const bool aligned =
       ((reinterpret_cast<uintptr_t>(snap) | reinterpret_cast<uintptr_t>(mask)) & 15u) == 0;
   if (aligned) {
