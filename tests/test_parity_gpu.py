@@ -622,6 +622,33 @@ def test_many_thousands_of_parameters(sbd, oracle_mod, frac):
     assert np.array_equal(np_bits(g_old), new)
 
 
+def test_two_streams_at_once(sbd, oracle_mod):
+    """Two parameter lists diffed and applied concurrently on two streams:
+    each stream has its own cached workspace (and so its own staging arena
+    and counters), and both results match the oracle."""
+    cases = []
+    for seed, frac in ((61, 0.02), (62, 0.15)):
+        olds, news = _param_list(seed, MANY_SIZES + [9 * TILE + 5], frac)
+        cases.append((olds, news, oracle_mod.diff_many(olds, news)))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    out = []
+    for (olds, news, _), st in zip(cases, streams):
+        g_o = [gpu_bits(o) for o in olds]
+        g_n = [gpu_bits(x) for x in news]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            gi, gv, gn, go = sbd.diff_many(g_o, g_n)
+            sbd.apply_many_(g_o, gi, gv, go)
+        out.append((gi, gv, gn, go, g_o))
+    torch.cuda.synchronize()
+    for (olds, news, (ri, rv, rn, ro)), (gi, gv, gn, go, g_o) in zip(cases, out):
+        assert np.array_equal(go.cpu().numpy(), ro)
+        assert np.array_equal(gi.cpu().numpy(), ri)
+        assert np.array_equal(np_bits(gv), rv)
+        for s_, x in zip(g_o, news):
+            assert np.array_equal(np_bits(s_), x)
+
+
 def test_diff_many_then_apply_many_without_host_sync(sbd):
     """The receiver can follow the sender on one stream: apply_many reads the
     device offsets written by diff_many; the result equals `new` bitwise."""
