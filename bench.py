@@ -78,7 +78,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="llama7b",
                     choices=["tensor1m", "qwen3_0p6b", "llama7b", "sweep256m", "llama405b_share"],
@@ -249,8 +249,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_step = 1e3 * wall / args.steps
-    op_ms = [sum(events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps))
-             / args.steps for i in range(4)]
+    samples = [sorted(events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps))
+               for i in range(4)]
+    op_ms = [sum(x) / args.steps for x in samples]  # the mean: what a step spends
     if dplan.changed() != nnz_total or not torch.equal(snap.view(torch.int16),
                                                        old.view(torch.int16)):
         print("bench.py: timed steps changed the result", file=sys.stderr)
@@ -260,14 +261,16 @@ def main():
     workload_key = f"{cfg.key}:{mode}:{lr:g}"
     traffic = measured_traffic(workload_key)
     kernels = []
-    for name, ms, b in zip(names, op_ms, alg):
+    for name, ms, b, x in zip(names, op_ms, alg, samples):
         gbs = b / (ms * 1e-3) / 1e9
-        kernels.append({"kernel": name, "ms": round(ms, 4), "alg_bytes": b,
+        kernels.append({"kernel": name, "ms": round(ms, 4), "ms_median": round(x[len(x) // 2], 4),
+                        "ms_min": round(x[0], 4), "alg_bytes": b,
                         "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
                         "weights_gbs": round(2 * n_model / (ms * 1e-3) / 1e9, 1),
                         "traffic": traffic.get(name)})
     for kk in kernels:
-        log(f"[bench] {kk['kernel']:17s} {kk['ms']:8.3f} ms  {kk['achieved_gbs']:8.1f} GB/s "
+        log(f"[bench] {kk['kernel']:17s} {kk['ms']:8.3f} ms (median {kk['ms_median']:.3f}, min "
+            f"{kk['ms_min']:.3f})  {kk['achieved_gbs']:8.1f} GB/s "
             f"({100 * kk['frac']:.1f} % of peak)  weights {kk['weights_gbs']:.1f} GB/s")
     dom = max(range(4), key=lambda i: op_ms[i])
     roofline = {"bound": "hbm", "kernel": names[dom],
