@@ -292,9 +292,10 @@ delta_status delta_apply_streamed(int32_t nparams, uint16_t *const *snap_ptrs,
  *  nparams, snap_ptrs, numels  the receiver's list, as delta_apply_many.
  *  idx_host, val_host  (host) the concatenated delta, in pinned host memory
  *                      the runtime maps for the GPU (hipHostMalloc, torch's
- *                      pin_memory); both ends of each array are checked
- *                      before anything is launched, and any other host memory
- *                      is rejected with DELTA_E_INVALID.
+ *                      pin_memory); each array must lie whole inside one
+ *                      such allocation, which is checked before anything is
+ *                      launched, and any other host memory is rejected with
+ *                      DELTA_E_INVALID.
  *  offsets_host        (host) int64[nparams+1]: offsets[0] == 0,
  *                      non-decreasing; copied to the workspace with the table.
  *  max_nnz             entries j < min(offsets[nparams], max_nnz) are applied.

@@ -112,7 +112,8 @@ delta_status apply_streamed_impl(int32_t nparams, uint16_t* const* snap_ptrs,
     return s;
   };
   if (nparams < 0 || nchunks < 0) return fail(DELTA_E_INVALID, "delta_apply_streamed: negative count");
-  if (nchunks > 0 && (chunks == nullptr || snap_ptrs == nullptr || numels == nullptr))
+  if ((nchunks > 0 && chunks == nullptr) ||
+      (nparams > 0 && (snap_ptrs == nullptr || numels == nullptr)))
     return fail(DELTA_E_INVALID, "delta_apply_streamed: null argument");
   std::vector<SnapParam> table(static_cast<size_t>(nparams));
   for (int32_t p = 0; p < nparams; ++p) {

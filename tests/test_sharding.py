@@ -94,6 +94,10 @@ def test_streamed_abi_rejects_bad_chunks():
     assert call([chunk(0, 2, dec)]) == _abi.DELTA_E_INVALID
     assert "decrease" in lib.delta_last_error().decode()
     assert call([chunk(0, 2, good)], staging_bytes=16) == _abi.DELTA_E_WORKSPACE
+    # a parameter list without its arrays is rejected even with no chunks
+    assert lib.delta_apply_streamed(3, None, None, 0, None, ctypes.c_void_p(256), 1 << 40,
+                                    None, None) == _abi.DELTA_E_INVALID
+    assert "null argument" in lib.delta_last_error().decode()
     assert lib.xor_apply_streamed(None, None, 10, 0, None, 0, None, None) == _abi.DELTA_E_INVALID
     assert lib.xor_apply_streamed(ctypes.c_void_p(16), ctypes.c_void_p(16), 100, 64,
                                   ctypes.c_void_p(256), 8, None, None) == _abi.DELTA_E_WORKSPACE
