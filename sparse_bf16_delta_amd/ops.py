@@ -308,6 +308,8 @@ def apply_streamed_(snaps: Sequence[torch.Tensor], idx: torch.Tensor, val: torch
             or not idx.is_contiguous()):
         raise ValueError("idx must be a contiguous host int32 tensor")
     _host_bits(val, "val")
+    if idx.numel() != val.numel():
+        raise ValueError("idx and val must have equal length")
     if (not isinstance(offsets, torch.Tensor) or offsets.device.type != "cpu" or
             offsets.dtype != torch.int64 or offsets.numel() != k + 1):
         raise ValueError("offsets must be a host int64 tensor of nparams + 1 entries")
@@ -378,8 +380,10 @@ def wire_encode(idx: torch.Tensor, offsets: torch.Tensor, numels: Sequence[int])
     int64[P+1]) on the device; one device-to-host read of the offsets sizes it."""
     k = len(numels)
     dev = idx.device
-    if idx.dtype != torch.int32 or offsets.dtype != torch.int64 or offsets.numel() != k + 1:
-        raise ValueError("idx must be int32 and offsets int64[nparams+1]")
+    if (idx.dtype != torch.int32 or not idx.is_contiguous() or dev.type != "cuda"
+            or offsets.dtype != torch.int64 or offsets.numel() != k + 1 or offsets.device != dev):
+        raise ValueError("idx must be contiguous int32 on a GPU and offsets int64[nparams+1] "
+                         "on the same device")
     off = offsets.cpu().tolist()
     size = sum((off[p + 1] - off[p]) * wire_width(n) for p, n in enumerate(numels))
     positions = torch.empty(max(size, 1), dtype=torch.uint8, device=dev)
@@ -398,6 +402,12 @@ def wire_decode(positions: torch.Tensor, pos_offsets: torch.Tensor, offsets: tor
     """int32 parameter-local indices back from a positions block."""
     k = len(numels)
     dev = positions.device
+    if (positions.dtype != torch.uint8 or not positions.is_contiguous() or dev.type != "cuda"
+            or pos_offsets.dtype != torch.int64 or pos_offsets.numel() != k + 1
+            or pos_offsets.device != dev or offsets.dtype != torch.int64
+            or offsets.numel() != k + 1 or offsets.device != dev):
+        raise ValueError("positions must be contiguous uint8 on a GPU, pos_offsets and offsets "
+                         "int64[nparams+1] on the same device")
     total = int(offsets[k].item())
     idx = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
     lib = load()

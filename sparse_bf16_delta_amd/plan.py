@@ -16,7 +16,7 @@ from typing import Sequence
 import torch
 
 from ._abi import DeltaError, HostChunk, check, load
-from .ops import _bits, _ptr, _range, _stream
+from .ops import _BIT_DTYPES, _bits, _ptr, _range, _stream
 
 
 class DiffPlan:
@@ -108,9 +108,21 @@ class ApplyPlan:
             max_nnz: int | None = None, violations: torch.Tensor | None = None):
         """Enqueue the scatter of a diff_many-layout delta; returns without syncing.
         Entries j < min(offsets[nparams], max_nnz) are applied."""
-        if offsets.numel() != self.nparams + 1 or offsets.dtype != torch.int64:
-            raise ValueError("offsets must be int64[nparams+1]")
-        m = idx.numel() if max_nnz is None else int(max_nnz)
+        dev = self.device
+        _bits(val, "val")
+        if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.device != dev:
+            raise ValueError("idx must be a contiguous int32 tensor on the snapshots' device")
+        if val.numel() != idx.numel() or val.device != dev:
+            raise ValueError("idx and val must have equal length on the snapshots' device")
+        if (offsets.numel() != self.nparams + 1 or offsets.dtype != torch.int64
+                or not offsets.is_contiguous() or offsets.device != dev):
+            raise ValueError("offsets must be a contiguous int64[nparams+1] on the snapshots' "
+                             "device")
+        if violations is not None and (violations.dtype != torch.int64 or
+                                       violations.device != dev):
+            raise ValueError("violations must be an int64 tensor on the snapshots' device")
+        # the kernel never reads past the buffers, whatever the device offsets say
+        m = idx.numel() if max_nnz is None else min(int(max_nnz), idx.numel())
         check(load().delta_apply_many(self.nparams, self._sptrs, self._nums, _ptr(idx), _ptr(val),
                                       _ptr(offsets), m,
                                       _ptr(violations) if violations is not None else None,
@@ -160,9 +172,15 @@ class StreamedApplyPlan:
         after the snapshots are updated."""
         if (idx.device.type != "cpu" or val.device.type != "cpu" or offsets.device.type != "cpu"
                 or idx.dtype != torch.int32 or offsets.dtype != torch.int64
-                or offsets.numel() != self.nparams + 1):
-            raise ValueError("idx int32, val and offsets int64[nparams+1] must be host tensors")
+                or offsets.numel() != self.nparams + 1 or not idx.is_contiguous()
+                or not val.is_contiguous() or val.dtype not in _BIT_DTYPES):
+            raise ValueError("idx int32, val (bf16 bits) and offsets int64[nparams+1] must be "
+                             "contiguous host tensors")
+        if idx.numel() != val.numel():
+            raise ValueError("idx and val must have equal length")
         off = offsets.tolist()
+        if off[0] != 0 or any(x > y for x, y in zip(off, off[1:])) or off[-1] > idx.numel():
+            raise ValueError("offsets must start at 0, not decrease and stay within idx")
         b = self.bounds
         rel = torch.empty(self.nparams + self.nchunks, dtype=torch.int64)
         r = rel.numpy()

@@ -212,7 +212,11 @@ def test_apply_many_host_rejects_unpinned_and_bad_offsets(sbd):
     st = lib.delta_apply_many_host(1, sp, nums, _ptr(p_idx), _ptr(p_val), _ptr(bad), 3, None,
                                    _ptr(ws), ws.numel(), _stream(snap.device))
     assert st == _abi.DELTA_E_INVALID and b"offsets[0]" in lib.delta_last_error()
+    # the streamed receiver refuses a val shorter than idx before any copy
+    with pytest.raises(ValueError, match="equal length"):
+        sbd.apply_streamed_([snap], p_idx, p_val[:2].view(torch.bfloat16), off, [0, 1])
     torch.cuda.synchronize()
+    assert torch.equal(snap, before)
     assert torch.equal(snap, before)
     sbd.apply_many_host_([snap], p_idx, p_val.view(torch.bfloat16), off)
     assert [int(snap[i]) for i in (1, 5, 9)] == [7, 7, 7]

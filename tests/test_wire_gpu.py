@@ -94,3 +94,23 @@ def test_wire_encode_respects_capacity(sbd, oracle_mod):
     assert np.array_equal(got[:whole], want_pos[:whole])
     assert np.all(got[whole:] == 0xAB)  # the entry across the cut and all past it: untouched
     assert np.array_equal(po.cpu().numpy(), want_po)  # the true sizes
+
+
+def test_wire_wrappers_reject_bad_arguments(sbd):
+    """dtype, device and length mistakes raise before anything is launched."""
+    idx = torch.arange(4, dtype=torch.int32, device="cuda")
+    off = torch.tensor([0, 4], dtype=torch.int64, device="cuda")
+    with pytest.raises(ValueError):
+        sbd.wire_encode(idx.long(), off, [10])
+    with pytest.raises(ValueError):
+        sbd.wire_encode(idx, off.cpu(), [10])
+    with pytest.raises(ValueError):
+        sbd.wire_encode(idx, off, [10, 20])
+    pos, po = sbd.wire_encode(idx, off, [10])
+    with pytest.raises(ValueError):
+        sbd.wire_decode(pos.view(torch.int8), po, off, [10])
+    with pytest.raises(ValueError):
+        sbd.wire_decode(pos, po.int(), off, [10])
+    with pytest.raises(ValueError):
+        sbd.wire_decode(pos, po, off.cpu(), [10])
+    assert torch.equal(sbd.wire_decode(pos, po, off, [10]), idx)
