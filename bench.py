@@ -91,6 +91,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU-time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--torch-cpu-seconds", type=float, default=5.0,
+                    help="time budget of the second CPU point: the sources' own torch-CPU "
+                         "formulation on every host core (0 skips it)")
     ap.add_argument("--wire", action="store_true",
                     help="time the wire encoding of the list's delta: positions block encode, "
                          "decode and the flush hashes")
@@ -324,6 +327,8 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, cfg, olds, news, dplan, nnz_total)
+        if args.torch_cpu_seconds > 0:
+            result["cpu_torch"] = cpu_torch_formulation(args, olds, news, dplan)
     print(json.dumps(result), flush=True)
 
 
@@ -923,6 +928,52 @@ def cpu_baseline(args, cfg, olds, news, dplan, nnz_total):
                       "(diff, apply, xor_mask, xor_apply) per tensor, single-threaded C",
             "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
             "sample_parity_identical": identical}
+
+
+def cpu_torch_formulation(args, olds, news, dplan):
+    """A second, labelled CPU point: the sources' own torch formulation (verl
+    review, `shard_delta_indices`: an int16 view compare, nonzero and a
+    gather; TRL article section 4.3: `snap[idx] = val`; XOR summary: mask and
+    apply by XOR), with torch's intra-op threads on every host core, timed on
+    whole tensors in list order until the budget is used.  Device-to-host
+    copies are outside the timed region; the sample's deltas are compared with
+    the GPU's."""
+    import torch
+
+    threads = torch.get_num_threads()
+    offs_dev = dplan.offsets.cpu().tolist()
+    done_bytes, spent, tensors, elems, identical = 0, 0.0, 0, 0, True
+    for p, (o_t, n_t) in enumerate(zip(olds, news)):
+        if spent >= args.torch_cpu_seconds:
+            break
+        o = o_t.detach().reshape(-1).view(torch.int16).cpu()
+        x = n_t.detach().reshape(-1).view(torch.int16).cpu()
+        t0 = time.perf_counter()
+        idx = (x != o).nonzero().squeeze(1)
+        val = x[idx]
+        snap = o.clone()
+        snap[idx] = val
+        mask = o ^ x
+        snap2 = o.clone()
+        snap2 ^= mask
+        spent += time.perf_counter() - t0
+        done_bytes += 2 * o.numel()
+        tensors += 1
+        elems += o.numel()
+        a, b = offs_dev[p], offs_dev[p + 1]
+        if b <= dplan.capacity:
+            identical &= bool(torch.equal(dplan.idx[a:b].cpu().long(), idx) and
+                              torch.equal(dplan.val[a:b].view(torch.int16).cpu(), val) and
+                              torch.equal(snap, x) and torch.equal(snap2, x))
+    gbs = done_bytes / spent / 1e9 if spent > 0 else None
+    log(f"[bench] cpu torch formulation: {tensors} tensors, {elems:,} elements, {spent:.1f} s, "
+        f"{threads} threads, {gbs:.3f} GB/s, matches the GPU on the sample: {identical}")
+    return {"value": round(gbs, 4) if gbs else None, "unit": "GB/s", "threads": threads,
+            "kind": "torch_cpu_formulation",
+            "sample": f"first {tensors} of {len(olds)} tensors ({elems} elements), full step "
+                      "(int16-view compare + nonzero + gather, index assignment, XOR mask, "
+                      "in-place XOR) per tensor",
+            "sample_matches_gpu": identical}
 
 
 if __name__ == "__main__":
