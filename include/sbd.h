@@ -15,8 +15,10 @@
  *    comment says (host).  The library never reads tensor data on the host.
  *  - `stream` is a hipStream_t passed as `void*` (NULL = the default
  *    stream).  Every call only enqueues work on `stream` and returns; none
- *    waits for the GPU, except the documented host-to-device copy of a
- *    parameter table in the *_many calls.
+ *    waits for the GPU except the *_streamed receivers, which return once
+ *    their last apply is done.  (The *_many calls copy their parameter table
+ *    from host memory; HIP stages that copy before the call returns, without
+ *    waiting for the stream.)
  *  - Ownership: the caller allocates and frees every buffer (outputs,
  *    counters, workspace).  The library allocates no device memory and keeps
  *    no state between calls except the calling thread's error message.
@@ -113,9 +115,10 @@ delta_status delta_diff(const uint16_t *old_bits, const uint16_t *new_bits, int6
  *                      (offsets[nparams] is the true total).  Parameter p's
  *                      entries are idx/val[offsets[p] .. offsets[p+1]).
  *  ws, ws_bytes        at least delta_workspace_size(sum(numels), nparams).
- * The parameter table (32 bytes per tensor) is copied host-to-device on
- * `stream`; HIP performs copies from pageable host memory synchronously, so
- * the host arrays may be freed as soon as the call returns.
+ * The parameter table (40 bytes per tensor) is copied host-to-device on
+ * `stream`; HIP has staged a copy from pageable host memory by the time the
+ * call returns (without waiting for the stream), so the host arrays may be
+ * freed as soon as the call returns.
  */
 delta_status delta_diff_many(int32_t nparams, const uint16_t *const *old_ptrs,
                              const uint16_t *const *new_ptrs, const int64_t *numels,
