@@ -11,9 +11,9 @@
 // How, on gfx950: three phases in five short launches, and no workgroup ever
 // waits for another one.
 //  1. Count and stage.  One workgroup of 512 lanes (eight wave64s) per tile
-//     of 32768 elements; a tile never straddles a parameter.  A lane issues
-//     eight 16-byte loads of `old` and eight of `new` up front, so a CU keeps
-//     hundreds of KB of reads in flight.  Per 16-byte chunk the lane forms an
+//     of 32768 elements; a tile never straddles a parameter.  A lane loads
+//     eight 16-byte chunks of `old` and eight of `new`; three such workgroups
+//     share a CU.  Per 16-byte chunk the lane forms an
 //     8-bit change mask; its popcount is prefix-summed across the wave with
 //     four ballots over its bits plus mbcnt, and the 64 (iteration, wave)
 //     group totals are scanned in LDS, giving every change its slot inside
