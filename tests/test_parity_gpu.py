@@ -567,6 +567,42 @@ def test_apply_many_matches_oracle(sbd, oracle_mod, frac):
         assert np.array_equal(np_bits(s), w)
 
 
+def test_apply_many_max_nnz_cuts_the_delta(sbd, oracle_mod):
+    """Only entries j < min(offsets[nparams], max_nnz) are applied: cut at zero,
+    inside the first chunk, inside a parameter, on a parameter boundary, one
+    short of the total and past it; the oracle applies the same prefix."""
+    olds, news = _param_list(21, MANY_SIZES, 0.3)
+    ri, rv, rn, ro = oracle_mod.diff_many(olds, news)
+    total = int(ro[-1])
+    boundary = int(ro[len(olds) // 2])
+    gi = torch.from_numpy(ri).cuda()
+    gv = torch.from_numpy(rv.view(np.int16)).cuda().view(torch.bfloat16)
+    go = torch.from_numpy(ro).cuda()
+    for cut in sorted({0, 1, 777, boundary, boundary + 1, total // 2 + 3, total - 1, total,
+                       total + 5000}):
+        want = []
+        for p, o in enumerate(olds):
+            w = o.copy()
+            a, b = int(ro[p]), min(int(ro[p + 1]), cut)
+            if b > a:
+                oracle_mod.apply_(w, ri[a:b], rv[a:b])
+            want.append(w)
+        snaps = [gpu_bits(o) for o in olds]
+        sbd.apply_many_(snaps, gi, gv, go, max_nnz=cut, check_indices=True)
+        for s, w in zip(snaps, want):
+            assert np.array_equal(np_bits(s), w), cut
+        # a plan given a prefix of the delta and an unbounded max_nnz applies
+        # exactly that prefix (it never reads past the buffers)
+        from sparse_bf16_delta_amd.plan import ApplyPlan
+
+        k = min(cut, total)
+        snaps = [gpu_bits(o) for o in olds]
+        ApplyPlan(snaps).run(gi[:k], gv[:k], go, max_nnz=1 << 40)
+        torch.cuda.synchronize()
+        for s, w in zip(snaps, want):
+            assert np.array_equal(np_bits(s), w), ("plan", cut)
+
+
 @pytest.mark.parametrize("frac", [0.05, 0.5, 1.0])
 def test_apply_many_adjacent_unaligned_params(sbd, oracle_mod, frac):
     """Parameters packed back to back at odd element offsets share 64- and
