@@ -746,6 +746,21 @@ def test_xor_mask_may_alias_new(sbd, oracle_mod):
     assert np.array_equal(np_bits(g_n), want)
 
 
+def test_aliased_inputs(sbd, oracle_mod):
+    """old and new may be the very same buffer (an empty delta, also in a
+    list), and the mask may overwrite old as well as new."""
+    old, new = rand_case(78, 3 * TILE + 5, 0.1)
+    g = gpu_bits(old)
+    gi, gv = sbd.diff(g, g)
+    assert gi.numel() == 0 and gv.numel() == 0
+    gi, gv, nnz, offs = sbd.diff_many([g, g[:TILE + 3]], [g, g[:TILE + 3]])
+    assert gi.numel() == 0 and int(offs[-1].item()) == 0 and int(nnz.sum().item()) == 0
+    want = oracle_mod.xor_mask(old, new)
+    g_o, g_n = gpu_bits(old), gpu_bits(new)
+    sbd.xor_mask(g_o, g_n, out=g_o)
+    assert np.array_equal(np_bits(g_o), want)
+
+
 def test_c1_single_tensor_roundtrip(sbd, oracle_mod):
     """1024x1024 bf16, fp32-master step at lr 3e-6: diff, apply, XOR round trip."""
     cfg = workloads.CONFIGS["tensor1m"]
