@@ -49,6 +49,8 @@
 //    unspecified; every other position keeps its value (a rewritten segment
 //    is written back with the values read from it, and lies inside the
 //    snapshot).
+#include <atomic>
+
 #include "sbd_internal.h"
 
 namespace sbd {
@@ -478,14 +480,15 @@ constexpr int64_t kApplyGridFactor = 16;
 
 template <bool kMany, bool kSegOK>
 int64_t apply_grid_limit() {
-  static int64_t cached[64] = {0};
+  static std::atomic<int64_t> cached[64];  // zero-initialised; threads may race to fill it
   constexpr int64_t kFallback = 256 * 8 * kApplyGridFactor;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
     (void)hipGetLastError();
     return kFallback;
   }
-  if (cached[dev] == 0) {
+  int64_t lim = cached[dev].load(std::memory_order_relaxed);
+  if (lim == 0) {
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, apply_kernel<kMany, kSegOK>,
                                                      kApplyBlock, 0) != hipSuccess ||
@@ -494,9 +497,10 @@ int64_t apply_grid_limit() {
       (void)hipGetLastError();
       return kFallback;
     }
-    cached[dev] = int64_t(per_cu) * cus * kApplyGridFactor;
+    lim = int64_t(per_cu) * cus * kApplyGridFactor;
+    cached[dev].store(lim, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return lim;
 }
 
 template <bool kMany, bool kSegOK>

@@ -45,6 +45,8 @@
 // and 4 read per changed element, a dense tile re-reads `new` (2 bytes per
 // element), and the tile count, prefix, position and descriptor add about 60
 // bytes per tile.
+#include <atomic>
+
 #include "sbd_internal.h"
 
 namespace sbd {
@@ -581,10 +583,14 @@ __global__ __launch_bounds__(kDiffBlock) void diff_dense_kernel(
 // dense tiles, so a larger grid would leave a tail.  Queried once per device.
 template <bool kMany, typename IdxT>
 int64_t dense_grid_limit() {
-  static int64_t cached[64] = {0};
+  static std::atomic<int64_t> cached[64];  // zero-initialised; threads may race to fill it
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int64_t lim = cached[dev].load(std::memory_order_relaxed);
+  if (lim == 0) {
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, diff_dense_kernel<kMany, IdxT>,
                                                      kDiffBlock, 0) != hipSuccess ||
@@ -593,9 +599,10 @@ int64_t dense_grid_limit() {
       (void)hipGetLastError();
       return 256;
     }
-    cached[dev] = int64_t(per_cu) * cus;
+    lim = int64_t(per_cu) * cus;
+    cached[dev].store(lim, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return lim;
 }
 
 }  // namespace
