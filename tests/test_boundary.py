@@ -124,6 +124,36 @@ def test_argument_errors_return_before_any_launch():
     assert lib.xor_apply(None, one, 5, None) == _abi.DELTA_E_INVALID
 
 
+def test_error_message_is_per_thread():
+    """delta_last_error describes the calling thread's last failure: threads
+    failing at the same time with different arguments (ctypes releases the
+    GIL during each call) each read back their own message."""
+    import threading
+
+    lib = _abi.load()
+    one = ctypes.c_void_p(16)  # never dereferenced: every call is rejected first
+    barrier = threading.Barrier(4)
+    bad = []
+
+    def worker(k):
+        n = -(1000 + k)
+        barrier.wait()
+        for _ in range(2000):
+            if lib.delta_diff(one, one, n, one, one, 0, one, one, 1 << 20, None) != _abi.DELTA_E_INVALID:
+                bad.append((k, "status"))
+                return
+            if f"n={n}" not in lib.delta_last_error().decode():
+                bad.append((k, lib.delta_last_error().decode()))
+                return
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad
+
+
 def test_python_layer_rejects_bad_tensors():
     cpu = torch.zeros(8, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
