@@ -685,6 +685,51 @@ def test_two_streams_at_once(sbd, oracle_mod):
             assert np.array_equal(np_bits(s_), x)
 
 
+def test_two_host_threads(sbd, oracle_mod):
+    """Two host threads, each with its own stream (and so its own cached
+    workspace), diff and apply their own parameter lists at the same time --
+    the library calls run without the GIL -- five rounds each, every round
+    against the oracle."""
+    import threading
+
+    cases = []
+    for seed, frac in ((71, 0.03), (72, 0.2)):
+        olds, news = _param_list(seed, MANY_SIZES + [5 * TILE + 9], frac)
+        cases.append((olds, news, oracle_mod.diff_many(olds, news)))
+    errors = []
+    barrier = threading.Barrier(2)
+
+    def worker(k):
+        try:
+            olds, news, (ri, rv, rn, ro) = cases[k]
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                g_n = [gpu_bits(x) for x in news]
+                barrier.wait(timeout=60)
+                for r in range(5):
+                    g_o = [gpu_bits(o) for o in olds]
+                    gi, gv, gn, go = sbd.diff_many(g_o, g_n)
+                    sbd.apply_many_(g_o, gi, gv, go)
+                    st.synchronize()
+                    ok = (np.array_equal(go.cpu().numpy(), ro)
+                          and np.array_equal(gi.cpu().numpy(), ri)
+                          and np.array_equal(np_bits(gv), rv)
+                          and all(np.array_equal(np_bits(s_), x) for s_, x in zip(g_o, news)))
+                    if not ok:
+                        errors.append((k, r))
+                        return
+        except Exception as e:  # reported by the main thread
+            errors.append((k, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors
+
+
 def test_diff_many_then_apply_many_without_host_sync(sbd):
     """The receiver can follow the sender on one stream: apply_many reads the
     device offsets written by diff_many; the result equals `new` bitwise."""
