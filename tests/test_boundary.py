@@ -182,3 +182,20 @@ def test_product_path_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
     assert "oracle" not in open(HEADER).read().lower()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 (or a launcher's WORLD_SIZE
+    above 1) exits with a message before touching a device."""
+    import subprocess
+    import sys
+
+    env = dict(os.environ)
+    env.pop("WORLD_SIZE", None)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, env=env)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+    env["WORLD_SIZE"] = "8"
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")],
+                       capture_output=True, text=True, timeout=120, env=env)
+    assert r.returncode == 2 and "WORLD_SIZE=8" in r.stderr
