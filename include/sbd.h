@@ -119,6 +119,11 @@ delta_status delta_diff(const uint16_t *old_bits, const uint16_t *new_bits, int6
  * `stream`; HIP has staged a copy from pageable host memory by the time the
  * call returns (without waiting for the stream), so the host arrays may be
  * freed as soon as the call returns.
+ * Errors: DELTA_E_INVALID (nparams < 0, capacity < 0, a null array or
+ * output, a negative numel, a null tensor pointer with numel > 0),
+ * DELTA_E_RANGE (a numel above 2^31-1, or more than 2^23 tiles of 32768
+ * elements -- about 2^38 elements -- in one call), DELTA_E_WORKSPACE (too
+ * small or not 256-byte aligned), DELTA_E_HIP.
  */
 delta_status delta_diff_many(int32_t nparams, const uint16_t *const *old_ptrs,
                              const uint16_t *const *new_ptrs, const int64_t *numels,
