@@ -100,6 +100,13 @@ def test_argument_errors_return_before_any_launch():
                                None) == _abi.DELTA_E_INVALID
     assert lib.delta_diff_many(2, ptrs, ptrs, ok2, one, one, 10, one, one, one, 64,
                                None) == _abi.DELTA_E_WORKSPACE
+    # more than 2^23 tiles of 32768 elements in one call
+    k = 129
+    kp = (ctypes.c_void_p * k)(*([16] * k))
+    kn = (ctypes.c_int64 * k)(*([(1 << 31) - 1] * k))
+    assert lib.delta_diff_many(k, kp, kp, kn, one, one, 10, one, one, one, 1 << 40,
+                               None) == _abi.DELTA_E_RANGE
+    assert "tiles" in _err(lib)
     assert lib.delta_apply(one, -1, one, one, 3, None, None) == _abi.DELTA_E_INVALID
     assert lib.delta_apply(one, 1 << 31, one, one, 3, None, None) == _abi.DELTA_E_RANGE
     assert lib.delta_apply(None, 10, one, one, 3, None, None) == _abi.DELTA_E_INVALID
