@@ -200,7 +200,14 @@ delta_status delta_apply(uint16_t *snapshot, int64_t n, const int32_t *idx,
  *                      not apply a truncated delta (check the total first).
  *  violations          optional device int64[1], as in delta_apply.
  *  ws, ws_bytes        at least delta_workspace_size(0, nparams) bytes.
- * The snapshot table is copied host-to-device as in delta_diff_many.
+ * The snapshot table is copied host-to-device as in delta_diff_many.  The
+ * launch is bounded by the workgroups the GPU holds at once, and each stops
+ * at the true total, so a max_nnz far above it (a buffer's capacity) costs
+ * no idle work.
+ * Errors: DELTA_E_INVALID (nparams < 0, max_nnz < 0, a null array or pointer
+ * when there are entries to apply, a negative numel, a null snapshot with
+ * numel > 0), DELTA_E_RANGE (a numel above 2^31-1), DELTA_E_WORKSPACE (too
+ * small or not 256-byte aligned), DELTA_E_HIP.
  */
 delta_status delta_apply_many(int32_t nparams, uint16_t *const *snap_ptrs,
                               const int64_t *numels, const int32_t *idx,
