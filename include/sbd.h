@@ -176,14 +176,26 @@ delta_status delta_diff_many_sharded(int32_t nparams, const uint16_t *const *old
  *                      at those entries' positions are unspecified; no other
  *                      position, and nothing outside the snapshot, changes.
  *  nnz                 (host) entry count.
- *  violations          optional device int64[1] (NULL to skip): receives the
- *                      number of entries that are out of range or not
- *                      strictly above their predecessor.  Diagnostic only.
- * Errors: DELTA_E_INVALID, DELTA_E_RANGE (n > 2^31-1), DELTA_E_HIP.
+ * Errors: DELTA_E_INVALID (n < 0, nnz < 0, a null pointer with nnz > 0),
+ * DELTA_E_RANGE (n > 2^31-1), DELTA_E_HIP.
  */
 delta_status delta_apply(uint16_t *snapshot, int64_t n, const int32_t *idx,
-                         const uint16_t *val, int64_t nnz, int64_t *violations,
-                         void *stream);
+                         const uint16_t *val, int64_t nnz, void *stream);
+
+/*
+ * delta_apply_checked -- delta_apply plus the optional validation of the
+ * index precondition (strictly ascending, inside [0, n)), done by the same
+ * kernels while they apply.
+ *  violations          device int64[1] (required): receives the number of
+ *                      entries that are out of range or not strictly above
+ *                      their predecessor.  Diagnostic: the caller reads it
+ *                      after the stream has passed the call.
+ * Arguments and errors otherwise as delta_apply, plus DELTA_E_INVALID for a
+ * null `violations`.
+ */
+delta_status delta_apply_checked(uint16_t *snapshot, int64_t n, const int32_t *idx,
+                                 const uint16_t *val, int64_t nnz, int64_t *violations,
+                                 void *stream);
 
 /*
  * delta_apply_many -- delta_apply over a parameter list in one launch, the
@@ -198,7 +210,8 @@ delta_status delta_apply(uint16_t *snapshot, int64_t n, const int32_t *idx,
  *  max_nnz             (host) capacity of idx/val: entries j < min(
  *                      offsets[nparams], max_nnz) are applied.  The caller must
  *                      not apply a truncated delta (check the total first).
- *  violations          optional device int64[1], as in delta_apply.
+ *  violations          optional device int64[1] (NULL to skip), as in
+ *                      delta_apply_checked.
  *  ws, ws_bytes        at least delta_workspace_size(0, nparams) bytes.
  * The snapshot table is copied host-to-device as in delta_diff_many.  The
  * launch is bounded by the workgroups the GPU holds at once, and each stops
@@ -314,7 +327,8 @@ delta_status delta_apply_streamed(int32_t nparams, uint16_t *const *snap_ptrs,
  *  offsets_host        (host) int64[nparams+1]: offsets[0] == 0,
  *                      non-decreasing; copied to the workspace with the table.
  *  max_nnz             entries j < min(offsets[nparams], max_nnz) are applied.
- *  violations          optional device int64[1], as in delta_apply.
+ *  violations          optional device int64[1] (NULL to skip), as in
+ *                      delta_apply_checked.
  *  ws, ws_bytes        at least delta_workspace_size(0, nparams) bytes.
  * The call only enqueues the apply: idx_host and val_host must stay valid and
  * unchanged until the stream has passed it.  Index contract as delta_apply.

@@ -48,7 +48,8 @@ SIGNATURES = {
     "delta_diff_many": (_st, [_i32, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "delta_diff_many_sharded": (_st, [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
                                       _sz, _vp]),
-    "delta_apply": (_st, [_vp, _i64, _vp, _vp, _i64, _vp, _vp]),
+    "delta_apply": (_st, [_vp, _i64, _vp, _vp, _i64, _vp]),
+    "delta_apply_checked": (_st, [_vp, _i64, _vp, _vp, _i64, _vp, _vp]),
     "delta_apply_many": (_st, [_i32, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "delta_streamed_staging_size": (_sz, [_i32, _i32, _i32, _i64]),
     "delta_apply_streamed": (_st, [_i32, _vp, _vp, _i32, _vp, _vp, _sz, _vp, _vp]),

@@ -205,20 +205,40 @@ delta_status delta_diff_many_sharded(int32_t nparams, const uint16_t* const* old
                         flat_offsets, idx, val, capacity, nnz, offsets, ws, ws_bytes, stream);
 }
 
-delta_status delta_apply(uint16_t* snapshot, int64_t n, const int32_t* idx, const uint16_t* val,
-                         int64_t nnz, int64_t* violations, void* stream) {
+}  // extern "C"
+
+namespace {
+
+delta_status apply_one(const char* fn, uint16_t* snapshot, int64_t n, const int32_t* idx,
+                       const uint16_t* val, int64_t nnz, int64_t* violations, void* stream) {
   if (n < 0 || nnz < 0)
-    return fail(DELTA_E_INVALID, "delta_apply: n=%lld nnz=%lld", (long long)n, (long long)nnz);
+    return fail(DELTA_E_INVALID, "%s: n=%lld nnz=%lld", fn, (long long)n, (long long)nnz);
   if (n > kInt32Max)
-    return fail(DELTA_E_RANGE, "delta_apply: n=%lld exceeds the int32 index range",
-                (long long)n);
+    return fail(DELTA_E_RANGE, "%s: n=%lld exceeds the int32 index range", fn, (long long)n);
   if (nnz > 0 && (snapshot == nullptr || idx == nullptr || val == nullptr))
-    return fail(DELTA_E_INVALID, "delta_apply: null pointer with nnz=%lld", (long long)nnz);
+    return fail(DELTA_E_INVALID, "%s: null pointer with nnz=%lld", fn, (long long)nnz);
   sbd::SnapParam single{snapshot, n};
   g_error.clear();
-  return hip_status(sbd::launch_apply(nullptr, single, 1, nullptr, idx, val, nnz, violations,
+  return hip_status(sbd::launch_apply(nullptr, single, 1, nullptr, idx, val, nnz, n, violations,
                                       static_cast<hipStream_t>(stream)),
-                    "delta_apply launch");
+                    fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+delta_status delta_apply(uint16_t* snapshot, int64_t n, const int32_t* idx, const uint16_t* val,
+                         int64_t nnz, void* stream) {
+  return apply_one("delta_apply", snapshot, n, idx, val, nnz, nullptr, stream);
+}
+
+delta_status delta_apply_checked(uint16_t* snapshot, int64_t n, const int32_t* idx,
+                                 const uint16_t* val, int64_t nnz, int64_t* violations,
+                                 void* stream) {
+  if (violations == nullptr)
+    return fail(DELTA_E_INVALID, "delta_apply_checked: violations is null");
+  return apply_one("delta_apply_checked", snapshot, n, idx, val, nnz, violations, stream);
 }
 
 delta_status delta_apply_many(int32_t nparams, uint16_t* const* snap_ptrs, const int64_t* numels,
@@ -231,13 +251,14 @@ delta_status delta_apply_many(int32_t nparams, uint16_t* const* snap_ptrs, const
   if (nparams == 0 || max_nnz == 0) {
     g_error.clear();
     return hip_status(sbd::launch_apply(nullptr, sbd::SnapParam{nullptr, 0}, 0, nullptr, nullptr,
-                                        nullptr, 0, violations, static_cast<hipStream_t>(stream)),
+                                        nullptr, 0, 0, violations, static_cast<hipStream_t>(stream)),
                       "delta_apply_many launch");
   }
   if (snap_ptrs == nullptr || numels == nullptr || offsets == nullptr || idx == nullptr ||
       val == nullptr)
     return fail(DELTA_E_INVALID, "delta_apply_many: null pointer argument");
   std::vector<sbd::SnapParam> table(static_cast<size_t>(nparams));
+  int64_t total_elems = 0;
   for (int32_t p = 0; p < nparams; ++p) {
     const int64_t n = numels[p];
     if (n < 0)
@@ -249,6 +270,7 @@ delta_status delta_apply_many(int32_t nparams, uint16_t* const* snap_ptrs, const
     if (n > 0 && snap_ptrs[p] == nullptr)
       return fail(DELTA_E_INVALID, "delta_apply_many: null snapshot for parameter %d", p);
     table[p] = sbd::SnapParam{snap_ptrs[p], n};
+    total_elems += n;
   }
   const size_t need = 256 + align256(sizeof(sbd::SnapParam) * size_t(nparams));
   if (ws == nullptr || ws_bytes < need)
@@ -263,7 +285,7 @@ delta_status delta_apply_many(int32_t nparams, uint16_t* const* snap_ptrs, const
   if (e != hipSuccess) return hip_status(e, "delta_apply_many table copy");
   g_error.clear();
   return hip_status(sbd::launch_apply(d_table, sbd::SnapParam{nullptr, 0}, nparams, offsets, idx,
-                                      val, max_nnz, violations, s),
+                                      val, max_nnz, total_elems, violations, s),
                     "delta_apply_many launch");
 }
 

@@ -6,44 +6,57 @@
 // snapshot[idx[j]] = val[j] for every entry j.  In the batched form, entry j
 // belongs to the parameter p with offsets[p] <= j < offsets[p+1].
 //
-// How, on gfx950:
-//  * The entries are taken in chunks of 2048 consecutive ones.  A workgroup
-//    applies one chunk at a time, striding over the chunks of a bounded grid
-//    (kApplyGridFactor below); a lane loads 8 entries as two 16-byte idx
-//    loads and one 16-byte val load, so the delta is read once, coalesced.
-//  * The memory system handles a 2-byte store to a line of HBM as a masked
-//    write of its 32-byte sector; a sector written whole, or better a 64-byte
-//    segment, costs it less.  So a chunk whose entries are well formed
-//    (one parameter, all in range, strictly ascending) may rewrite the
-//    segments strictly inside its span whole.  A "segment" is an aligned
-//    64-byte unit of memory (32 bf16), whatever the snapshot's alignment.
-//    How depends on the entries per element of span:
-//      - sparse (more than kMergeSpread elements per entry, about 4 %
-//        density or less), and only when the whole delta has at least
-//        kSegMinTotal entries: the workgroup lists the segments its entries
-//        touch (a scan in LDS); four lanes read, patch and write back each
-//        listed segment, 16 bytes each, nontemporal.  A smaller delta keeps
-//        2-byte stores: its touched segments fit in or near the 256 MB
-//        memory-side cache, which absorbs masked stores (measured at
-//        2^28-2^30 elements and 0.3-1 % density: 1-3x faster than the
-//        rewrite); at the 79 million entries of a 7B-shaped step the rewrite
-//        is 8 % faster;
-//      - dense (kMergeMinSpread to kMergeSpread elements per entry, about
-//        4 % to 33 %): nearly every segment is touched, so the workgroup
-//        reads its whole span into LDS in 8192-element windows, patches it
-//        from its entries (held in registers) and writes it back;
-//      - denser still (runs that cover whole segments): 2-byte stores, which
-//        already merge into full lines in L2 without reading the snapshot.
-//    The first and the last touched segment, which a neighbouring chunk
-//    (applied by another workgroup, possibly at the same time) may share,
-//    are always written with 2-byte stores, as is every entry of a chunk
-//    that breaks the precondition or spans parameters.
+// How, on gfx950.  The memory system handles a 2-byte store to HBM as a
+// masked write of its 32-byte sector; a sector written whole, or better a
+// 64-byte segment, costs it less.  So a chunk of entries that is well formed
+// (one parameter, all in range, strictly ascending) may rewrite the segments
+// strictly inside its span whole.  A "segment" is an aligned 64-byte unit of
+// memory (32 bf16), whatever the snapshot's alignment.  The first and the
+// last touched segment of a chunk, which a neighbouring chunk (applied by
+// another workgroup, possibly at the same time) may share, are always written
+// with 2-byte stores, as is every entry of a chunk that breaks the
+// precondition or spans parameters.  How the interior is written depends on
+// the elements of span per entry:
+//   - sparse (more than kMergeSpread elements per entry, about 4 % density or
+//     less): read, patch and write back each touched segment (the segment
+//     rewrite), but only for deltas of at least kSegMinTotal entries.  A
+//     smaller delta's touched segments fit in or near the 256 MB memory-side
+//     cache, which absorbs masked stores (measured at 2^28-2^30 elements and
+//     0.3-1 % density: 2-byte stores 1-3x faster than the rewrite);
+//   - dense (kMergeMinSpread to kMergeSpread elements per entry, about 4 % to
+//     33 %): nearly every segment is touched, so the workgroup reads its
+//     whole span into LDS in 8192-element windows, patches it from its
+//     entries (held in registers) and writes it back;
+//   - denser still (runs that cover whole segments): 2-byte stores, which
+//     already merge into full lines in L2 without reading the snapshot.
+//
+// Two kernels share these rules:
+//  * apply_kernel (deltas below kSegMinTotal entries): 256-lane workgroups,
+//    chunks of 2048 entries (8 per lane, two 16-byte idx loads and one
+//    16-byte val load), a grid bounded at kApplyGridFactor times the
+//    workgroups the GPU holds at once, striding over the chunks; scatter and
+//    windows only.
+//  * apply_big_kernel (larger deltas): 1024-lane workgroups, chunks of 1024
+//    entries (one per lane), one chunk per workgroup in dispatch order.  The
+//    segment rewrite's cost is set by how HBM sees the reads and writes, and
+//    it is lowest when the workgroups in flight cover one narrow, advancing
+//    band of the snapshot -- which the hardware dispatcher gives for free
+//    when every workgroup takes the next small chunk and exits.  Measured on
+//    the 7B-shaped delta's 66.4 million touched segments (read and rewrite
+//    of a precomputed list, nontemporal): one pass per 1024-lane workgroup,
+//    4 lanes per segment, 2.38 ms; the same in 256- or 512-lane workgroups
+//    2.47-2.58 ms; workgroups that each walk a chunk of a few hundred
+//    segments in several passes, or a persistent grid striding over chunks,
+//    2.71-2.78 ms; 8 segments in flight per lane 3.2 ms; cached instead of
+//    nontemporal accesses 3.0 ms; 32-byte units 4.0 ms, 128-byte lines 2.73.
+//    In each touched segment four lanes read 16 bytes each, patch them from
+//    the entries (staged in LDS) and write them back; a chunk's segments
+//    (about 860 at 1.2 % density) take a few passes, two in flight per lane.
 //  * Snapshot pointers come from the parameter table in memory; they are
 //    cast to the global address space so the stores are global, not flat.
-//  * The parameter of the chunk's first entry comes from one 64-way
-//    search over the device offsets; each lane then walks forward.  The
-//    offsets are read on the GPU, so no host round trip separates diff and
-//    apply.
+//  * The parameter of the chunk's first entry comes from one 64-way search
+//    over the device offsets; the offsets are read on the GPU, so no host
+//    round trip separates diff and apply.
 //  * An index outside [0, numel) is skipped, never written.  With unsorted
 //    or repeated indices the values at those entries' positions are
 //    unspecified; every other position keeps its value (a rewritten segment
@@ -61,17 +74,34 @@ constexpr int kApplyWaves = kApplyBlock / 64;
 constexpr int kApplyPer = 8;
 constexpr int kApplyChunk = kApplyBlock * kApplyPer;  // 2048 entries per chunk
 // Elements of span per entry that choose between the ways of writing a
-// well-formed workgroup's interior segments (see above).
+// well-formed chunk's interior segments (see above).
 constexpr int64_t kMergeSpread = 24;
 constexpr int64_t kMergeMinSpread = 3;
-constexpr int kSegElems = 32;                        // bf16 per 64-byte segment
-constexpr int kSegLanes = kSegElems / kVec;          // 4 lanes x 16 bytes per segment
-constexpr int kSegGroups = kApplyBlock / kSegLanes;  // segments per workgroup pass
+constexpr int kSegElems = 32;                // bf16 per 64-byte segment
+constexpr int kSegLanes = kSegElems / kVec;  // 4 lanes x 16 bytes per segment
+constexpr int kSegGroups = kApplyBlock / kSegLanes;  // segments per apply_kernel pass
 constexpr int kSegUnroll = 4;                        // segments in flight per lane
-// Fewest delta entries for which sparse workgroups rewrite whole segments.
+// Fewest delta entries for which sparse chunks rewrite whole segments.
 constexpr int64_t kSegMinTotal = int64_t(1) << 25;
 constexpr int kMergeWindow = 8192;  // snapshot elements patched in LDS at a time
 static_assert(kMergeWindow % kSegElems == 0, "windows hold whole segments");
+
+// Large deltas: one entry per lane of a 1024-lane workgroup.
+constexpr int kBigBlock = 1024;
+constexpr int kBigWaves = kBigBlock / 64;
+constexpr int kBigChunk = kBigBlock;
+constexpr int kBigSegPass = kBigBlock / kSegLanes;  // segments rewritten per pass
+// Segments in flight per four lanes: the loads of two passes are issued
+// before the first pass is patched and written.  On the 7B-shaped delta, one
+// pass at a time 2.69 ms, two 2.60 ms, four 2.78 ms (the floor of the bare
+// read and rewrite of its touched segments, one pass per workgroup, 2.48 ms
+// on that machine).
+constexpr int kBigSegDepth = 2;
+// At most this many workgroups per launch; each strides over chunks beyond
+// it (2^17 chunks of 1024 entries: a delta of 134 million entries takes one
+// pass).  A launch whose max_nnz (a buffer's capacity) far exceeds the true
+// total therefore starts at most this many workgroups that find no work.
+constexpr int64_t kBigGridCap = int64_t(1) << 17;
 
 enum ApplyMode : int { kScatter = 0, kWindows = 1, kSegments = 2 };
 
@@ -99,6 +129,30 @@ struct ApplyShared {
   };
 };
 
+// The touched-segment list of a sparse chunk of the large-delta kernel.
+struct BigSegList {
+  uint32_t pos[kBigChunk];    // per entry: its index plus the segment shift
+  uint16_t val[kBigChunk];    // per entry: its value
+  uint16_t first[kBigChunk];  // the first entry of each listed segment
+};
+
+struct BigShared {
+  int64_t total;
+  int32_t p0;
+  int32_t one_param;
+  uint32_t wmin[kBigWaves];
+  uint32_t wmax[kBigWaves];
+  uint32_t wcnt[kBigWaves];
+  int32_t wfirst[kBigWaves];
+  int32_t wlast[kBigWaves];
+  uint32_t wsegs[kBigWaves];  // listed segments per wave
+  uint32_t last_first;        // the first entry in the last touched segment
+  union {
+    __attribute__((aligned(16))) uint16_t win[kMergeWindow];
+    __attribute__((aligned(16))) BigSegList sl;
+  };
+};
+
 __global__ __launch_bounds__(64) void zero_i64_kernel(int64_t* p) {
   if (threadIdx.x == 0) *p = 0;
 }
@@ -112,6 +166,35 @@ __device__ __forceinline__ void set_elem(u32x4& x, uint32_t k, uint32_t v) {
   x.y = q == 1u ? (x.y & keep) | put : x.y;
   x.z = q == 2u ? (x.z & keep) | put : x.z;
   x.w = q == 3u ? (x.w & keep) | put : x.w;
+}
+
+// Wave 0 of a workgroup: the delta's applicable total, the parameter of
+// entry j0 and whether the chunk [j0, j0 + chunk) stays in it, into LDS.
+template <bool kMany, typename Shared>
+__device__ __forceinline__ void chunk_head(int64_t j0, int chunk, int32_t nparams,
+                                          const int64_t* __restrict__ offsets, int64_t max_nnz,
+                                          Shared& sh) {
+  if (threadIdx.x < 64) {
+    int64_t total = max_nnz;
+    if constexpr (kMany) {
+      const int64_t t = offsets[nparams];
+      total = t < max_nnz ? t : max_nnz;
+      if (j0 < total) {
+        const int32_t lo = find_param_wave0(offsets, nparams, j0);
+        if (threadIdx.x == 0) {
+          sh.p0 = lo;
+          const int64_t end = j0 + chunk < total ? j0 + chunk : total;
+          sh.one_param = offsets[lo + 1] >= end ? 1 : 0;
+        }
+      }
+    } else {
+      if (threadIdx.x == 0) {
+        sh.p0 = 0;
+        sh.one_param = 1;
+      }
+    }
+    if (threadIdx.x == 0) sh.total = total;
+  }
 }
 
 // Applies entries [j0, j0 + kApplyChunk) of the delta.  Every lane of the
@@ -466,16 +549,231 @@ __global__ __launch_bounds__(kApplyBlock) void apply_kernel(
   }
 }
 
-// The grid is bounded by kApplyGridFactor times the workgroups the GPU holds
-// at once, queried once per device; each workgroup then strides over chunks.
-// A caller that passes its buffer's capacity as max_nnz (diff and apply in one
-// stream, no host read of the count) would otherwise launch one workgroup per
-// chunk of that capacity, most of which find no entries and exit: on the
-// 7B-shaped list at 1.2 % with a capacity of an eighth of the elements, about
-// 370,000 such workgroups took 0.1 ms.  Measured against one workgroup per
-// chunk: equal or faster on every list and density tried (up to 7 % at 8-12 %
-// density); a factor of 1 or 2 was 10-25 % slower (too little dynamic
-// balancing between chunks of different cost).
+// Applies entries [j0, j0 + kBigChunk) of a delta of at least kSegMinTotal
+// entries, one per lane; the same contract as apply_chunk.
+template <bool kMany>
+__device__ __forceinline__ bool apply_big_chunk(
+    int64_t j0, const SnapParam* __restrict__ table, const SnapParam& single, int32_t nparams,
+    const int64_t* __restrict__ offsets, const int32_t* __restrict__ idx,
+    const uint16_t* __restrict__ val, int64_t max_nnz, int64_t* __restrict__ violations,
+    BigShared& sh) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t j = j0 + tid;
+  int32_t iv = 0;
+  uint16_t vv = 0;
+  if (j < max_nnz) {
+    iv = idx[j];
+    vv = val[j];
+  }
+  chunk_head<kMany>(j0, kBigChunk, nparams, offsets, max_nnz, sh);
+  __syncthreads();
+  const int64_t total = sh.total;
+  if (j0 >= total) return true;
+  const int n_entries = total - j0 < kBigChunk ? int(total - j0) : kBigChunk;
+  const bool have = tid < n_entries;
+  int mode = kScatter;
+  uint32_t shift = 0, ufirst = 0, ulast = 0, lo_end = 0, hi_start = 0;
+  SnapParam dm = single;
+  if (sh.one_param) {
+    if constexpr (kMany) dm = table[sh.p0];
+    shift = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dm.snap) & 63u) >> 1;
+    if ((reinterpret_cast<uintptr_t>(dm.snap) & 1u) == 0) {
+      const uint32_t i = static_cast<uint32_t>(iv);
+      const bool in = have && static_cast<uint64_t>(i) < static_cast<uint64_t>(dm.numel);
+      uint32_t umin = in ? i : 0xFFFFFFFFu, umax = in ? i : 0u, cnt = in ? 1u : 0u;
+      const int32_t prev = __shfl_up(iv, 1, 64);
+      const bool sorted = !(have && lane > 0 && !(iv > prev));
+      const bool wave_sorted = __ballot(!sorted) == 0ull;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t a = static_cast<uint32_t>(__shfl_xor(static_cast<int>(umin), o, 64));
+        const uint32_t b = static_cast<uint32_t>(__shfl_xor(static_cast<int>(umax), o, 64));
+        umin = a < umin ? a : umin;
+        umax = b > umax ? b : umax;
+        cnt += static_cast<uint32_t>(__shfl_xor(static_cast<int>(cnt), o, 64));
+      }
+      if (lane == 0) {
+        sh.wmin[wave] = umin;
+        sh.wmax[wave] = umax;
+        sh.wcnt[wave] = wave_sorted ? cnt : 0xFFFFFFFFu;
+        sh.wfirst[wave] = iv;
+      }
+      const bool next_have = __shfl_down(have ? 1 : 0, 1, 64) != 0;
+      if (have && (lane == 63 || !next_have)) sh.wlast[wave] = iv;
+      __syncthreads();
+      uint32_t gmin = 0xFFFFFFFFu, gmax = 0u, gcnt = 0u;
+      bool ok = true;
+      if (lane < kBigWaves) {
+        gmin = sh.wmin[lane];
+        gmax = sh.wmax[lane];
+        gcnt = sh.wcnt[lane];
+        ok = gcnt != 0xFFFFFFFFu &&
+             (lane == 0 || lane * 64 >= n_entries || sh.wfirst[lane] > sh.wlast[lane - 1]);
+        if (!ok) gcnt = 0u;
+      }
+#pragma unroll
+      for (int o = kBigWaves / 2; o > 0; o >>= 1) {
+        const uint32_t a = static_cast<uint32_t>(__shfl_xor(static_cast<int>(gmin), o, 64));
+        const uint32_t b = static_cast<uint32_t>(__shfl_xor(static_cast<int>(gmax), o, 64));
+        gmin = a < gmin ? a : gmin;
+        gmax = b > gmax ? b : gmax;
+        gcnt += static_cast<uint32_t>(__shfl_xor(static_cast<int>(gcnt), o, 64));
+      }
+      gmin = static_cast<uint32_t>(__shfl(static_cast<int>(gmin), 0, 64));
+      gmax = static_cast<uint32_t>(__shfl(static_cast<int>(gmax), 0, 64));
+      gcnt = static_cast<uint32_t>(__shfl(static_cast<int>(gcnt), 0, 64));
+      const bool well_formed =
+          __ballot(!ok) == 0ull && gcnt == static_cast<uint32_t>(n_entries);
+      if (well_formed && gcnt > 0u) {
+        ufirst = (gmin + shift) / kSegElems;
+        ulast = (gmax + shift) / kSegElems;
+        const int64_t span = int64_t(gmax - gmin) + 1;
+        if (ulast >= ufirst + 2u) {
+          if (span > kMergeSpread * int64_t(gcnt))
+            mode = total >= kSegMinTotal ? kSegments : kScatter;
+          else if (span >= kMergeMinSpread * int64_t(gcnt))
+            mode = kWindows;
+        }
+        lo_end = (ufirst + 1u) * kSegElems - shift;
+        hi_start = ulast * kSegElems - shift;
+      }
+    }
+  }
+  int64_t bad = 0;
+  if (have) {
+    int32_t p = 0;
+    SnapParam d = single;
+    int64_t seg_start = 0;
+    if constexpr (kMany) {
+      p = sh.p0;
+      if (!sh.one_param) {
+        int64_t seg_end = offsets[p + 1];
+        while (seg_end <= j) seg_end = offsets[++p + 1];
+      }
+      seg_start = offsets[p];
+      d = table[p];
+    }
+    const uint32_t i = static_cast<uint32_t>(iv);
+    const bool in_range = static_cast<uint64_t>(i) < static_cast<uint64_t>(d.numel);
+    const bool interior = mode != kScatter && i >= lo_end && i < hi_start;
+    if (in_range && !interior) *global_ptr(d.snap + i) = vv;
+    if (violations != nullptr) {
+      int32_t prev = __shfl_up(iv, 1, 64);
+      if (lane == 0 && j > seg_start) prev = idx[j - 1];
+      bad = (!in_range || (j > seg_start && iv <= prev)) ? 1 : 0;
+    }
+  }
+  if (mode == kSegments) {
+    const uintptr_t seg0 = reinterpret_cast<uintptr_t>(dm.snap) - 2u * shift;
+    int32_t before = __shfl_up(iv, 1, 64);
+    if (lane == 0) before = wave > 0 ? sh.wlast[wave - 1] : 0;
+    const uint32_t u = (static_cast<uint32_t>(iv) + shift) / kSegElems;
+    const uint32_t pu = (static_cast<uint32_t>(before) + shift) / kSegElems;
+    const bool lead = have && (tid == 0 || u != pu);
+    const bool listed = lead && u > ufirst && u < ulast;
+    if (lead && u == ulast) sh.last_first = uint32_t(tid);
+    sh.sl.pos[tid] = static_cast<uint32_t>(iv) + shift;
+    sh.sl.val[tid] = vv;
+    const uint64_t lb = __ballot(listed);
+    if (lane == 0) sh.wsegs[wave] = static_cast<uint32_t>(__popcll(lb));
+    __syncthreads();
+    uint32_t before_w = 0u, ns = lane < kBigWaves ? sh.wsegs[lane] : 0u;
+    before_w = lane < wave ? ns : 0u;
+#pragma unroll
+    for (int o = kBigWaves / 2; o > 0; o >>= 1) {
+      before_w += static_cast<uint32_t>(__shfl_xor(static_cast<int>(before_w), o, 64));
+      ns += static_cast<uint32_t>(__shfl_xor(static_cast<int>(ns), o, 64));
+    }
+    before_w = static_cast<uint32_t>(__shfl(static_cast<int>(before_w), 0, 64));
+    ns = static_cast<uint32_t>(__shfl(static_cast<int>(ns), 0, 64));
+    const uint32_t slot = before_w + static_cast<uint32_t>(__popcll(lb & ((1ull << lane) - 1ull)));
+    if (listed) sh.sl.first[slot] = static_cast<uint16_t>(tid);
+    __syncthreads();
+    const uint32_t g = static_cast<uint32_t>(tid) / kSegLanes;
+    const uint32_t sub = static_cast<uint32_t>(tid) % kSegLanes;
+    const uint32_t last_first = sh.last_first;
+    for (uint32_t s0 = g; s0 < ns; s0 += kBigSegDepth * kBigSegPass) {
+      u32x4 x[kBigSegDepth];
+      uintptr_t aa[kBigSegDepth];
+#pragma unroll
+      for (int k = 0; k < kBigSegDepth; ++k) {
+        const uint32_t s = s0 + k * kBigSegPass;
+        if (s < ns) {
+          const uint32_t eb = sh.sl.first[s];
+          aa[k] = seg0 + uintptr_t(sh.sl.pos[eb] / kSegElems) * 64u + sub * 16u;
+          x[k] = __builtin_nontemporal_load(global_ptr(reinterpret_cast<const u32x4*>(aa[k])));
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kBigSegDepth; ++k) {
+        const uint32_t s = s0 + k * kBigSegPass;
+        if (s < ns) {
+          const uint32_t eb = sh.sl.first[s];
+          const uint32_t ee = s + 1u < ns ? uint32_t(sh.sl.first[s + 1u]) : last_first;
+          for (uint32_t e = eb; e < ee; ++e) {
+            const uint32_t off = sh.sl.pos[e] % kSegElems;
+            if (off / kVec == sub) set_elem(x[k], off % kVec, sh.sl.val[e]);
+          }
+          __builtin_nontemporal_store(x[k], global_ptr(reinterpret_cast<u32x4*>(aa[k])));
+        }
+      }
+    }
+  }
+  if (mode == kWindows) {
+    const uint32_t i = static_cast<uint32_t>(iv);
+    for (uint32_t w0 = lo_end; w0 < hi_start; w0 += kMergeWindow) {
+      const uint32_t w1 = hi_start - w0 < uint32_t(kMergeWindow) ? hi_start : w0 + kMergeWindow;
+      for (uint32_t c = threadIdx.x; c < (w1 - w0) / kVec; c += kBigBlock) {
+        const u32x4 x = *global_ptr(reinterpret_cast<const u32x4*>(dm.snap + w0) + c);
+        *reinterpret_cast<u32x4*>(&sh.win[c * kVec]) = x;
+      }
+      __syncthreads();
+      if (have && i >= w0 && i < w1) sh.win[i - w0] = vv;
+      __syncthreads();
+      for (uint32_t c = threadIdx.x; c < (w1 - w0) / kVec; c += kBigBlock) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(&sh.win[c * kVec]);
+        *global_ptr(reinterpret_cast<u32x4*>(dm.snap + w0) + c) = x;
+      }
+      __syncthreads();
+    }
+  }
+  if (violations != nullptr) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) bad += __shfl_xor(bad, o, 64);
+    if (lane == 0 && bad != 0)
+      atomicAdd(reinterpret_cast<unsigned long long*>(violations),
+                static_cast<unsigned long long>(bad));
+  }
+  return false;
+}
+
+template <bool kMany>
+__global__ __launch_bounds__(kBigBlock) void apply_big_kernel(
+    const SnapParam* __restrict__ table, SnapParam single, int32_t nparams,
+    const int64_t* __restrict__ offsets, const int32_t* __restrict__ idx,
+    const uint16_t* __restrict__ val, int64_t max_nnz, int64_t* __restrict__ violations) {
+  __shared__ BigShared sh;
+  const int64_t nchunks = (max_nnz + kBigChunk - 1) / kBigChunk;
+  for (int64_t chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {
+    const bool past = apply_big_chunk<kMany>(chunk * kBigChunk, table, single, nparams, offsets,
+                                             idx, val, max_nnz, violations, sh);
+    __syncthreads();  // the shared state is rewritten by the next chunk
+    if (past) break;
+  }
+}
+
+// The grid of apply_kernel is bounded by kApplyGridFactor times the
+// workgroups the GPU holds at once, queried once per device; each workgroup
+// then strides over chunks.  A caller that passes its buffer's capacity as
+// max_nnz (diff and apply in one stream, no host read of the count) would
+// otherwise launch one workgroup per chunk of that capacity, most of which
+// find no entries and exit: on the 7B-shaped list at 1.2 % with a capacity of
+// an eighth of the elements, about 370,000 such workgroups took 0.1 ms.
+// Measured against one workgroup per chunk: equal or faster on every list and
+// density tried (up to 7 % at 8-12 % density); a factor of 1 or 2 was 10-25 %
+// slower (too little dynamic balancing between chunks of different cost).
 constexpr int64_t kApplyGridFactor = 16;
 
 template <bool kMany, bool kSegOK>
@@ -504,45 +802,60 @@ int64_t apply_grid_limit() {
 }
 
 template <bool kMany, bool kSegOK>
-void launch_apply_kernel(unsigned blocks, const SnapParam* d_table, const SnapParam& single,
-                         int32_t nparams, const int64_t* offsets, const int32_t* idx,
-                         const uint16_t* val, int64_t max_nnz, int64_t* violations,
-                         hipStream_t stream) {
+void launch_apply_kernel(const SnapParam* d_table, const SnapParam& single, int32_t nparams,
+                         const int64_t* offsets, const int32_t* idx, const uint16_t* val,
+                         int64_t max_nnz, int64_t* violations, hipStream_t stream) {
+  int64_t blocks = (max_nnz + kApplyChunk - 1) / kApplyChunk;
   const int64_t lim = apply_grid_limit<kMany, kSegOK>();
-  if (int64_t(blocks) > lim) blocks = static_cast<unsigned>(lim);
-  apply_kernel<kMany, kSegOK><<<dim3(blocks), dim3(kApplyBlock), 0, stream>>>(
+  if (blocks > lim) blocks = lim;
+  apply_kernel<kMany, kSegOK><<<dim3(unsigned(blocks)), dim3(kApplyBlock), 0, stream>>>(
       d_table, single, nparams, offsets, idx, val, max_nnz, violations);
+}
+
+// Which kernel: apply_big_kernel when the delta is large enough for the
+// segment rewrite and sparse enough that its chunks take it (max_nnz entries
+// over total_elems elements leave more than kMergeSpread elements per entry);
+// else apply_kernel, which also rewrites the segments of sparse chunks when
+// max_nnz allows kSegMinTotal entries (a capacity far above the true count,
+// or a dense delta).  The windows of mid-density chunks run better in 256-lane
+// workgroups issuing several loads per lane: a dense in-place read and
+// rewrite measured 6.1 TB/s in that shape against 4.0 TB/s in 1024-lane
+// workgroups with one load per lane (the Qwen3-0.6B-shaped list at 8 %:
+// 0.51 ms against 0.77 ms).
+template <bool kMany>
+void launch_apply_kernels(const SnapParam* d_table, const SnapParam& single, int32_t nparams,
+                          const int64_t* offsets, const int32_t* idx, const uint16_t* val,
+                          int64_t max_nnz, int64_t total_elems, int64_t* violations,
+                          hipStream_t stream) {
+  if (max_nnz >= kSegMinTotal && max_nnz <= total_elems / kMergeSpread) {
+    int64_t blocks = (max_nnz + kBigChunk - 1) / kBigChunk;
+    if (blocks > kBigGridCap) blocks = kBigGridCap;
+    apply_big_kernel<kMany><<<dim3(unsigned(blocks)), dim3(kBigBlock), 0, stream>>>(
+        d_table, single, nparams, offsets, idx, val, max_nnz, violations);
+  } else if (max_nnz >= kSegMinTotal) {
+    launch_apply_kernel<kMany, true>(d_table, single, nparams, offsets, idx, val, max_nnz,
+                                     violations, stream);
+  } else {
+    launch_apply_kernel<kMany, false>(d_table, single, nparams, offsets, idx, val, max_nnz,
+                                      violations, stream);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_apply(const SnapParam* d_table, const SnapParam& single, int32_t nparams,
                         const int64_t* offsets, const int32_t* idx, const uint16_t* val,
-                        int64_t max_nnz, int64_t* violations, hipStream_t stream) {
+                        int64_t max_nnz, int64_t total_elems, int64_t* violations,
+                        hipStream_t stream) {
   clear_stale_error();
   if (violations != nullptr) zero_i64_kernel<<<dim3(1), dim3(64), 0, stream>>>(violations);
   if (max_nnz > 0) {
-    int64_t blocks = (max_nnz + kApplyChunk - 1) / kApplyChunk;
-    if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
-    const unsigned b = unsigned(blocks);
-    // the segment rewrite needs a delta of kSegMinTotal entries, which only a
-    // capacity that large can hold
-    const bool seg = max_nnz >= kSegMinTotal;
-    if (d_table != nullptr) {
-      if (seg)
-        launch_apply_kernel<true, true>(b, d_table, single, nparams, offsets, idx, val, max_nnz,
-                                        violations, stream);
-      else
-        launch_apply_kernel<true, false>(b, d_table, single, nparams, offsets, idx, val, max_nnz,
-                                         violations, stream);
-    } else {
-      if (seg)
-        launch_apply_kernel<false, true>(b, nullptr, single, 1, nullptr, idx, val, max_nnz,
-                                         violations, stream);
-      else
-        launch_apply_kernel<false, false>(b, nullptr, single, 1, nullptr, idx, val, max_nnz,
-                                          violations, stream);
-    }
+    if (d_table != nullptr)
+      launch_apply_kernels<true>(d_table, single, nparams, offsets, idx, val, max_nnz,
+                                 total_elems, violations, stream);
+    else
+      launch_apply_kernels<false>(nullptr, single, 1, nullptr, idx, val, max_nnz, total_elems,
+                                  violations, stream);
   }
   return hipGetLastError();
 }

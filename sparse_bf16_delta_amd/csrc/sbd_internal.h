@@ -153,9 +153,12 @@ hipError_t launch_diff(const DiffParam* d_table, const DiffParam& single, int32_
                        int64_t capacity, int64_t* nnz, int64_t* offsets, void* ws,
                        const WsLayout& L, hipStream_t stream);
 
+// total_elems: the elements of all snapshots of the launch (the kernel is
+// chosen by the delta's size and its density bound max_nnz / total_elems).
 hipError_t launch_apply(const SnapParam* d_table, const SnapParam& single, int32_t nparams,
                         const int64_t* offsets, const int32_t* idx, const uint16_t* val,
-                        int64_t max_nnz, int64_t* violations, hipStream_t stream);
+                        int64_t max_nnz, int64_t total_elems, int64_t* violations,
+                        hipStream_t stream);
 
 // The streamed receiver (stream.hip); on failure `err` receives the message.
 size_t streamed_staging_size(int32_t nparams, int32_t nchunks, int32_t max_chunk_params,

@@ -197,11 +197,14 @@ delta_status apply_streamed_impl(int32_t nparams, uint16_t* const* snap_ptrs,
                          hipMemcpyHostToDevice, cs);
     if (e == hipSuccess) e = hipEventRecord(ev.copied[s], cs);
     if (e == hipSuccess) e = hipStreamWaitEvent(as, ev.copied[s], 0);
+    int64_t chunk_elems = 0;
+    for (int32_t q = 0; q < ch.nparams; ++q) chunk_elems += numels[ch.first_param + q];
     if (e == hipSuccess)
       e = launch_apply(d_table + ch.first_param, SnapParam{nullptr, 0}, ch.nparams,
                        d_offsets + size_t(c) * ostride,
                        reinterpret_cast<const int32_t*>(slot + L.idx),
-                       reinterpret_cast<const uint16_t*>(slot + L.val), nnz, nullptr, as);
+                       reinterpret_cast<const uint16_t*>(slot + L.val), nnz, chunk_elems,
+                       nullptr, as);
     if (e == hipSuccess) e = hipEventRecord(ev.applied[s], as);
   }
   // every copy waits on an apply, so the apply stream finishing means all done
@@ -309,6 +312,7 @@ delta_status apply_host_impl(int32_t nparams, uint16_t* const* snap_ptrs, const 
   std::vector<char> host(host_apply_workspace_size(nparams), 0);
   SnapParam* table = reinterpret_cast<SnapParam*>(host.data());
   int64_t* offs = reinterpret_cast<int64_t*>(host.data() + table_bytes);
+  int64_t total_elems = 0;
   for (int32_t p = 0; p < nparams; ++p) {
     if (numels[p] < 0 || numels[p] > 2147483647LL) {
       snprintf(buf, sizeof buf, "delta_apply_many_host: numels[%d]=%lld outside [0, 2^31-1]", p,
@@ -320,6 +324,7 @@ delta_status apply_host_impl(int32_t nparams, uint16_t* const* snap_ptrs, const 
       return fail(DELTA_E_INVALID, buf);
     }
     table[p] = SnapParam{snap_ptrs[p], numels[p]};
+    total_elems += numels[p];
   }
   int64_t total = 0;
   if (nparams > 0) {
@@ -362,7 +367,7 @@ delta_status apply_host_impl(int32_t nparams, uint16_t* const* snap_ptrs, const 
     const int64_t* d_offs =
         reinterpret_cast<const int64_t*>(static_cast<const char*>(ws) + table_bytes);
     e = launch_apply(total > 0 ? d_table : nullptr, SnapParam{nullptr, 0}, nparams, d_offs,
-                     d_idx, d_val, total, violations, s);
+                     d_idx, d_val, total, total_elems, violations, s);
   }
   if (e != hipSuccess) return fail(DELTA_E_HIP, hipGetErrorString(e));
   return DELTA_OK;

@@ -184,10 +184,15 @@ def apply_(snap: torch.Tensor, idx: torch.Tensor, val: torch.Tensor, check_indic
         raise ValueError("idx and val must have equal length on the snapshot's device")
     n = snap.numel()
     _range(n, "apply")
-    v = _violations(snap.device, check_indices)
-    check(load().delta_apply(_ptr(snap), n, _ptr(idx), _ptr(val), idx.numel(),
-                             _ptr(v) if v is not None else None, _stream(snap.device)))
-    _raise_on_violations(v)
+    lib = load()
+    if check_indices:
+        v = _violations(snap.device, True)
+        check(lib.delta_apply_checked(_ptr(snap), n, _ptr(idx), _ptr(val), idx.numel(), _ptr(v),
+                                      _stream(snap.device)))
+        _raise_on_violations(v)
+    else:
+        check(lib.delta_apply(_ptr(snap), n, _ptr(idx), _ptr(val), idx.numel(),
+                              _stream(snap.device)))
     return snap
 
 

@@ -97,7 +97,7 @@ int main() {
       return fail("delta_diff index names an unchanged position");
     if (val[j] != new_h[idx[j]]) return fail("delta_diff value is not new's pattern");
   }
-  if (delta_apply(d_snap, n, d_idx, d_val, nnz, nullptr, st) != DELTA_OK)
+  if (delta_apply(d_snap, n, d_idx, d_val, nnz, st) != DELTA_OK)
     return fail("delta_apply");
   std::vector<uint16_t> got(n);
   HIP_OK(hipMemcpyAsync(got.data(), d_snap, n * 2, hipMemcpyDeviceToHost, st));

@@ -107,9 +107,11 @@ def test_argument_errors_return_before_any_launch():
     assert lib.delta_diff_many(k, kp, kp, kn, one, one, 10, one, one, one, 1 << 40,
                                None) == _abi.DELTA_E_RANGE
     assert "tiles" in _err(lib)
-    assert lib.delta_apply(one, -1, one, one, 3, None, None) == _abi.DELTA_E_INVALID
-    assert lib.delta_apply(one, 1 << 31, one, one, 3, None, None) == _abi.DELTA_E_RANGE
-    assert lib.delta_apply(None, 10, one, one, 3, None, None) == _abi.DELTA_E_INVALID
+    assert lib.delta_apply(one, -1, one, one, 3, None) == _abi.DELTA_E_INVALID
+    assert lib.delta_apply(one, 1 << 31, one, one, 3, None) == _abi.DELTA_E_RANGE
+    assert lib.delta_apply(None, 10, one, one, 3, None) == _abi.DELTA_E_INVALID
+    assert lib.delta_apply_checked(one, 10, one, one, 3, None, None) == _abi.DELTA_E_INVALID
+    assert lib.delta_apply_checked(one, -1, one, one, 3, one, None) == _abi.DELTA_E_INVALID
     assert lib.delta_apply_many(2, ptrs, big, one, one, one, 5, None, one, 1 << 20,
                                 None) == _abi.DELTA_E_RANGE
     assert lib.delta_apply_many(2, ptrs, ok2, one, one, one, 5, None, one, 8,
@@ -206,3 +208,31 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")],
                        capture_output=True, text=True, timeout=120, env=env)
     assert r.returncode == 2 and "WORLD_SIZE=8" in r.stderr
+
+
+def _declaration(name):
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+    assert m, name
+    params = [" ".join(p.replace("*", " * ").split()) for p in m.group(1).split(",")]
+    # drop the parameter names, keep the types
+    return [p.rsplit(" ", 1)[0] if p != "void" else p for p in params]
+
+
+def test_core_signatures_are_the_boundary_contract():
+    """The core calls keep the argument lists of the boundary contract: the
+    sparse delta (int32 indices, bf16 bits, device count, workspace), the
+    in-place apply with a host entry count, and the XOR pair.  The stream is
+    a hipStream_t passed as void* so that the header needs no HIP include."""
+    u16c, u16 = "const uint16_t *", "uint16_t *"
+    assert _declaration("delta_workspace_size") == ["int64_t", "int32_t"]
+    assert _declaration("delta_diff") == [u16c, u16c, "int64_t", "int32_t *", u16, "int64_t",
+                                          "int64_t *", "void *", "size_t", "void *"]
+    assert _declaration("delta_diff_many") == [
+        "int32_t", "const uint16_t * const *", "const uint16_t * const *", "const int64_t *",
+        "int32_t *", u16, "int64_t", "int64_t *", "int64_t *", "void *", "size_t", "void *"]
+    assert _declaration("delta_apply") == [u16, "int64_t", "const int32_t *", u16c, "int64_t",
+                                           "void *"]
+    assert _declaration("xor_mask") == [u16c, u16c, u16, "int64_t", "void *"]
+    assert _declaration("xor_apply") == [u16, u16c, "int64_t", "void *"]
+    assert _declaration("delta_last_error") == ["void"]

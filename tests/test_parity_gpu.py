@@ -457,10 +457,14 @@ def test_apply_segment_rewrite_large(sbd, pad):
     assert torch.equal(buf[pad:pad + n], old)
 
 
-def test_apply_many_segment_rewrite_unaligned_params(sbd):
+@pytest.mark.parametrize("cap_factor", [1, 3])
+def test_apply_many_segment_rewrite_unaligned_params(sbd, cap_factor):
     """A list packed back to back at odd element offsets (each parameter's
     segments start at a different shift, edge segments shared with the
-    neighbours), more than 2^25 entries in all."""
+    neighbours), more than 2^25 entries in all.  With the exact count the
+    large-delta kernel applies it (one entry per lane); with a buffer three
+    times that size passed as the capacity, the density bound rules that
+    kernel out and the 2048-entry-chunk kernel rewrites the segments."""
     sizes = [(1 << 29) + 7, 5, (1 << 28) + 3, 1000, (1 << 29) - 11]
     total = sum(sizes)
     old, new = _sparse_pair(total, 21)
@@ -475,8 +479,13 @@ def test_apply_many_segment_rewrite_unaligned_params(sbd):
         counts.append(i.numel())
         pos += n
     offsets = torch.tensor([0] + list(np.cumsum(counts)), dtype=torch.int64, device="cuda")
-    assert int(offsets[-1]) >= (1 << 25)
-    sbd.apply_many_(views, torch.cat(idxs), torch.cat(vals), offsets, check_indices=True)
+    m = int(offsets[-1])
+    assert m >= (1 << 25)
+    idx = torch.full((cap_factor * m,), -1, dtype=torch.int32, device="cuda")
+    val = torch.zeros(cap_factor * m, dtype=torch.bfloat16, device="cuda")
+    idx[:m] = torch.cat(idxs)
+    val[:m] = torch.cat(vals)
+    sbd.apply_many_(views, idx, val, offsets, max_nnz=cap_factor * m, check_indices=True)
     assert torch.equal(buf[1:1 + total], new)
     assert int(buf[0]) == 7 and bool((buf[1 + total:] == 7).all())
 
