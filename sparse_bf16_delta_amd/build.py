@@ -1,4 +1,6 @@
-"""Compile libsbd.so (all HIP sources, gfx950) in-tree with hipcc."""
+"""Compile libsbd.so (all HIP sources under csrc/, gfx950) in-tree with hipcc,
+and the benchmark's memory-ceiling kernels (ceiling/) into a library of their
+own, libsbd_ceiling.so, which the delta library never links or loads."""
 from __future__ import annotations
 
 import glob
@@ -9,6 +11,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libsbd.so")
+CEILING_LIB = os.path.join(PKG, "libsbd_ceiling.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -29,14 +32,19 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
+def _compile(out, srcs, verbose):
+    tmp = out + ".tmp"
     cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-           "-o", tmp, *sources()]
+           "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    _compile(LIB, sources(), verbose)
+    _compile(CEILING_LIB, [os.path.join(PKG, "ceiling", "ceiling.hip")], verbose)
     return LIB
 
 
