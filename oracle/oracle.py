@@ -44,6 +44,12 @@ def _load():
     lib.oracle_wire_encode.restype = i64
     lib.oracle_wire_decode.argtypes = [i32, vp, vp, vp, vp, vp]
     lib.oracle_wire_decode.restype = ctypes.c_int
+    lib.oracle_wire_blocked_size.argtypes = [i32, vp, i64]
+    lib.oracle_wire_blocked_size.restype = i64
+    lib.oracle_wire_encode_blocked.argtypes = [i32, vp, vp, vp, vp]
+    lib.oracle_wire_encode_blocked.restype = i64
+    lib.oracle_wire_decode_blocked.argtypes = [i32, vp, vp, i64, vp, vp]
+    lib.oracle_wire_decode_blocked.restype = ctypes.c_int
     lib.oracle_hash_bytes.argtypes = [vp, i64]
     lib.oracle_hash_bytes.restype = ctypes.c_uint64
     lib.oracle_hash_bf16.argtypes = [vp, i64]
@@ -273,3 +279,37 @@ def hash_bf16(bits) -> int:
 def wire_checksum(positions, values_bits) -> int:
     """The flush checksum as the pages define it, on unbounded integers."""
     return hash_bytes(positions) ^ (hash_bf16(values_bits) << 1)
+
+
+def wire_blocked_size(numels, entries: int) -> int:
+    """Bytes of the blocked positions of `entries` entries over the list."""
+    nums = np.ascontiguousarray(numels, dtype=np.int64)
+    return int(_load().oracle_wire_blocked_size(nums.size, _ptr(nums), int(entries)))
+
+
+def wire_encode_blocked(idx, offsets, numels) -> np.ndarray:
+    """Blocked positions (uint8 bytes: the block tables, then 2-byte offsets)
+    of a diff_many-layout delta."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+    nums = np.ascontiguousarray(numels, dtype=np.int64)
+    size = wire_blocked_size(nums, int(offsets[-1] - offsets[0]))
+    out = np.zeros(max(size, 1), dtype=np.uint8)
+    got = _load().oracle_wire_encode_blocked(nums.size, _ptr(nums), _ptr(idx), _ptr(offsets),
+                                             _ptr(out))
+    if got < 0:
+        raise ValueError("oracle_wire_encode_blocked rejected the delta")
+    return out[:got].copy()
+
+
+def wire_decode_blocked(data, offsets, numels) -> np.ndarray:
+    """int32 parameter-local indices back from blocked positions."""
+    data = np.ascontiguousarray(data, dtype=np.uint8)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+    nums = np.ascontiguousarray(numels, dtype=np.int64)
+    idx = np.zeros(max(int(offsets[-1]), 1), dtype=np.int32)
+    rc = _load().oracle_wire_decode_blocked(nums.size, _ptr(nums), _ptr(data), data.size,
+                                            _ptr(offsets), _ptr(idx))
+    if rc != 0:
+        raise ValueError("oracle_wire_decode_blocked rejected the bytes")
+    return idx[:int(offsets[-1])]

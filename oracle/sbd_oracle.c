@@ -429,3 +429,132 @@ uint64_t oracle_hash_bf16(const uint16_t *bits, int64_t n)
     }
     return h;
 }
+
+/*
+ * Blocked positions: a 2-byte position for every parameter, whatever its size.
+ *
+ * [VERL] encode.py `DeltaParam.pos_width` sends positions at 2 or 4 bytes.
+ * A parameter of more than 65536 elements cannot use 2 bytes as such; the
+ * reading taken here (the pages do not give one) cuts its index range into
+ * blocks of 65536 elements.  A position is stored as its offset inside its
+ * block, 2 bytes little-endian; each block stores, 4 bytes little-endian, the
+ * number of the parameter's entries that lie before it (the block's base in
+ * the parameter's entry list; its base element is its number times 65536).
+ * A flush's blocked positions are one byte block: first the block tables of
+ * all parameters in list order (ceil(numel / 65536) words each), then the
+ * 2-byte offsets of all entries in entry order.  Decoding entry j of
+ * parameter p takes the last block b whose base is at most j - offsets[p]
+ * and gives 65536 * b + offset.
+ *
+ * oracle_wire_blocked_size -- the block's size in bytes for `entries`
+ * entries over the list: 4 bytes per 65536-element block plus 2 per entry.
+ */
+int64_t oracle_wire_blocked_size(int32_t nparams, const int64_t *numels, int64_t entries)
+{
+    int32_t p;
+    int64_t blocks = 0;
+    if (nparams < 0 || entries < 0)
+        return -1;
+    for (p = 0; p < nparams; ++p) {
+        if (numels[p] < 0)
+            return -1;
+        blocks += (numels[p] + 65535) / 65536;
+    }
+    return 4 * blocks + 2 * entries;
+}
+
+/*
+ * oracle_wire_encode_blocked -- writes the blocked positions of a
+ * diff_many-layout delta (parameter-local idx, offsets[nparams+1]) to `out`
+ * and returns their size, or -1 if an index is outside its parameter or
+ * not strictly above its predecessor (the delta's own invariant, which the
+ * block bases rely on).  A block's base is the count of the parameter's
+ * entries below the block's first element, found by walking the entries
+ * once in ascending order.
+ *
+ * Pins: a hand-written worked example (tests/golden/wire_blocked.txt); the
+ * bases equal numpy's searchsorted of the block starts and the offsets its
+ * '<u2' bytes of idx & 0xFFFF; oracle_wire_decode_blocked inverts it.
+ */
+int64_t oracle_wire_encode_blocked(int32_t nparams, const int64_t *numels, const int32_t *idx,
+                                   const int64_t *offsets, uint8_t *out)
+{
+    int32_t p;
+    int64_t j, total, table_bytes, t = 0;
+    if (nparams < 0)
+        return -1;
+    total = offsets[nparams] - offsets[0];
+    table_bytes = oracle_wire_blocked_size(nparams, numels, 0);
+    if (total < 0 || table_bytes < 0)
+        return -1;
+    for (p = 0; p < nparams; ++p) {
+        int64_t nb = (numels[p] + 65535) / 65536, b;
+        int64_t begin = offsets[p], end = offsets[p + 1];
+        for (j = begin; j < end; ++j) {
+            if (idx[j] < 0 || idx[j] >= numels[p] || (j > begin && idx[j] <= idx[j - 1]))
+                return -1;
+        }
+        j = begin;
+        for (b = 0; b < nb; ++b) {
+            uint32_t base;
+            while (j < end && (int64_t)idx[j] < b * 65536)
+                ++j;
+            base = (uint32_t)(j - begin);
+            out[4 * t + 0] = (uint8_t)(base);
+            out[4 * t + 1] = (uint8_t)(base >> 8);
+            out[4 * t + 2] = (uint8_t)(base >> 16);
+            out[4 * t + 3] = (uint8_t)(base >> 24);
+            ++t;
+        }
+    }
+    for (j = offsets[0]; j < offsets[nparams]; ++j) {
+        uint32_t off = (uint32_t)idx[j] & 0xFFFFu;
+        out[table_bytes + 2 * (j - offsets[0]) + 0] = (uint8_t)off;
+        out[table_bytes + 2 * (j - offsets[0]) + 1] = (uint8_t)(off >> 8);
+    }
+    return table_bytes + 2 * total;
+}
+
+/*
+ * oracle_wire_decode_blocked -- the int32 parameter-local indices back from
+ * `nbytes` bytes of blocked positions.  Returns 0, or -1 if the bytes are too
+ * few for the list's tables and entries or a table is not a non-decreasing
+ * run of bases from 0 within the parameter's entry count (the entries
+ * decoded before the fault are written; the rest of idx is left alone).
+ */
+int oracle_wire_decode_blocked(int32_t nparams, const int64_t *numels, const uint8_t *in,
+                               int64_t nbytes, const int64_t *offsets, int32_t *idx)
+{
+    int32_t p;
+    int64_t t = 0, table_bytes, total;
+    if (nparams < 0)
+        return -1;
+    total = offsets[nparams] - offsets[0];
+    table_bytes = oracle_wire_blocked_size(nparams, numels, 0);
+    if (total < 0 || table_bytes < 0 || nbytes < table_bytes + 2 * total)
+        return -1;
+    for (p = 0; p < nparams; ++p) {
+        int64_t nb = (numels[p] + 65535) / 65536, b;
+        int64_t count = offsets[p + 1] - offsets[p];
+        for (b = 0; b < nb; ++b) {
+            const uint8_t *w = in + 4 * (t + b);
+            int64_t base = (int64_t)w[0] | ((int64_t)w[1] << 8) | ((int64_t)w[2] << 16) |
+                           ((int64_t)w[3] << 24);
+            int64_t next = count, k;
+            if (b + 1 < nb) {
+                const uint8_t *x = w + 4;
+                next = (int64_t)x[0] | ((int64_t)x[1] << 8) | ((int64_t)x[2] << 16) |
+                       ((int64_t)x[3] << 24);
+            }
+            if ((b == 0 && base != 0) || base > next || next > count)
+                return -1;
+            for (k = base; k < next; ++k) {
+                int64_t j = offsets[p] + k;
+                const uint8_t *h = in + table_bytes + 2 * (j - offsets[0]);
+                idx[j] = (int32_t)(65536 * b + ((int64_t)h[0] | ((int64_t)h[1] << 8)));
+            }
+        }
+        t += nb;
+    }
+    return 0;
+}

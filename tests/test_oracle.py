@@ -516,3 +516,70 @@ def test_hash_bytes_and_checksum_match_torch(oracle_mod):
     pos2 = pos.copy()
     pos2[len(pos2) // 2] ^= 4
     assert oracle_mod.wire_checksum(pos2, rv) != oracle_mod.wire_checksum(pos, rv)
+
+
+# ----------------------------------------------------------------------------
+# blocked positions: 2 bytes per position for any parameter size
+# ----------------------------------------------------------------------------
+
+
+def test_golden_wire_blocked(oracle_mod):
+    g = read_golden("wire_blocked.txt")
+    numels = [int(x) for x in g["numels"].split(",")]
+    idx = np.array([int(x) for x in g["positions"].split(",")], dtype=np.int32)
+    offsets = np.array([int(x) for x in g["offsets"].split(",")], dtype=np.int64)
+    want = bytes.fromhex(g["bytes_hex"].replace(" ", ""))
+    assert len(want) == int(g["size"])
+    got = oracle_mod.wire_encode_blocked(idx, offsets, numels)
+    assert got.tobytes() == want
+    assert oracle_mod.wire_blocked_size(numels, idx.size) == int(g["size"])
+    assert np.array_equal(oracle_mod.wire_decode_blocked(got, offsets, numels), idx)
+
+
+def _blocked_numpy(idx, offsets, numels):
+    """The same bytes from numpy alone: each block's base by a binary search
+    of its first element in the parameter's indices, offsets as '<u2'."""
+    tables, lows = [], []
+    for p, n in enumerate(numels):
+        seg = idx[offsets[p]:offsets[p + 1]].astype(np.int64)
+        nb = (n + 65535) // 65536
+        tables.append(np.searchsorted(seg, np.arange(nb, dtype=np.int64) * 65536)
+                      .astype("<u4").tobytes())
+        lows.append((seg & 0xFFFF).astype("<u2").tobytes())
+    return np.frombuffer(b"".join(tables) + b"".join(lows), dtype=np.uint8)
+
+
+@pytest.mark.parametrize("seed,frac", [(3, 0.001), (4, 0.03), (5, 0.5), (6, 1.0)])
+def test_wire_blocked_matches_numpy_and_round_trips(oracle_mod, seed, frac):
+    rng = np.random.default_rng(seed)
+    numels = [5, 65536, 65537, 300_001, 1, 0, 3000, 131072, 65535, 200_000]
+    olds, news = zip(*[rand_bits(rng, n, frac) for n in numels])
+    ri, rv, rn, ro = oracle_diff_many_np(olds, news)
+    got = oracle_mod.wire_encode_blocked(ri, ro, numels)
+    assert np.array_equal(got, _blocked_numpy(ri, ro, numels))
+    blocks = sum((n + 65535) // 65536 for n in numels)
+    assert got.size == 4 * blocks + 2 * ri.size == oracle_mod.wire_blocked_size(numels, ri.size)
+    assert np.array_equal(oracle_mod.wire_decode_blocked(got, ro, numels), ri)
+
+
+def test_wire_blocked_rejects_bad_input(oracle_mod):
+    numels = [200_000]
+    idx = np.array([5, 70_000, 140_000], dtype=np.int32)
+    off = np.array([0, 3], dtype=np.int64)
+    good = oracle_mod.wire_encode_blocked(idx, off, numels)
+    with pytest.raises(ValueError):  # too few bytes
+        oracle_mod.wire_decode_blocked(good[:-1], off, numels)
+    bad = good.copy()
+    bad[4] = 9  # the second block's base above the entry count
+    with pytest.raises(ValueError):
+        oracle_mod.wire_decode_blocked(bad, off, numels)
+    bad = good.copy()
+    bad[0] = 1  # the first block's base must be 0
+    with pytest.raises(ValueError):
+        oracle_mod.wire_decode_blocked(bad, off, numels)
+    with pytest.raises(ValueError):  # unsorted or out-of-range indices
+        oracle_mod.wire_encode_blocked(np.array([70_000, 5], dtype=np.int32), np.array([0, 2]),
+                                       numels)
+    with pytest.raises(ValueError):
+        oracle_mod.wire_encode_blocked(np.array([200_000], dtype=np.int32), np.array([0, 1]),
+                                       numels)
