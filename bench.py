@@ -472,7 +472,13 @@ def wire_run(args, props):
     log(f"[bench] wire, {cfg.key}: {nnz:,} changed; positions block {pos.numel():,} bytes "
         f"({pos.numel() / max(nnz, 1):.3f} per entry); round trip identical: {ok}; "
         f"checksum {checksum:#x}")
-    if not ok:
+    data = sbd.wire_encode_blocked(idx, offsets, numels)
+    back_b = sbd.wire_decode_blocked(data, offsets, numels)
+    ok_b = torch.equal(back_b, idx)
+    log(f"[bench] blocked positions {data.numel():,} bytes ({data.numel() / max(nnz, 1):.3f} per "
+        f"entry, {(data.numel() + 2 * nnz) / max(nnz, 1):.3f} per change with the values); "
+        f"round trip identical: {ok_b}")
+    if not (ok and ok_b):
         print("bench.py: wire decode does not invert encode", file=sys.stderr)
         sys.exit(1)
 
@@ -505,9 +511,21 @@ def wire_run(args, props):
                                          ws.data_ptr(), ws.numel(), sh))
 
     def dec():
-        _abi.check(lib.delta_wire_decode(k, nums, pos.data_ptr(), pos_off.data_ptr(),
-                                         offsets.data_ptr(), nnz, out.data_ptr(), ws.data_ptr(),
-                                         ws.numel(), sh))
+        _abi.check(lib.delta_wire_decode(k, nums, pos.data_ptr(), pos.numel(),
+                                         pos_off.data_ptr(), offsets.data_ptr(), nnz,
+                                         out.data_ptr(), None, ws.data_ptr(), ws.numel(), sh))
+
+    data2 = torch.empty_like(data)
+
+    def enc_b():
+        _abi.check(lib.delta_wire_encode_blocked(k, nums, idx.data_ptr(), offsets.data_ptr(), nnz,
+                                                 data2.data_ptr(), data2.numel(), ws.data_ptr(),
+                                                 ws.numel(), sh))
+
+    def dec_b():
+        _abi.check(lib.delta_wire_decode_blocked(k, nums, data.data_ptr(), data.numel(),
+                                                 offsets.data_ptr(), nnz, out.data_ptr(), None,
+                                                 ws.data_ptr(), ws.numel(), sh))
 
     def hsh():
         _abi.check(lib.delta_wire_hash(pos.data_ptr(), pos.numel(), val.data_ptr(), nnz,
@@ -516,11 +534,13 @@ def wire_run(args, props):
     rows = {}
     for name, fn, b in (("encode", enc, 4 * nnz + pos.numel()),
                         ("decode", dec, pos.numel() + 4 * nnz),
-                        ("hash", hsh, pos.numel() + 2 * nnz)):
+                        ("hash", hsh, pos.numel() + 2 * nnz),
+                        ("encode_blocked", enc_b, 4 * nnz + data.numel()),
+                        ("decode_blocked", dec_b, data.numel() + 4 * nnz)):
         ms = timed(fn)
         rows[name] = {"ms": round(ms, 4), "bytes": b,
                       "frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        log(f"[bench] {name:7s} {ms:8.3f} ms  {b / (ms * 1e-3) / 1e9:8.1f} GB/s "
+        log(f"[bench] {name:14s} {ms:8.3f} ms  {b / (ms * 1e-3) / 1e9:8.1f} GB/s "
             f"({100 * rows[name]['frac']:.1f} % of peak)")
     print(json.dumps({
         "metric": "wire encoding of the delta: encode, decode and hash times",
@@ -528,7 +548,10 @@ def wire_run(args, props):
         "higher_is_better": False, "dtype": "u8", "data": "synthetic",
         "config": {"workload": f"{cfg.title}: {k} tensors, {n_model} elements, {mode} step lr "
                                f"{lr:g}"},
-        "changed": nnz, "positions_bytes": pos.numel(), "rows": rows,
+        "changed": nnz, "positions_bytes": pos.numel(), "blocked_positions_bytes": data.numel(),
+        "bytes_per_change": {"per_parameter_width": round((pos.numel() + 2 * nnz) / max(nnz, 1), 4),
+                             "blocked": round((data.numel() + 2 * nnz) / max(nnz, 1), 4)},
+        "rows": rows,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None)},
     }), flush=True)
 

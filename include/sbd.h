@@ -368,9 +368,17 @@ delta_status xor_apply_streamed(uint16_t *snapshot, const uint16_t *mask_host, i
  * checksum computed before sending and after receiving:
  * hash(positions) ^ (hash(values) << 1), where hash is torch.hash_tensor's
  * XOR of the elements widened to 64 bits (bytes zero-extended; bf16 values
- * widened to IEEE double, NaNs quiet, taken as bits).  The combination is
- * left to the caller (it exceeds 64 bits).
+ * widened to IEEE double, NaNs quiet, taken as bits).
  */
+
+/*
+ * delta_wire_positions_size -- exact bytes of the positions block of a delta
+ * whose per-parameter counts are given by offsets_host (host int64[nparams+1],
+ * e.g. delta_diff_many's offsets after the one device-to-host read).  Pure
+ * host function; -1 for bad arguments.
+ */
+int64_t delta_wire_positions_size(int32_t nparams, const int64_t *numels,
+                                  const int64_t *offsets_host);
 
 /*
  * delta_wire_encode -- positions byte block of a delta_diff_many result.
@@ -395,12 +403,22 @@ delta_status delta_wire_encode(int32_t nparams, const int64_t *numels, const int
 /*
  * delta_wire_decode -- inverse of delta_wire_encode: int32 parameter-local
  * indices (the delta_diff_many layout) for entries j < min(offsets[nparams],
- * max_entries), from the byte block and the device pos_offsets and offsets.
+ * max_entries), from the byte block and the device pos_offsets and offsets,
+ * which may come from a remote sender and are not trusted:
+ *  positions_bytes     size of the received block; no byte outside
+ *                      [0, positions_bytes) is read.
+ *  violations          optional device int64[1] (NULL to skip): receives the
+ *                      number of entries whose bytes lie outside the block or
+ *                      outside their parameter's span, plus the number of
+ *                      parameters whose span is not count x width.  Such
+ *                      entries decode to -1, which no apply writes.
+ *  idx                 room for max_entries entries.
+ * Errors: DELTA_E_INVALID, DELTA_E_RANGE, DELTA_E_WORKSPACE, DELTA_E_HIP.
  */
 delta_status delta_wire_decode(int32_t nparams, const int64_t *numels, const uint8_t *positions,
-                               const int64_t *pos_offsets, const int64_t *offsets,
-                               int64_t max_entries, int32_t *idx, void *ws, size_t ws_bytes,
-                               void *stream);
+                               int64_t positions_bytes, const int64_t *pos_offsets,
+                               const int64_t *offsets, int64_t max_entries, int32_t *idx,
+                               int64_t *violations, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * delta_wire_hash -- hashes[0] = hash of the npos position bytes, hashes[1] =
@@ -408,6 +426,70 @@ delta_status delta_wire_decode(int32_t nparams, const int64_t *numels, const uin
  */
 delta_status delta_wire_hash(const uint8_t *positions, int64_t npos, const uint16_t *values,
                              int64_t nval, uint64_t *hashes, void *stream);
+
+/*
+ * delta_wire_checksum -- the flush checksum hash(positions) ^ (hash(values)
+ * << 1), which needs 65 bits: checksum[0] receives its low 64 bits and
+ * checksum[1] its bit 64 (0 or 1); device uint64[2], overwritten.
+ */
+delta_status delta_wire_checksum(const uint8_t *positions, int64_t npos, const uint16_t *values,
+                                 int64_t nval, uint64_t *checksum, void *stream);
+
+/*
+ * Blocked positions: 2 bytes per position for a parameter of any size.
+ * [VERL] encode.py sends positions at 2 or 4 bytes; 4 bytes are the cost of
+ * every parameter above 65536 elements in the format above.  Here each
+ * parameter's index range is cut into blocks of 65536 elements; every block
+ * stores the number of the parameter's entries before it (uint32
+ * little-endian: the block's base in the entry list, its first element being
+ * its number times 65536) and every entry its offset inside its block (uint16
+ * little-endian).  The bytes are the block tables of all parameters in list
+ * order (ceil(numel / 65536) words each), then the offsets of all entries in
+ * entry order: 4 bytes per block plus 2 per entry, about 2.005 bytes per
+ * position at 1 % density.
+ */
+
+/*
+ * delta_wire_blocked_size -- bytes of the blocked positions of `entries`
+ * entries over the list.  Pure host function; -1 for bad arguments.
+ */
+int64_t delta_wire_blocked_size(int32_t nparams, const int64_t *numels, int64_t entries);
+
+/*
+ * delta_wire_encode_blocked -- blocked positions of a delta_diff_many result
+ * (idx, device offsets as delta_diff_many wrote them; entries j <
+ * min(offsets[nparams], max_entries) are encoded; the indices must ascend
+ * within each parameter, as delta_diff_many's do).
+ *  out                 device, 4-byte aligned, room for out_capacity bytes;
+ *                      nothing at or past out_capacity is written.  The
+ *                      block's size is delta_wire_blocked_size(nparams,
+ *                      numels, entries).
+ *  ws, ws_bytes        at least delta_workspace_size(0, nparams).
+ * Errors: DELTA_E_INVALID, DELTA_E_RANGE (numel > 2^31-1), DELTA_E_WORKSPACE,
+ * DELTA_E_HIP.
+ */
+delta_status delta_wire_encode_blocked(int32_t nparams, const int64_t *numels, const int32_t *idx,
+                                       const int64_t *offsets, int64_t max_entries, uint8_t *out,
+                                       int64_t out_capacity, void *ws, size_t ws_bytes,
+                                       void *stream);
+
+/*
+ * delta_wire_decode_blocked -- int32 parameter-local indices back from
+ * `in_bytes` bytes of blocked positions (device, 4-byte aligned), for entries
+ * j < min(offsets[nparams], max_entries); idx has room for max_entries.  The
+ * bytes and offsets may come from a remote sender: nothing outside
+ * [0, in_bytes) is read, an entry whose offset lies outside the bytes or
+ * whose position falls outside its parameter decodes to -1, and `violations`
+ * (optional device int64[1]) receives the count of such entries plus the
+ * number of blocks whose base is not a non-decreasing run from 0 within the
+ * parameter's count.
+ * Errors: DELTA_E_INVALID (also: fewer bytes than the list's block tables),
+ * DELTA_E_RANGE, DELTA_E_WORKSPACE, DELTA_E_HIP.
+ */
+delta_status delta_wire_decode_blocked(int32_t nparams, const int64_t *numels, const uint8_t *in,
+                                       int64_t in_bytes, const int64_t *offsets,
+                                       int64_t max_entries, int32_t *idx, int64_t *violations,
+                                       void *ws, size_t ws_bytes, void *stream);
 
 /*
  * delta_last_error -- message for the calling thread's last non-OK status

@@ -24,7 +24,9 @@ from .ops import (  # noqa: F401
     xor_mask,
     wire_checksum,
     wire_decode,
+    wire_decode_blocked,
     wire_encode,
+    wire_encode_blocked,
     wire_hashes,
 )
 from .sharding import flat_offset, shard0_piece  # noqa: F401
@@ -33,5 +35,6 @@ __all__ = [
     "DeltaError", "DeltaRangeError", "load", "diff", "diff_many", "apply_", "apply_many_",
     "xor_mask", "xor_apply_", "workspace", "workspace_size", "default_capacity",
     "shard0_piece", "flat_offset", "apply_streamed_", "xor_apply_streamed_", "apply_many_host_",
-    "wire_encode", "wire_decode", "wire_hashes", "wire_checksum",
+    "wire_encode", "wire_decode", "wire_hashes", "wire_checksum", "wire_encode_blocked",
+    "wire_decode_blocked",
 ]

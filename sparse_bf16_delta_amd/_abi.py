@@ -57,8 +57,14 @@ SIGNATURES = {
     "xor_streamed_staging_size": (_sz, [_i64]),
     "xor_apply_streamed": (_st, [_vp, _vp, _i64, _i64, _vp, _sz, _vp, _vp]),
     "delta_wire_encode": (_st, [_i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _sz, _vp]),
-    "delta_wire_decode": (_st, [_i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "delta_wire_positions_size": (_i64, [_i32, _vp, _vp]),
+    "delta_wire_decode": (_st, [_i32, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "delta_wire_hash": (_st, [_vp, _i64, _vp, _i64, _vp, _vp]),
+    "delta_wire_checksum": (_st, [_vp, _i64, _vp, _i64, _vp, _vp]),
+    "delta_wire_blocked_size": (_i64, [_i32, _vp, _i64]),
+    "delta_wire_encode_blocked": (_st, [_i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
+    "delta_wire_decode_blocked": (_st, [_i32, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _sz,
+                                        _vp]),
     "xor_mask": (_st, [_vp, _vp, _vp, _i64, _vp]),
     "xor_apply": (_st, [_vp, _vp, _i64, _vp]),
     "delta_last_error": (ctypes.c_char_p, []),

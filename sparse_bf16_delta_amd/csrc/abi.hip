@@ -43,6 +43,18 @@ bool ws_aligned(const void* ws) { return (reinterpret_cast<uintptr_t>(ws) & 255u
 
 namespace sbd {
 
+delta_status fail_with(delta_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return s;
+}
+
+void clear_last_error() { g_error.clear(); }
+
 int64_t max_tiles_for(int64_t total_elems, int32_t nparams) {
   // each parameter adds at most one partial tile
   return total_elems / kDiffTile + int64_t(nparams) + 1;
@@ -342,6 +354,11 @@ delta_status xor_apply_streamed(uint16_t* snapshot, const uint16_t* mask_host, i
 
 namespace {
 
+// Bytes per position of a parameter in the per-parameter wire format: the
+// narrowest of the two widths the pages allow (2 or 4 bytes) that holds every
+// parameter-local index.
+int wire_width(int64_t numel) { return numel <= 65536 ? 2 : 4; }
+
 // Per-parameter position widths into the workspace's table region.
 delta_status upload_widths(const char* fn, int32_t nparams, const int64_t* numels, void* ws,
                            size_t ws_bytes, hipStream_t s, int32_t** d_widths) {
@@ -352,7 +369,7 @@ delta_status upload_widths(const char* fn, int32_t nparams, const int64_t* numel
     if (numels[p] < 0 || numels[p] > kInt32Max)
       return fail(numels[p] < 0 ? DELTA_E_INVALID : DELTA_E_RANGE,
                   "%s: numels[%d]=%lld outside [0, 2^31-1]", fn, p, (long long)numels[p]);
-    widths[p] = numels[p] <= 65536 ? 2 : 4;
+    widths[p] = wire_width(numels[p]);
   }
   const sbd::WsLayout L = sbd::ws_layout(sbd::max_tiles_for(0, nparams), nparams);
   if (ws == nullptr || ws_bytes < L.total)
@@ -392,23 +409,38 @@ delta_status delta_wire_encode(int32_t nparams, const int64_t* numels, const int
 }
 
 delta_status delta_wire_decode(int32_t nparams, const int64_t* numels, const uint8_t* positions,
-                               const int64_t* pos_offsets, const int64_t* offsets,
-                               int64_t max_entries, int32_t* idx, void* ws, size_t ws_bytes,
-                               void* stream) {
-  if (max_entries < 0) return fail(DELTA_E_INVALID, "delta_wire_decode: max_entries < 0");
+                               int64_t positions_bytes, const int64_t* pos_offsets,
+                               const int64_t* offsets, int64_t max_entries, int32_t* idx,
+                               int64_t* violations, void* ws, size_t ws_bytes, void* stream) {
+  if (max_entries < 0 || positions_bytes < 0)
+    return fail(DELTA_E_INVALID, "delta_wire_decode: negative size");
   if (offsets == nullptr || pos_offsets == nullptr)
     return fail(DELTA_E_INVALID, "delta_wire_decode: null offsets");
-  if (max_entries > 0 && (idx == nullptr || positions == nullptr))
-    return fail(DELTA_E_INVALID, "delta_wire_decode: null idx or positions");
+  if (max_entries > 0 && idx == nullptr) return fail(DELTA_E_INVALID, "delta_wire_decode: null idx");
+  if (positions_bytes > 0 && positions == nullptr)
+    return fail(DELTA_E_INVALID, "delta_wire_decode: null positions");
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* d_widths = nullptr;
   const delta_status st =
       upload_widths("delta_wire_decode", nparams, numels, ws, ws_bytes, s, &d_widths);
   if (st != DELTA_OK) return st;
   g_error.clear();
-  return hip_status(sbd::launch_wire_decode(nparams, d_widths, positions, pos_offsets, offsets,
-                                            max_entries, idx, s),
+  return hip_status(sbd::launch_wire_decode(nparams, d_widths, positions, positions_bytes,
+                                            pos_offsets, offsets, max_entries, idx, violations,
+                                            s),
                     "delta_wire_decode launch");
+}
+
+int64_t delta_wire_positions_size(int32_t nparams, const int64_t* numels,
+                                  const int64_t* offsets_host) {
+  if (nparams < 0 || (nparams > 0 && (numels == nullptr || offsets_host == nullptr))) return -1;
+  int64_t bytes = 0;
+  for (int32_t p = 0; p < nparams; ++p) {
+    const int64_t count = offsets_host[p + 1] - offsets_host[p];
+    if (numels[p] < 0 || numels[p] > kInt32Max || count < 0) return -1;
+    bytes += count * wire_width(numels[p]);
+  }
+  return bytes;
 }
 
 delta_status delta_wire_hash(const uint8_t* positions, int64_t npos, const uint16_t* values,
@@ -420,6 +452,120 @@ delta_status delta_wire_hash(const uint8_t* positions, int64_t npos, const uint1
   return hip_status(sbd::launch_wire_hash(positions, npos, values, nval, hashes,
                                           static_cast<hipStream_t>(stream)),
                     "delta_wire_hash launch");
+}
+
+delta_status delta_wire_checksum(const uint8_t* positions, int64_t npos, const uint16_t* values,
+                                 int64_t nval, uint64_t* checksum, void* stream) {
+  if (npos < 0 || nval < 0) return fail(DELTA_E_INVALID, "delta_wire_checksum: negative size");
+  if (checksum == nullptr || (npos > 0 && positions == nullptr) ||
+      (nval > 0 && values == nullptr))
+    return fail(DELTA_E_INVALID, "delta_wire_checksum: null pointer");
+  g_error.clear();
+  return hip_status(sbd::launch_wire_checksum(positions, npos, values, nval, checksum,
+                                              static_cast<hipStream_t>(stream)),
+                    "delta_wire_checksum launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// The blocked-positions parameter table (size, first block) into the
+// workspace's table region; the total block count in *nblocks.  A decode
+// passes the received byte count: fewer bytes than the tables is rejected
+// before anything is copied or launched.
+delta_status upload_blocked(const char* fn, int32_t nparams, const int64_t* numels, void* ws,
+                            size_t ws_bytes, hipStream_t s, sbd::BlockedParam** d_table,
+                            int64_t* nblocks, int64_t in_bytes = -1) {
+  if (nparams < 0) return fail(DELTA_E_INVALID, "%s: nparams=%d < 0", fn, nparams);
+  if (nparams > 0 && numels == nullptr) return fail(DELTA_E_INVALID, "%s: numels is null", fn);
+  std::vector<sbd::BlockedParam> table(static_cast<size_t>(nparams > 0 ? nparams : 1));
+  int64_t t = 0;
+  for (int32_t p = 0; p < nparams; ++p) {
+    if (numels[p] < 0 || numels[p] > kInt32Max)
+      return fail(numels[p] < 0 ? DELTA_E_INVALID : DELTA_E_RANGE,
+                  "%s: numels[%d]=%lld outside [0, 2^31-1]", fn, p, (long long)numels[p]);
+    table[p] = sbd::BlockedParam{numels[p], t};
+    t += (numels[p] + sbd::kPosBlockElems - 1) / sbd::kPosBlockElems;
+  }
+  *nblocks = t;
+  if (in_bytes >= 0 && 4 * t > in_bytes)
+    return fail(DELTA_E_INVALID, "%s: %lld bytes hold less than the %lld block bases of the list",
+                fn, (long long)in_bytes, (long long)t);
+  const sbd::WsLayout L = sbd::ws_layout(sbd::max_tiles_for(0, nparams), nparams);
+  if (ws == nullptr || ws_bytes < L.total)
+    return fail(DELTA_E_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, L.total);
+  if (!ws_aligned(ws)) return fail(DELTA_E_WORKSPACE, "%s: workspace not 256-byte aligned", fn);
+  *d_table = reinterpret_cast<sbd::BlockedParam*>(static_cast<char*>(ws) + L.table);
+  if (nparams == 0) return DELTA_OK;
+  const hipError_t e = hipMemcpyAsync(*d_table, table.data(),
+                                      sizeof(sbd::BlockedParam) * size_t(nparams),
+                                      hipMemcpyHostToDevice, s);
+  return e == hipSuccess ? DELTA_OK : hip_status(e, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t delta_wire_blocked_size(int32_t nparams, const int64_t* numels, int64_t entries) {
+  if (nparams < 0 || entries < 0 || (nparams > 0 && numels == nullptr)) return -1;
+  int64_t blocks = 0;
+  for (int32_t p = 0; p < nparams; ++p) {
+    if (numels[p] < 0 || numels[p] > kInt32Max) return -1;
+    blocks += (numels[p] + sbd::kPosBlockElems - 1) / sbd::kPosBlockElems;
+  }
+  return 4 * blocks + 2 * entries;
+}
+
+delta_status delta_wire_encode_blocked(int32_t nparams, const int64_t* numels, const int32_t* idx,
+                                       const int64_t* offsets, int64_t max_entries, uint8_t* out,
+                                       int64_t out_capacity, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  if (max_entries < 0 || out_capacity < 0)
+    return fail(DELTA_E_INVALID, "delta_wire_encode_blocked: negative size");
+  if (offsets == nullptr) return fail(DELTA_E_INVALID, "delta_wire_encode_blocked: null offsets");
+  if (max_entries > 0 && idx == nullptr)
+    return fail(DELTA_E_INVALID, "delta_wire_encode_blocked: null idx");
+  if (out_capacity > 0 && out == nullptr)
+    return fail(DELTA_E_INVALID, "delta_wire_encode_blocked: null output");
+  if ((reinterpret_cast<uintptr_t>(out) & 3u) != 0)
+    return fail(DELTA_E_INVALID, "delta_wire_encode_blocked: output not 4-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  sbd::BlockedParam* d_table = nullptr;
+  int64_t nblocks = 0;
+  const delta_status st = upload_blocked("delta_wire_encode_blocked", nparams, numels, ws,
+                                         ws_bytes, s, &d_table, &nblocks);
+  if (st != DELTA_OK) return st;
+  g_error.clear();
+  return hip_status(sbd::launch_wire_encode_blocked(nparams, d_table, nblocks, idx, offsets,
+                                                    max_entries, out, out_capacity, s),
+                    "delta_wire_encode_blocked launch");
+}
+
+delta_status delta_wire_decode_blocked(int32_t nparams, const int64_t* numels, const uint8_t* in,
+                                       int64_t in_bytes, const int64_t* offsets,
+                                       int64_t max_entries, int32_t* idx, int64_t* violations,
+                                       void* ws, size_t ws_bytes, void* stream) {
+  if (max_entries < 0 || in_bytes < 0)
+    return fail(DELTA_E_INVALID, "delta_wire_decode_blocked: negative size");
+  if (offsets == nullptr) return fail(DELTA_E_INVALID, "delta_wire_decode_blocked: null offsets");
+  if (max_entries > 0 && idx == nullptr)
+    return fail(DELTA_E_INVALID, "delta_wire_decode_blocked: null idx");
+  if (in_bytes > 0 && in == nullptr)
+    return fail(DELTA_E_INVALID, "delta_wire_decode_blocked: null input");
+  if ((reinterpret_cast<uintptr_t>(in) & 3u) != 0)
+    return fail(DELTA_E_INVALID, "delta_wire_decode_blocked: input not 4-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  sbd::BlockedParam* d_table = nullptr;
+  int64_t nblocks = 0;
+  const delta_status st = upload_blocked("delta_wire_decode_blocked", nparams, numels, ws,
+                                         ws_bytes, s, &d_table, &nblocks, in_bytes);
+  if (st != DELTA_OK) return st;
+  g_error.clear();
+  return hip_status(sbd::launch_wire_decode_blocked(nparams, d_table, nblocks, in, in_bytes,
+                                                    offsets, max_entries, idx, violations, s),
+                    "delta_wire_decode_blocked launch");
 }
 
 delta_status xor_mask(const uint16_t* old_bits, const uint16_t* new_bits, uint16_t* mask,

@@ -140,6 +140,11 @@ struct WsLayout {
 WsLayout ws_layout(int64_t max_tiles, int32_t nparams);
 int64_t max_tiles_for(int64_t total_elems, int32_t nparams);
 
+// The calling thread's last-error text (abi.hip): fail_with formats it and
+// returns `s`; clear_last_error empties it.
+delta_status fail_with(delta_status s, const char* fmt, ...);
+void clear_last_error();
+
 // The runtime keeps one error per thread, set by any failed call, and a
 // launch check reads it.  Every launcher clears it before launching, so a
 // failure left by some earlier, unrelated call is not reported as its own.
@@ -186,10 +191,30 @@ hipError_t launch_wire_encode(int32_t nparams, const int32_t* widths, const int3
                               int64_t positions_capacity, int64_t* pos_offsets,
                               hipStream_t stream);
 hipError_t launch_wire_decode(int32_t nparams, const int32_t* widths, const uint8_t* positions,
-                              const int64_t* pos_offsets, const int64_t* offsets,
-                              int64_t max_entries, int32_t* idx, hipStream_t stream);
+                              int64_t positions_bytes, const int64_t* pos_offsets,
+                              const int64_t* offsets, int64_t max_entries, int32_t* idx,
+                              int64_t* violations, hipStream_t stream);
 hipError_t launch_wire_hash(const uint8_t* positions, int64_t npos, const uint16_t* values,
                             int64_t nval, uint64_t* hashes, hipStream_t stream);
+// hash, then checksum[0..1] = the 65-bit hash(positions) ^ (hash(values) << 1)
+hipError_t launch_wire_checksum(const uint8_t* positions, int64_t npos, const uint16_t* values,
+                                int64_t nval, uint64_t* checksum, hipStream_t stream);
+
+// Blocked positions: blocks of kPosBlockElems elements per parameter; the
+// device table gives each parameter's size and its first block in the flush.
+constexpr int64_t kPosBlockElems = 65536;
+struct BlockedParam {
+  int64_t numel;
+  int64_t tbase;
+};
+hipError_t launch_wire_encode_blocked(int32_t nparams, const BlockedParam* bp, int64_t nblocks,
+                                      const int32_t* idx, const int64_t* offsets,
+                                      int64_t max_entries, uint8_t* out, int64_t out_capacity,
+                                      hipStream_t stream);
+hipError_t launch_wire_decode_blocked(int32_t nparams, const BlockedParam* bp, int64_t nblocks,
+                                      const uint8_t* in, int64_t in_bytes, const int64_t* offsets,
+                                      int64_t max_entries, int32_t* idx, int64_t* violations,
+                                      hipStream_t stream);
 
 hipError_t launch_xor_mask(const uint16_t* a, const uint16_t* b, uint16_t* out, int64_t n,
                            hipStream_t stream);

@@ -59,11 +59,17 @@ __global__ __launch_bounds__(kScanThreads) void wire_offsets_kernel(
   if (tid == 0) pos_offsets[nparams] = s_carry;
 }
 
+// Encode writes a position only if all its bytes fit `positions_capacity`.
+// Decode reads one only if its bytes lie inside the block
+// (`positions_capacity` is then the block's size) and inside its parameter's
+// span [pos_offsets[p], pos_offsets[p+1]); otherwise it writes -1 (never a
+// valid index) and counts the entry in `violations` (if not null).
 template <bool kDecode>
 __global__ __launch_bounds__(kWireBlock) void wire_code_kernel(
     int32_t nparams, const int32_t* __restrict__ widths, const int64_t* __restrict__ offsets,
     const int64_t* __restrict__ pos_offsets, int64_t max_entries, int32_t* __restrict__ idx,
-    uint8_t* __restrict__ positions, int64_t positions_capacity) {
+    uint8_t* __restrict__ positions, int64_t positions_capacity,
+    unsigned long long* __restrict__ violations) {
   __shared__ int32_t s_p0;
   __shared__ int64_t s_total;
   const int64_t nchunks = (max_entries + kWireChunk - 1) / kWireChunk;
@@ -87,6 +93,8 @@ __global__ __launch_bounds__(kWireBlock) void wire_code_kernel(
       int64_t seg_end = offsets[p + 1];
       int w = widths[p];
       int64_t base = pos_offsets[p] - offsets[p] * w;  // byte of entry j is base + j * w
+      int64_t span_end = kDecode ? pos_offsets[p + 1] : 0;
+      int64_t bad = 0;
 #pragma unroll
       for (int r = 0; r < kWirePer; ++r) {
         const int64_t j = j0 + int64_t(r) * kWireBlock + threadIdx.x;
@@ -97,13 +105,21 @@ __global__ __launch_bounds__(kWireBlock) void wire_code_kernel(
             } while (seg_end <= j);
             w = widths[p];
             base = pos_offsets[p] - offsets[p] * w;
+            if constexpr (kDecode) span_end = pos_offsets[p + 1];
           }
           const int64_t at = base + j * w;
           auto half = reinterpret_cast<uint16_t*>(positions + at);
           if constexpr (kDecode) {
-            uint32_t v = *global_ptr(half);
-            if (w == 4) v |= uint32_t(*global_ptr(half + 1)) << 16;
-            idx[j] = static_cast<int32_t>(v);
+            const int64_t first = pos_offsets[p];
+            if (at >= first && at >= 0 && at + w <= span_end && at + w <= positions_capacity &&
+                (at & 1) == 0) {
+              uint32_t v = *global_ptr(half);
+              if (w == 4) v |= uint32_t(*global_ptr(half + 1)) << 16;
+              idx[j] = static_cast<int32_t>(v);
+            } else {
+              idx[j] = -1;
+              ++bad;
+            }
           } else {
             if (at + w <= positions_capacity) {
               const uint32_t v = static_cast<uint32_t>(idx[j]);
@@ -113,9 +129,35 @@ __global__ __launch_bounds__(kWireBlock) void wire_code_kernel(
           }
         }
       }
+      if (kDecode && violations != nullptr) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) bad += __shfl_xor(bad, o, 64);
+        if ((threadIdx.x & 63) == 0 && bad != 0)
+          atomicAdd(violations, static_cast<unsigned long long>(bad));
+      }
     }
     __syncthreads();  // s_p0 / s_total are rewritten by the next chunk
   }
+}
+
+// Decode's per-parameter check: the span pos_offsets[p+1] - pos_offsets[p]
+// must be the parameter's count times its width; each parameter that is not
+// adds one to `violations` (its entries are then checked one by one above).
+__global__ __launch_bounds__(256) void wire_spans_kernel(int32_t nparams,
+                                                         const int32_t* __restrict__ widths,
+                                                         const int64_t* __restrict__ offsets,
+                                                         const int64_t* __restrict__ pos_offsets,
+                                                         unsigned long long* __restrict__ violations) {
+  const int32_t p = int32_t(blockIdx.x) * 256 + int32_t(threadIdx.x);
+  if (p < nparams) {
+    const int64_t count = offsets[p + 1] - offsets[p];
+    if (count < 0 || pos_offsets[p + 1] - pos_offsets[p] != count * widths[p])
+      atomicAdd(violations, 1ull);
+  }
+}
+
+__global__ __launch_bounds__(64) void wire_zero_kernel(unsigned long long* v) {
+  if (threadIdx.x == 0) *v = 0ull;
 }
 
 // IEEE widening of a bf16 pattern to double, as bits; a NaN keeps its payload
@@ -203,6 +245,182 @@ __global__ __launch_bounds__(kWireBlock) void wire_hash_kernel(const uint8_t* __
   }
 }
 
+// The flush checksum from the two hashes, in place: checksum = hash(positions)
+// ^ (hash(values) << 1), 65 bits as two words (low 64, then bit 64).
+__global__ __launch_bounds__(64) void wire_checksum_kernel(uint64_t* hashes) {
+  if (threadIdx.x == 0) {
+    const uint64_t hp = hashes[0], hv = hashes[1];
+    hashes[0] = hp ^ (hv << 1);
+    hashes[1] = hv >> 63;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Blocked positions (2 bytes per position for any parameter size): the
+// parameter's index range is cut into blocks of kPosBlockElems elements; each
+// block stores the count of the parameter's entries before it (uint32, the
+// block's base in its entry list) and each entry its offset inside its block
+// (uint16).  Layout: the block tables of all parameters, then the offsets of
+// all entries in entry order.
+// ---------------------------------------------------------------------------
+// Largest p with bp[p].tbase <= t: the parameter holding global block t (a
+// parameter with no blocks shares its tbase with the next and is skipped).
+__device__ __forceinline__ int32_t block_param(const BlockedParam* __restrict__ bp,
+                                               int32_t nparams, int64_t t) {
+  int32_t lo = 0, hi = nparams - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (bp[mid].tbase <= t)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// One thread per block: its base, the first entry of its parameter at or
+// above the block's first element (a binary search over the ascending
+// indices), as a 4-byte word at out[4t] when it fits.
+__global__ __launch_bounds__(256) void wire_blocked_table_kernel(
+    int32_t nparams, const BlockedParam* __restrict__ bp, int64_t nblocks,
+    const int32_t* __restrict__ idx, const int64_t* __restrict__ offsets, int64_t max_entries,
+    uint8_t* __restrict__ out, int64_t out_capacity) {
+  const int64_t t0 = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  const int64_t tot = offsets[nparams] < max_entries ? offsets[nparams] : max_entries;
+  for (int64_t t = t0; t < nblocks; t += stride) {
+    const int32_t p = block_param(bp, nparams, t);
+    const int64_t b = t - bp[p].tbase;
+    const int64_t first = offsets[p];
+    int64_t lo = first, hi = offsets[p + 1] < tot ? offsets[p + 1] : tot;
+    if (hi < lo) hi = lo;
+    const int64_t target = b * kPosBlockElems;
+    while (lo < hi) {  // first entry with idx >= target
+      const int64_t mid = lo + ((hi - lo) >> 1);
+      if (int64_t(idx[mid]) < target)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    if (4 * t + 4 <= out_capacity)
+      *global_ptr(reinterpret_cast<uint32_t*>(out + 4 * t)) = static_cast<uint32_t>(lo - first);
+  }
+}
+
+// Every entry's offset inside its block, 2 bytes at out[lows + 2j].
+__global__ __launch_bounds__(256) void wire_blocked_lows_kernel(
+    int32_t nparams, const int32_t* __restrict__ idx, const int64_t* __restrict__ offsets,
+    int64_t max_entries, uint8_t* __restrict__ out, int64_t lows, int64_t out_capacity) {
+  const int64_t tot = offsets[nparams] < max_entries ? offsets[nparams] : max_entries;
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  for (int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x; j < tot; j += stride) {
+    if (lows + 2 * j + 2 <= out_capacity)
+      *global_ptr(reinterpret_cast<uint16_t*>(out + lows + 2 * j)) =
+          static_cast<uint16_t>(static_cast<uint32_t>(idx[j]) & 0xFFFFu);
+  }
+}
+
+// Decode: workgroups of kWireChunk consecutive entries as wire_code_kernel;
+// each lane keeps a (parameter, block) cursor that only moves forward, found
+// by a binary search over the parameter's bases when the parameter changes.
+// An entry whose offset lies past `in_bytes`, or whose position falls outside
+// its parameter, becomes -1 and is counted in `violations` (if not null).
+__global__ __launch_bounds__(kWireBlock) void wire_blocked_decode_kernel(
+    int32_t nparams, const BlockedParam* __restrict__ bp, int64_t nblocks,
+    const uint8_t* __restrict__ in, int64_t in_bytes, const int64_t* __restrict__ offsets,
+    int64_t max_entries, int32_t* __restrict__ idx, unsigned long long* __restrict__ violations) {
+  __shared__ int32_t s_p0;
+  __shared__ int64_t s_total;
+  const auto words = global_ptr(reinterpret_cast<const uint32_t*>(in));
+  const int64_t lows = 4 * nblocks;
+  const int64_t nchunks = (max_entries + kWireChunk - 1) / kWireChunk;
+  for (int64_t chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {
+    const int64_t j0 = chunk * kWireChunk;
+    if (threadIdx.x < 64) {
+      const int64_t t = offsets[nparams];
+      const int64_t total = t < max_entries ? t : max_entries;
+      if (j0 < total) {
+        const int32_t p0 = find_param_wave0(offsets, nparams, j0);
+        if (threadIdx.x == 0) s_p0 = p0;
+      }
+      if (threadIdx.x == 0) s_total = total;
+    }
+    __syncthreads();
+    const int64_t total = s_total;
+    if (j0 < total) {
+      int32_t p = s_p0;
+      int64_t seg_end = offsets[p + 1];
+      int64_t first = offsets[p];
+      int64_t nb = (bp[p].numel + kPosBlockElems - 1) / kPosBlockElems, tb = bp[p].tbase, b = -1;
+      int64_t bad = 0;
+#pragma unroll 4
+      for (int r = 0; r < kWirePer; ++r) {
+        const int64_t j = j0 + int64_t(r) * kWireBlock + threadIdx.x;
+        if (j < total) {
+          if (seg_end <= j) {
+            do {
+              seg_end = offsets[++p + 1];
+            } while (seg_end <= j);
+            first = offsets[p];
+            nb = (bp[p].numel + kPosBlockElems - 1) / kPosBlockElems;
+            tb = bp[p].tbase;
+            b = -1;
+          }
+          const int64_t local = j - first;
+          if (b < 0) {  // last block whose base is <= local
+            int64_t lo = 0, hi = nb - 1;
+            while (lo < hi) {
+              const int64_t mid = (lo + hi + 1) >> 1;
+              if (int64_t(words[tb + mid]) <= local)
+                lo = mid;
+              else
+                hi = mid - 1;
+            }
+            b = lo;
+          } else {
+            while (b + 1 < nb && int64_t(words[tb + b + 1]) <= local) ++b;
+          }
+          const int64_t at = lows + 2 * j;
+          int64_t v = -1;
+          if (nb > 0 && at + 2 <= in_bytes) {
+            v = b * kPosBlockElems + int64_t(*global_ptr(reinterpret_cast<const uint16_t*>(in + at)));
+            if (v >= bp[p].numel) v = -1;
+          }
+          idx[j] = static_cast<int32_t>(v);
+          bad += v < 0 ? 1 : 0;
+        }
+      }
+      if (violations != nullptr) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) bad += __shfl_xor(bad, o, 64);
+        if ((threadIdx.x & 63) == 0 && bad != 0)
+          atomicAdd(violations, static_cast<unsigned long long>(bad));
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Table check for decode: per block, the first base is 0 and bases do not
+// decrease or exceed the parameter's count; each block that breaks this adds
+// one to `violations`.
+__global__ __launch_bounds__(256) void wire_blocked_check_kernel(
+    int32_t nparams, const BlockedParam* __restrict__ bp, int64_t nblocks,
+    const uint8_t* __restrict__ in, const int64_t* __restrict__ offsets,
+    unsigned long long* __restrict__ violations) {
+  const auto words = global_ptr(reinterpret_cast<const uint32_t*>(in));
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  for (int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x; t < nblocks; t += stride) {
+    const int32_t p = block_param(bp, nparams, t);
+    const int64_t b = t - bp[p].tbase;
+    const int64_t nb = (bp[p].numel + kPosBlockElems - 1) / kPosBlockElems;
+    const int64_t count = offsets[p + 1] - offsets[p];
+    const int64_t base = words[t];
+    const int64_t next = b + 1 < nb ? int64_t(words[t + 1]) : count;
+    if ((b == 0 && base != 0) || base > next || next > count) atomicAdd(violations, 1ull);
+  }
+}
+
 unsigned code_grid(int64_t max_entries) {
   int64_t blocks = (max_entries + kWireChunk - 1) / kWireChunk;
   if (blocks < 1) blocks = 1;
@@ -222,18 +440,34 @@ hipError_t launch_wire_encode(int32_t nparams, const int32_t* widths, const int3
   if (nparams > 0 && max_entries > 0)
     wire_code_kernel<false><<<dim3(code_grid(max_entries)), dim3(kWireBlock), 0, stream>>>(
         nparams, widths, offsets, pos_offsets, max_entries, const_cast<int32_t*>(idx), positions,
-        positions_capacity);
+        positions_capacity, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_wire_decode(int32_t nparams, const int32_t* widths, const uint8_t* positions,
-                              const int64_t* pos_offsets, const int64_t* offsets,
-                              int64_t max_entries, int32_t* idx, hipStream_t stream) {
+                              int64_t positions_bytes, const int64_t* pos_offsets,
+                              const int64_t* offsets, int64_t max_entries, int32_t* idx,
+                              int64_t* violations, hipStream_t stream) {
   clear_stale_error();
+  auto v = reinterpret_cast<unsigned long long*>(violations);
+  if (v != nullptr) {
+    wire_zero_kernel<<<dim3(1), dim3(64), 0, stream>>>(v);
+    if (nparams > 0)
+      wire_spans_kernel<<<dim3(unsigned((nparams + 255) / 256)), dim3(256), 0, stream>>>(
+          nparams, widths, offsets, pos_offsets, v);
+  }
   if (nparams > 0 && max_entries > 0)
     wire_code_kernel<true><<<dim3(code_grid(max_entries)), dim3(kWireBlock), 0, stream>>>(
         nparams, widths, offsets, pos_offsets, max_entries, idx,
-        const_cast<uint8_t*>(positions), 0);
+        const_cast<uint8_t*>(positions), positions_bytes, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_wire_checksum(const uint8_t* positions, int64_t npos, const uint16_t* values,
+                                int64_t nval, uint64_t* checksum, hipStream_t stream) {
+  const hipError_t e = launch_wire_hash(positions, npos, values, nval, checksum, stream);
+  if (e != hipSuccess) return e;
+  wire_checksum_kernel<<<dim3(1), dim3(64), 0, stream>>>(checksum);
   return hipGetLastError();
 }
 
@@ -249,6 +483,52 @@ hipError_t launch_wire_hash(const uint8_t* positions, int64_t npos, const uint16
   if (blocks > 2048) blocks = 2048;
   wire_hash_kernel<<<dim3(unsigned(blocks)), dim3(kWireBlock), 0, stream>>>(positions, npos,
                                                                            values, nval, hashes);
+  return hipGetLastError();
+}
+
+}  // namespace sbd
+
+namespace sbd {
+
+hipError_t launch_wire_encode_blocked(int32_t nparams, const BlockedParam* bp, int64_t nblocks,
+                                      const int32_t* idx, const int64_t* offsets,
+                                      int64_t max_entries, uint8_t* out, int64_t out_capacity,
+                                      hipStream_t stream) {
+  clear_stale_error();
+  if (nparams <= 0) return hipSuccess;
+  if (nblocks > 0) {
+    int64_t g = (nblocks + 255) / 256;
+    if (g > 4096) g = 4096;
+    wire_blocked_table_kernel<<<dim3(unsigned(g)), dim3(256), 0, stream>>>(
+        nparams, bp, nblocks, idx, offsets, max_entries, out, out_capacity);
+  }
+  if (max_entries > 0) {
+    int64_t g = (max_entries + 255) / 256;
+    if (g > 65536) g = 65536;
+    wire_blocked_lows_kernel<<<dim3(unsigned(g)), dim3(256), 0, stream>>>(
+        nparams, idx, offsets, max_entries, out, 4 * nblocks, out_capacity);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_wire_decode_blocked(int32_t nparams, const BlockedParam* bp, int64_t nblocks,
+                                      const uint8_t* in, int64_t in_bytes, const int64_t* offsets,
+                                      int64_t max_entries, int32_t* idx, int64_t* violations,
+                                      hipStream_t stream) {
+  clear_stale_error();
+  auto v = reinterpret_cast<unsigned long long*>(violations);
+  if (v != nullptr) {
+    wire_zero_kernel<<<dim3(1), dim3(64), 0, stream>>>(v);
+    if (nparams > 0 && nblocks > 0) {
+      int64_t g = (nblocks + 255) / 256;
+      if (g > 4096) g = 4096;
+      wire_blocked_check_kernel<<<dim3(unsigned(g)), dim3(256), 0, stream>>>(nparams, bp, nblocks,
+                                                                            in, offsets, v);
+    }
+  }
+  if (nparams > 0 && max_entries > 0)
+    wire_blocked_decode_kernel<<<dim3(code_grid(max_entries)), dim3(kWireBlock), 0, stream>>>(
+        nparams, bp, nblocks, in, in_bytes, offsets, max_entries, idx, v);
   return hipGetLastError();
 }
 

@@ -17,6 +17,8 @@ memory and the current stream only.  Names mirror the sources' callables:
                                      host delta itself (no staging)
   wire_encode / wire_decode / wire_checksum -- the flush's positions block
                                      and checksum (verl review, encode.py)
+  wire_encode_blocked / wire_decode_blocked -- 2-byte positions for any
+                                     parameter size (per-block bases)
 
 Bit patterns travel as bfloat16 tensors (int16/uint16 views are accepted too);
 indices are int32, counts and offsets int64, all on the same device.
@@ -375,36 +377,46 @@ def xor_apply_streamed_(snap: torch.Tensor, mask: torch.Tensor, chunk_elems: int
     return snap
 
 
-def wire_width(numel: int) -> int:
-    """Bytes per position of a parameter in the wire encoding."""
-    return 2 if int(numel) <= 65536 else 4
+def _wire_args(idx, offsets, numels):
+    k = len(numels)
+    if (idx.dtype != torch.int32 or not idx.is_contiguous() or idx.device.type != "cuda"
+            or offsets.dtype != torch.int64 or offsets.numel() != k + 1
+            or offsets.device != idx.device):
+        raise ValueError("idx must be contiguous int32 on a GPU and offsets int64[nparams+1] "
+                         "on the same device")
+    return k, (ctypes.c_int64 * max(k, 1))(*[int(n) for n in numels])
 
 
 def wire_encode(idx: torch.Tensor, offsets: torch.Tensor, numels: Sequence[int]):
     """Positions byte block of a diff_many result: (positions uint8, pos_offsets
     int64[P+1]) on the device; one device-to-host read of the offsets sizes it."""
-    k = len(numels)
+    k, nums = _wire_args(idx, offsets, numels)
     dev = idx.device
-    if (idx.dtype != torch.int32 or not idx.is_contiguous() or dev.type != "cuda"
-            or offsets.dtype != torch.int64 or offsets.numel() != k + 1 or offsets.device != dev):
-        raise ValueError("idx must be contiguous int32 on a GPU and offsets int64[nparams+1] "
-                         "on the same device")
-    off = offsets.cpu().tolist()
-    size = sum((off[p + 1] - off[p]) * wire_width(n) for p, n in enumerate(numels))
+    off_h = offsets.cpu().contiguous()
+    size = int(load().delta_wire_positions_size(k, nums, ctypes.c_void_p(off_h.data_ptr())))
+    if size < 0:
+        raise ValueError("offsets or numels out of range")
     positions = torch.empty(max(size, 1), dtype=torch.uint8, device=dev)
     pos_offsets = torch.empty(k + 1, dtype=torch.int64, device=dev)
     lib = load()
     ws = workspace(lib.delta_workspace_size(0, k), dev)
-    nums = (ctypes.c_int64 * max(k, 1))(*[int(n) for n in numels])
-    check(lib.delta_wire_encode(k, nums, _ptr(idx), _ptr(offsets), min(off[-1], idx.numel()),
-                                _ptr(positions), size, _ptr(pos_offsets), _ptr(ws), ws.numel(),
-                                _stream(dev)))
+    check(lib.delta_wire_encode(k, nums, _ptr(idx), _ptr(offsets),
+                                min(int(off_h[-1]), idx.numel()), _ptr(positions), size,
+                                _ptr(pos_offsets), _ptr(ws), ws.numel(), _stream(dev)))
     return positions[:size], pos_offsets
+
+
+def _raise_on_wire_violations(v):
+    bad = int(v.item())
+    if bad:
+        raise DeltaError(1, f"{bad} malformed entries or spans in the received positions")
 
 
 def wire_decode(positions: torch.Tensor, pos_offsets: torch.Tensor, offsets: torch.Tensor,
                 numels: Sequence[int]) -> torch.Tensor:
-    """int32 parameter-local indices back from a positions block."""
+    """int32 parameter-local indices back from a positions block (which may
+    come from a remote sender: the library reads nothing outside it and
+    counts malformed entries, which raise here)."""
     k = len(numels)
     dev = positions.device
     if (positions.dtype != torch.uint8 or not positions.is_contiguous() or dev.type != "cuda"
@@ -414,12 +426,59 @@ def wire_decode(positions: torch.Tensor, pos_offsets: torch.Tensor, offsets: tor
         raise ValueError("positions must be contiguous uint8 on a GPU, pos_offsets and offsets "
                          "int64[nparams+1] on the same device")
     total = int(offsets[k].item())
+    if total < 0:
+        raise ValueError("offsets give a negative entry count")
     idx = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
+    v = torch.empty(1, dtype=torch.int64, device=dev)
     lib = load()
     ws = workspace(lib.delta_workspace_size(0, k), dev)
     nums = (ctypes.c_int64 * max(k, 1))(*[int(n) for n in numels])
-    check(lib.delta_wire_decode(k, nums, _ptr(positions), _ptr(pos_offsets), _ptr(offsets),
-                                total, _ptr(idx), _ptr(ws), ws.numel(), _stream(dev)))
+    check(lib.delta_wire_decode(k, nums, _ptr(positions), positions.numel(), _ptr(pos_offsets),
+                                _ptr(offsets), total, _ptr(idx), _ptr(v), _ptr(ws), ws.numel(),
+                                _stream(dev)))
+    _raise_on_wire_violations(v)
+    return idx[:total]
+
+
+def wire_encode_blocked(idx: torch.Tensor, offsets: torch.Tensor, numels: Sequence[int]):
+    """Blocked positions (2 bytes per position for any parameter size) of a
+    diff_many result, as a uint8 device tensor; one device-to-host read of
+    the total sizes it."""
+    k, nums = _wire_args(idx, offsets, numels)
+    dev = idx.device
+    total = min(int(offsets[k].item()), idx.numel())
+    lib = load()
+    size = int(lib.delta_wire_blocked_size(k, nums, total))
+    if size < 0:
+        raise ValueError("numels out of range")
+    out = torch.empty(max(size, 1), dtype=torch.uint8, device=dev)
+    ws = workspace(lib.delta_workspace_size(0, k), dev)
+    check(lib.delta_wire_encode_blocked(k, nums, _ptr(idx), _ptr(offsets), total, _ptr(out), size,
+                                        _ptr(ws), ws.numel(), _stream(dev)))
+    return out[:size]
+
+
+def wire_decode_blocked(data: torch.Tensor, offsets: torch.Tensor,
+                        numels: Sequence[int]) -> torch.Tensor:
+    """int32 parameter-local indices back from blocked positions (untrusted
+    bytes: nothing outside them is read; malformed entries raise)."""
+    k = len(numels)
+    dev = data.device
+    if (data.dtype != torch.uint8 or not data.is_contiguous() or dev.type != "cuda"
+            or offsets.dtype != torch.int64 or offsets.numel() != k + 1 or offsets.device != dev):
+        raise ValueError("data must be contiguous uint8 on a GPU and offsets int64[nparams+1] "
+                         "on the same device")
+    total = int(offsets[k].item())
+    if total < 0:
+        raise ValueError("offsets give a negative entry count")
+    idx = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
+    v = torch.empty(1, dtype=torch.int64, device=dev)
+    lib = load()
+    ws = workspace(lib.delta_workspace_size(0, k), dev)
+    nums = (ctypes.c_int64 * max(k, 1))(*[int(n) for n in numels])
+    check(lib.delta_wire_decode_blocked(k, nums, _ptr(data), data.numel(), _ptr(offsets), total,
+                                        _ptr(idx), _ptr(v), _ptr(ws), ws.numel(), _stream(dev)))
+    _raise_on_wire_violations(v)
     return idx[:total]
 
 
@@ -436,9 +495,16 @@ def wire_hashes(positions: torch.Tensor, values: torch.Tensor) -> tuple[int, int
 
 
 def wire_checksum(positions: torch.Tensor, values: torch.Tensor) -> int:
-    """The flush checksum: hash(positions) ^ (hash(values) << 1), unbounded."""
-    p, v = wire_hashes(positions, values)
-    return p ^ (v << 1)
+    """The flush checksum hash(positions) ^ (hash(values) << 1), computed by
+    the library as 65 bits in two words, returned as one Python int."""
+    _bits(values, "values")
+    if positions.dtype != torch.uint8 or positions.device != values.device:
+        raise ValueError("positions must be uint8 on the values' device")
+    c = torch.empty(2, dtype=torch.int64, device=values.device)
+    check(load().delta_wire_checksum(_ptr(positions), positions.numel(), _ptr(values),
+                                     values.numel(), _ptr(c), _stream(values.device)))
+    lo, hi = (x & (2 ** 64 - 1) for x in c.cpu().tolist())
+    return lo | (hi << 64)
 
 
 def xor_mask(old: torch.Tensor, new: torch.Tensor, out: torch.Tensor | None = None):

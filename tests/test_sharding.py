@@ -142,10 +142,53 @@ def test_wire_abi_rejects_bad_arguments():
         _abi.DELTA_E_INVALID
     assert "numels[1]" in lib.delta_last_error().decode()
     big = (ctypes.c_int64 * 1)(1 << 31)
-    assert lib.delta_wire_decode(1, big, one, one, one, 5, one, one, 1 << 30, None) == \
+    assert lib.delta_wire_decode(1, big, one, 8, one, one, 5, one, None, one, 1 << 30, None) == \
         _abi.DELTA_E_RANGE
+    assert lib.delta_wire_decode(1, nums, one, -1, one, one, 5, one, None, one, 1 << 30,
+                                 None) == _abi.DELTA_E_INVALID
+    assert lib.delta_wire_decode(1, nums, None, 8, one, one, 5, one, None, one, 1 << 30,
+                                 None) == _abi.DELTA_E_INVALID
     ok = (ctypes.c_int64 * 1)(10)
     assert lib.delta_wire_encode(1, ok, one, one, 5, one, 10, one, one, 1, None) == \
         _abi.DELTA_E_WORKSPACE
     assert lib.delta_wire_hash(None, 4, None, 0, one, None) == _abi.DELTA_E_INVALID
     assert lib.delta_wire_hash(one, -1, one, 0, one, None) == _abi.DELTA_E_INVALID
+
+
+def test_wire_sizes_are_the_library_rule():
+    """The byte counts a caller needs come from the library, from the widths
+    and block tables that the oracle pins (the binding holds no width rule)."""
+    lib = _abi.load()
+    numels = [5, 65536, 65537, 300_001, 0]
+    nums = (ctypes.c_int64 * len(numels))(*numels)
+    off = (ctypes.c_int64 * 6)(0, 3, 10, 12, 20, 20)
+    counts = [3, 7, 2, 8, 0]
+    from oracle import oracle as o
+
+    want = sum(c * o.wire_width(n) for c, n in zip(counts, numels))
+    assert lib.delta_wire_positions_size(len(numels), nums, off) == want
+    assert lib.delta_wire_blocked_size(len(numels), nums, 20) == o.wire_blocked_size(numels, 20)
+    assert lib.delta_wire_blocked_size(len(numels), nums, 20) == 4 * (1 + 1 + 2 + 5 + 0) + 40
+    bad = (ctypes.c_int64 * 6)(0, 3, 2, 12, 20, 20)
+    assert lib.delta_wire_positions_size(len(numels), nums, bad) == -1
+    assert lib.delta_wire_blocked_size(-1, nums, 0) == -1
+
+
+def test_blocked_wire_abi_rejects_bad_arguments():
+    lib = _abi.load()
+    one = ctypes.c_void_p(16)
+    nums = (ctypes.c_int64 * 1)(200_000)  # 4 blocks: 16 bytes of tables
+    assert lib.delta_wire_encode_blocked(1, nums, one, one, -1, one, 8, one, 1 << 30,
+                                         None) == _abi.DELTA_E_INVALID
+    assert lib.delta_wire_encode_blocked(1, nums, one, one, 5, ctypes.c_void_p(18), 8, one,
+                                         1 << 30, None) == _abi.DELTA_E_INVALID
+    assert "aligned" in lib.delta_last_error().decode()
+    assert lib.delta_wire_encode_blocked(1, nums, one, one, 5, one, 8, one, 1, None) == \
+        _abi.DELTA_E_WORKSPACE
+    # fewer bytes than the block tables: rejected before anything is read
+    assert lib.delta_wire_decode_blocked(1, nums, one, 12, one, 5, one, None, one, 1 << 30,
+                                         None) == _abi.DELTA_E_INVALID
+    assert "block bases" in lib.delta_last_error().decode()
+    big = (ctypes.c_int64 * 1)(1 << 31)
+    assert lib.delta_wire_decode_blocked(1, big, one, 1 << 20, one, 5, one, None, one, 1 << 30,
+                                         None) == _abi.DELTA_E_RANGE

@@ -114,3 +114,114 @@ def test_wire_wrappers_reject_bad_arguments(sbd):
     with pytest.raises(ValueError):
         sbd.wire_decode(pos, po, off.cpu(), [10])
     assert torch.equal(sbd.wire_decode(pos, po, off, [10]), idx)
+
+
+def test_wire_decode_untrusted_block(sbd, oracle_mod):
+    """A received positions block that is truncated, or whose parameter spans
+    do not match the counts, is read only inside its bytes: the bad entries
+    come back as -1 and are counted (the binding raises)."""
+    import ctypes
+    from sparse_bf16_delta_amd import _abi
+    from sparse_bf16_delta_amd.ops import _ptr, _stream
+
+    olds, news = delta_case(13, NUMELS, 0.05)
+    ri, rv, rn, ro = oracle_mod.diff_many(olds, news)
+    want_pos, want_po = oracle_mod.wire_encode(ri, ro, NUMELS)
+    off = torch.from_numpy(ro).cuda()
+    lib = _abi.load()
+    ws = torch.empty(lib.delta_workspace_size(0, len(NUMELS)), dtype=torch.uint8, device="cuda")
+    nums = (ctypes.c_int64 * len(NUMELS))(*NUMELS)
+    k = len(NUMELS)
+
+    def decode(pos_bytes, po, nbytes):
+        pos = torch.from_numpy(pos_bytes.copy()).cuda()
+        pot = torch.from_numpy(np.asarray(po, dtype=np.int64).copy()).cuda()
+        idx = torch.full((ri.size,), 77, dtype=torch.int32, device="cuda")
+        v = torch.full((1,), -1, dtype=torch.int64, device="cuda")
+        _abi.check(lib.delta_wire_decode(k, nums, _ptr(pos), nbytes, _ptr(pot), _ptr(off),
+                                         ri.size, _ptr(idx), _ptr(v), _ptr(ws), ws.numel(),
+                                         _stream(off.device)))
+        return idx.cpu().numpy(), int(v.item())
+
+    got, bad = decode(want_pos, want_po, want_pos.size)
+    assert bad == 0 and np.array_equal(got, ri)
+    # truncated: the last 10 bytes are missing (the block is 4-byte wide there)
+    got, bad = decode(want_pos[:-10], want_po, want_pos.size - 10)
+    lost = (10 + 3) // 4  # entries whose bytes reach into the missing tail
+    assert bad == lost
+    assert np.array_equal(got[:-lost], ri[:-lost]) and np.all(got[-lost:] == -1)
+    # a span shifted past the block: parameter 3's start moved beyond the end
+    po2 = want_po.copy()
+    po2[3] = want_po[-1] + 64
+    got, bad = decode(want_pos, po2, want_pos.size)
+    n3 = int(ro[4] - ro[3])
+    assert bad >= n3 and np.all(got[ro[3]:ro[4]] == -1)
+    with pytest.raises(sbd.DeltaError, match="malformed"):
+        sbd.wire_decode(torch.from_numpy(want_pos[:-10].copy()).cuda(),
+                        torch.from_numpy(want_po).cuda(), off, NUMELS)
+
+
+BLOCKED_NUMELS = [5, 65536, 65537, 300_001, 1, 0, 3000, 131072, 65535, 200_003, 1 << 22]
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.001, 0.0118, 0.3, 1.0])
+def test_wire_blocked_matches_oracle(sbd, oracle_mod, frac):
+    """Blocked positions of a diff_many delta equal the oracle's bytes, decode
+    back to the delta, and the flush checksum over them equals the oracle's."""
+    olds, news = delta_case(int(frac * 1000) + 3, BLOCKED_NUMELS, frac)
+    ri, rv, rn, ro = oracle_mod.diff_many(olds, news)
+    want = oracle_mod.wire_encode_blocked(ri, ro, BLOCKED_NUMELS)
+    gi, gv, gn, go = sbd.diff_many([torch.from_numpy(o.view(np.int16)).cuda() for o in olds],
+                                   [torch.from_numpy(x.view(np.int16)).cuda() for x in news])
+    data = sbd.wire_encode_blocked(gi, go, BLOCKED_NUMELS)
+    assert np.array_equal(data.cpu().numpy(), want)
+    back = sbd.wire_decode_blocked(data, go, BLOCKED_NUMELS)
+    assert np.array_equal(back.cpu().numpy(), ri)
+    assert sbd.wire_checksum(data, gv) == oracle_mod.wire_checksum(want, rv)
+    print(f"frac {frac}: {ri.size} entries, {want.size} bytes "
+          f"({want.size / max(ri.size, 1):.3f} per entry)")
+
+
+def test_wire_blocked_capacity_and_untrusted_bytes(sbd, oracle_mod):
+    """Encode writes nothing at or past its capacity; decode of truncated or
+    corrupted bytes reads only inside them and counts what is wrong."""
+    import ctypes
+    from sparse_bf16_delta_amd import _abi
+    from sparse_bf16_delta_amd.ops import _ptr, _stream
+
+    olds, news = delta_case(21, BLOCKED_NUMELS, 0.02)
+    ri, rv, rn, ro = oracle_mod.diff_many(olds, news)
+    want = oracle_mod.wire_encode_blocked(ri, ro, BLOCKED_NUMELS)
+    idx = torch.from_numpy(ri).cuda()
+    off = torch.from_numpy(ro).cuda()
+    lib = _abi.load()
+    k = len(BLOCKED_NUMELS)
+    nums = (ctypes.c_int64 * k)(*BLOCKED_NUMELS)
+    ws = torch.empty(lib.delta_workspace_size(0, k), dtype=torch.uint8, device="cuda")
+    cut = want.size - 101
+    out = torch.full((want.size + 256,), 0xAB, dtype=torch.uint8, device="cuda")
+    _abi.check(lib.delta_wire_encode_blocked(k, nums, _ptr(idx), _ptr(off), ri.size, _ptr(out),
+                                             cut, _ptr(ws), ws.numel(), _stream(idx.device)))
+    got = out.cpu().numpy()
+    assert np.array_equal(got[:cut - 1], want[:cut - 1])  # whole 2-byte offsets below the cut
+    assert np.all(got[cut:] == 0xAB)
+
+    def decode(data, nbytes):
+        d = torch.from_numpy(data.copy()).cuda()
+        res = torch.full((ri.size,), 77, dtype=torch.int32, device="cuda")
+        v = torch.full((1,), -1, dtype=torch.int64, device="cuda")
+        _abi.check(lib.delta_wire_decode_blocked(k, nums, _ptr(d), nbytes, _ptr(off), ri.size,
+                                                 _ptr(res), _ptr(v), _ptr(ws), ws.numel(),
+                                                 _stream(off.device)))
+        return res.cpu().numpy(), int(v.item())
+
+    res, bad = decode(want, want.size)
+    assert bad == 0 and np.array_equal(res, ri)
+    res, bad = decode(want[:-6], want.size - 6)  # three offsets missing
+    assert bad == 3 and np.all(res[-3:] == -1) and np.array_equal(res[:-3], ri[:-3])
+    broken = want.copy()
+    broken[4 * 3:4 * 3 + 4] = np.frombuffer(np.uint32(1 << 30).tobytes(), dtype=np.uint8)
+    res, bad = decode(broken, broken.size)  # a base far above its parameter's count
+    assert bad >= 1
+    with pytest.raises(sbd.DeltaError, match="malformed"):
+        sbd.wire_decode_blocked(torch.from_numpy(want[:-6].copy()).cuda(), off, BLOCKED_NUMELS)
