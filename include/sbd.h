@@ -96,6 +96,26 @@ delta_status delta_diff(const uint16_t *old_bits, const uint16_t *new_bits, int6
                         void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * delta_diff_noalloc -- delta_diff with no workspace argument and no device
+ * allocation, for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The compaction's
+ * scratch is a static device array inside the library (48 MiB on each GPU the
+ * library runs on, held until the process ends), so n is limited to
+ * delta_diff_noalloc_max_elems() elements (2^26); larger tensors are rejected
+ * with DELTA_E_RANGE before anything is enqueued.  Arguments, outputs and the
+ * capacity protocol as delta_diff.  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (two streams or two threads at once)
+ * race and must be serialised by the caller.
+ * Errors: DELTA_E_INVALID, DELTA_E_RANGE (n above the limit), DELTA_E_HIP.
+ */
+delta_status delta_diff_noalloc(const uint16_t *old_bits, const uint16_t *new_bits, int64_t n,
+                                int32_t *idx, uint16_t *val, int64_t capacity, int64_t *nnz,
+                                void *stream);
+
+/* delta_diff_noalloc_max_elems -- the largest n delta_diff_noalloc accepts. */
+int64_t delta_diff_noalloc_max_elems(void);
+
+/*
  * delta_diff_many -- delta_diff over a whole parameter list in one pass.
  *
  * [VERL] code-snippet section, `gather_v_batched_to_rank0`: the deltas of K

@@ -45,6 +45,8 @@ _st = ctypes.c_int
 SIGNATURES = {
     "delta_workspace_size": (_sz, [_i64, _i32]),
     "delta_diff": (_st, [_vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "delta_diff_noalloc": (_st, [_vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp]),
+    "delta_diff_noalloc_max_elems": (_i64, []),
     "delta_diff_many": (_st, [_i32, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "delta_diff_many_sharded": (_st, [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
                                       _sz, _vp]),

@@ -236,3 +236,21 @@ def test_core_signatures_are_the_boundary_contract():
     assert _declaration("xor_mask") == [u16c, u16c, u16, "int64_t", "void *"]
     assert _declaration("xor_apply") == [u16, u16c, "int64_t", "void *"]
     assert _declaration("delta_last_error") == ["void"]
+
+
+def test_noalloc_diff_argument_checks():
+    """delta_diff_noalloc rejects what does not fit its static scratch, and bad
+    arguments, before anything reaches the GPU."""
+    lib = _abi.load()
+    top = lib.delta_diff_noalloc_max_elems()
+    assert top == 1 << 26
+    # the scratch layout for the largest accepted tensor stays within 48 MiB
+    assert lib.delta_workspace_size(top, 1) <= 48 << 20
+    one = ctypes.c_void_p(16)
+    assert lib.delta_diff_noalloc(one, one, top + 1, one, one, 5, one, None) == _abi.DELTA_E_RANGE
+    assert "static scratch" in _err(lib)
+    assert lib.delta_diff_noalloc(one, one, -1, one, one, 5, one, None) == _abi.DELTA_E_INVALID
+    assert lib.delta_diff_noalloc(one, one, 10, one, one, -1, one, None) == _abi.DELTA_E_INVALID
+    assert lib.delta_diff_noalloc(one, one, 10, one, one, 5, None, None) == _abi.DELTA_E_INVALID
+    assert lib.delta_diff_noalloc(None, one, 10, one, one, 5, one, None) == _abi.DELTA_E_INVALID
+    assert lib.delta_diff_noalloc(one, one, 10, None, one, 5, one, None) == _abi.DELTA_E_INVALID
