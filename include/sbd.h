@@ -50,20 +50,34 @@ typedef enum {
 } delta_status;
 
 /*
- * delta_workspace_size -- bytes of scratch workspace that delta_diff,
- * delta_diff_many and delta_apply_many need for a parameter list of
- * `nparams` tensors holding `total_elems` elements in all (an upper bound
+ * delta_workspace_size -- bytes of scratch workspace with which delta_diff,
+ * delta_diff_many and delta_apply_many never run short, for a parameter list
+ * of `nparams` tensors holding `total_elems` elements in all (an upper bound
  * that holds for any split of the elements).  Pure host function.
  * The workspace holds, per 32768-element tile of the compaction, its change
- * count, its running offset, its descriptor, a 4 KB staging slot and a 16 KB
- * share of a staging arena for its compacted entries -- about 0.63 bytes per
- * element -- plus the device copy of the parameter table.  Every function
- * taking a workspace requires it to start on a 256-byte boundary (device
- * allocations do) and fails with DELTA_E_WORKSPACE otherwise.  Its contents
- * on entry do not matter and are clobbered.  Returns 0 for negative
+ * count, its running offset, its descriptor and a 2 KB staging slot, plus the
+ * device copy of the parameter table (these are the minimum,
+ * delta_workspace_size_for(total_elems, nparams, 0): about 0.06 bytes per
+ * element), and then a staging arena for the compacted entries of tiles with
+ * more than 512 changes and the change masks of tiles with more than 4096:
+ * here its worst case, 16 KB per tile (about 0.5 bytes per element).  Every
+ * function taking a workspace requires it to start on a 256-byte boundary
+ * (device allocations do) and fails with DELTA_E_WORKSPACE otherwise.  Its
+ * contents on entry do not matter and are clobbered.  Returns 0 for negative
  * arguments.
  */
 size_t delta_workspace_size(int64_t total_elems, int32_t nparams);
+
+/*
+ * delta_workspace_size_for -- the workspace for a diff that keeps at most
+ * `capacity` entries: the minimum plus an arena of 4 bytes per kept entry
+ * (and 16 per tile), capped at delta_workspace_size.  While the true count
+ * is at most `capacity`, the arena never runs out; any other size from the
+ * minimum up also works: a diff's bytes beyond the minimum become its arena,
+ * and a tile that finds no room there is recomputed from both inputs instead
+ * (the same result, more reads).  0 for negative arguments.
+ */
+size_t delta_workspace_size_for(int64_t total_elems, int32_t nparams, int64_t capacity);
 
 /*
  * delta_diff -- bitwise change detection and stream compaction of one tensor.
@@ -85,7 +99,9 @@ size_t delta_workspace_size(int64_t total_elems, int32_t nparams);
  *  nnz                 device int64[1]: receives the TRUE number of changed
  *                      elements, even when it exceeds `capacity` -- the caller
  *                      then re-allocates and calls again.
- *  ws, ws_bytes        workspace of at least delta_workspace_size(n, 1) bytes.
+ *  ws, ws_bytes        workspace of at least delta_workspace_size_for(n, 1, 0)
+ *                      bytes; delta_workspace_size_for(n, 1, capacity) keeps
+ *                      every staged tile in the arena (see there).
  * The work is five kernel launches on `stream` (count and stage, two scans,
  * place, dense tiles); no workgroup waits for another.
  * Errors: DELTA_E_INVALID (null pointers, n < 0, capacity < 0),
@@ -101,7 +117,7 @@ delta_status delta_diff(const uint16_t *old_bits, const uint16_t *new_bits, int6
  * tight serving loops, harnesses that forbid hipMalloc.  The compaction's
  * scratch is a static device array inside the library (48 MiB on each GPU the
  * library runs on, held until the process ends), so n is limited to
- * delta_diff_noalloc_max_elems() elements (2^26); larger tensors are rejected
+ * delta_diff_noalloc_max_elems() elements (2^28); larger tensors are rejected
  * with DELTA_E_RANGE before anything is enqueued.  Arguments, outputs and the
  * capacity protocol as delta_diff.  Every call on one GPU shares that GPU's
  * array: calls that overlap on one GPU (two streams or two threads at once)
@@ -134,7 +150,9 @@ int64_t delta_diff_noalloc_max_elems(void);
  *  offsets             device int64[nparams+1]: exclusive running sum of nnz
  *                      (offsets[nparams] is the true total).  Parameter p's
  *                      entries are idx/val[offsets[p] .. offsets[p+1]).
- *  ws, ws_bytes        at least delta_workspace_size(sum(numels), nparams).
+ *  ws, ws_bytes        at least delta_workspace_size_for(sum(numels), nparams,
+ *                      0); delta_workspace_size_for(sum(numels), nparams,
+ *                      capacity) is the recommended size.
  * The parameter table (40 bytes per tensor) is copied host-to-device on
  * `stream`; HIP has staged a copy from pageable host memory by the time the
  * call returns (without waiting for the stream), so the host arrays may be

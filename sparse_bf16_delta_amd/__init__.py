@@ -16,6 +16,8 @@ from .ops import (  # noqa: F401
     apply_streamed_,
     default_capacity,
     diff,
+    diff_workspace_size,
+    release_workspaces,
     diff_many,
     workspace,
     workspace_size,
@@ -36,5 +38,5 @@ __all__ = [
     "xor_mask", "xor_apply_", "workspace", "workspace_size", "default_capacity",
     "shard0_piece", "flat_offset", "apply_streamed_", "xor_apply_streamed_", "apply_many_host_",
     "wire_encode", "wire_decode", "wire_hashes", "wire_checksum", "wire_encode_blocked",
-    "wire_decode_blocked",
+    "wire_decode_blocked", "diff_workspace_size", "release_workspaces",
 ]

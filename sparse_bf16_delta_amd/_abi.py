@@ -44,6 +44,7 @@ _i64, _i32, _sz, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c
 _st = ctypes.c_int
 SIGNATURES = {
     "delta_workspace_size": (_sz, [_i64, _i32]),
+    "delta_workspace_size_for": (_sz, [_i64, _i32, _i64]),
     "delta_diff": (_st, [_vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "delta_diff_noalloc": (_st, [_vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp]),
     "delta_diff_noalloc_max_elems": (_i64, []),

@@ -90,6 +90,12 @@ WsLayout ws_layout(int64_t max_tiles, int32_t nparams) {
   return L;
 }
 
+uint64_t arena_quads_for(const WsLayout& L, size_t ws_bytes) {
+  const size_t have = ws_bytes > L.wide ? ws_bytes - L.wide : 0;
+  const size_t most = L.total - L.wide;
+  return static_cast<uint64_t>((have < most ? have : most) / 16);
+}
+
 }  // namespace sbd
 
 extern "C" {
@@ -97,6 +103,18 @@ extern "C" {
 size_t delta_workspace_size(int64_t total_elems, int32_t nparams) {
   if (total_elems < 0 || nparams < 0) return 0;
   return sbd::ws_layout(sbd::max_tiles_for(total_elems, nparams), nparams).total;
+}
+
+size_t delta_workspace_size_for(int64_t total_elems, int32_t nparams, int64_t capacity) {
+  if (total_elems < 0 || nparams < 0 || capacity < 0) return 0;
+  const int64_t tiles = sbd::max_tiles_for(total_elems, nparams);
+  const sbd::WsLayout L = sbd::ws_layout(tiles, nparams);
+  const int64_t keep = capacity < total_elems ? capacity : total_elems;
+  // 4 bytes per kept entry, plus up to 16 bytes of quad rounding per tile;
+  // none at all for capacity 0 (the minimum)
+  const size_t arena = keep > 0 ? align256(size_t(4 * keep) + 16 * size_t(tiles)) : 0;
+  const size_t most = L.total - L.wide;
+  return L.wide + (arena < most ? arena : most);
 }
 
 const char* delta_last_error(void) { return g_error.c_str(); }
@@ -117,16 +135,17 @@ delta_status delta_diff(const uint16_t* old_bits, const uint16_t* new_bits, int6
     return fail(DELTA_E_INVALID, "delta_diff: null output with capacity=%lld",
                 (long long)capacity);
   const sbd::WsLayout L = sbd::ws_layout(sbd::max_tiles_for(n, 1), 1);
-  if (ws == nullptr || ws_bytes < L.total)
-    return fail(DELTA_E_WORKSPACE, "delta_diff: workspace %zu bytes, need %zu", ws_bytes,
-                L.total);
+  if (ws == nullptr || ws_bytes < L.wide)
+    return fail(DELTA_E_WORKSPACE, "delta_diff: workspace %zu bytes, need at least %zu",
+                ws_bytes, L.wide);
   if (!ws_aligned(ws))
     return fail(DELTA_E_WORKSPACE, "delta_diff: workspace not 256-byte aligned");
   sbd::DiffParam single{old_bits, new_bits, n, 0, 0};
   const int64_t tiles = (n + sbd::kDiffTile - 1) / sbd::kDiffTile;  // < kMaxTiles for n < 2^31
   g_error.clear();
   return hip_status(sbd::launch_diff(nullptr, single, 1, tiles, idx, false, val, capacity, nnz,
-                                     nullptr, ws, L, static_cast<hipStream_t>(stream)),
+                                     nullptr, ws, L, sbd::arena_quads_for(L, ws_bytes),
+                                     static_cast<hipStream_t>(stream)),
                     "delta_diff launch");
 }
 
@@ -179,8 +198,9 @@ delta_status diff_many_impl(const char* fn, bool global_idx, int32_t nparams,
     return fail(DELTA_E_RANGE, "%s: %lld tiles exceed one launch (%lld)", fn, (long long)tiles,
                 (long long)sbd::kMaxTiles);
   const sbd::WsLayout L = sbd::ws_layout(sbd::max_tiles_for(total, nparams), nparams);
-  if (ws == nullptr || ws_bytes < L.total)
-    return fail(DELTA_E_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, L.total);
+  if (ws == nullptr || ws_bytes < L.wide)
+    return fail(DELTA_E_WORKSPACE, "%s: workspace %zu bytes, need at least %zu", fn, ws_bytes,
+                L.wide);
   if (!ws_aligned(ws)) return fail(DELTA_E_WORKSPACE, "%s: workspace not 256-byte aligned", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
   sbd::DiffParam* d_table = reinterpret_cast<sbd::DiffParam*>(static_cast<char*>(ws) + L.table);
@@ -192,7 +212,8 @@ delta_status diff_many_impl(const char* fn, bool global_idx, int32_t nparams,
   g_error.clear();
   sbd::DiffParam none{nullptr, nullptr, 0, 0, 0};
   return hip_status(sbd::launch_diff(nparams > 0 ? d_table : nullptr, none, nparams, tiles, idx,
-                                     global_idx, val, capacity, nnz, offsets, ws, L, s),
+                                     global_idx, val, capacity, nnz, offsets, ws, L,
+                                     sbd::arena_quads_for(L, ws_bytes), s),
                     fn);
 }
 

@@ -19,15 +19,20 @@
 //     group totals are scanned in LDS, giving every change its slot inside
 //     the tile in ascending element order.  A tile with at most 4096 changes
 //     is compacted in LDS as (tile-local index << 16 | new bits) and copied
-//     with 16-byte nontemporal stores: a tile with up to 1024 changes into a
-//     4 KB workspace slot of its own, a tile with more into a staging arena
+//     with 16-byte nontemporal stores: a tile with up to 512 changes into a
+//     2 KB workspace slot of its own, a tile with more into a staging arena
 //     shared by all tiles, at a position it takes with one atomic add on a
 //     workspace counter (so the arena fills as one dense, ascending write
 //     stream; fixed 16 KB slots, a few KB written in each, cost 1.3 ms more
 //     on the 7B-shaped list at 8 % density, while for sparse tiles the
 //     atomic's latency costs more than the slot saves).  A denser tile
-//     stores its 4 KB change mask in its slot instead.  The tile count goes
-//     to a per-tile array and the workgroup ends.
+//     stores its 4 KB change mask in the arena instead.  The arena is what
+//     the caller's workspace holds past the fixed regions: a tile that finds
+//     it full keeps nothing there and is treated as a dense tile whose mask
+//     the dense kernel recomputes, so any arena size gives the same result,
+//     and one sized from the caller's capacity never runs out while the
+//     delta fits that capacity.  The tile count goes to a per-tile array and
+//     the workgroup ends.
 //  2. Scan.  One workgroup per 4096 tiles scans their counts (prefix inside
 //     the chunk, chunk total) and lists the dense tiles; one workgroup scans
 //     the chunk totals and writes the per-parameter counts and offsets.
@@ -43,8 +48,8 @@
 // that the slot round trip adds here.
 // Traffic: the 4n-byte read happens once; a staged tile adds 4 bytes written
 // and 4 read per changed element, a dense tile re-reads `new` (2 bytes per
-// element), and the tile count, prefix, position and descriptor add about 60
-// bytes per tile.
+// element; both inputs if its mask found no room), and the tile count,
+// prefix, position and descriptor add about 60 bytes per tile.
 #include <atomic>
 
 #include "sbd_internal.h"
@@ -57,12 +62,19 @@ static_assert(kGroups <= 64, "one (iteration, wave) group per lane of a wave");
 static_assert(kDiffIters <= 8, "a lane's change mask is at most 8 bytes");
 static_assert(kDiffTile <= 65536, "tile-local indices are staged in 16 bits");
 static_assert(kStageCap % 4 == 0, "staged entries are copied four at a time");
-static_assert(kCompactWords * 4 >= kDiffBlock * 8, "a compact slot holds a tile's change mask");
+static_assert(kWideWords * 4 >= kDiffBlock * 8, "a tile's change mask fits its arena share");
+constexpr uint64_t kMaskQuads = kDiffBlock * 8 / 16;  // arena quads of a dense tile's mask
 static_assert(kCompactCap % 4 == 0 && kCompactCap <= kStageCap, "slot tiers");
 static_assert(kScanChunk == kScanBlock * 4, "a scan lane takes four tiles");
 static_assert(kMaxTiles / kScanChunk <= kScanBlock * 4, "the chunk totals fit one workgroup");
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// A tile whose entries did not fit the staging arena is handled as a dense
+// tile: its count carries this flag (for the scan's dense list) and its
+// arena position is kNoArena (for the placing kernel).
+constexpr uint32_t kDenseFlag = 0x80000000u;
+constexpr uint64_t kNoArena = ~0ull;
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
@@ -232,7 +244,7 @@ template <bool kMany>
 __global__ __launch_bounds__(kDiffBlock) void diff_count_kernel(
     const TileDesc* __restrict__ tdesc, DiffParam single, uint32_t* __restrict__ counts,
     uint32_t* __restrict__ compact, uint32_t* __restrict__ wide, uint32_t* __restrict__ ndense,
-    uint64_t* __restrict__ tile_pos, unsigned long long* __restrict__ ctr) {
+    uint64_t* __restrict__ tile_pos, unsigned long long* __restrict__ ctr, uint64_t arena_quads) {
   __shared__ __attribute__((aligned(16))) uint32_t s_stage[kStageCap];
   __shared__ uint64_t s_pos;
   __shared__ uint32_t s_wtot[kGroups];
@@ -272,17 +284,26 @@ __global__ __launch_bounds__(kDiffBlock) void diff_count_kernel(
 
   uint32_t lp[kDiffIters], goff[kDiffIters], agg, gexcl;
   tile_offsets(m, lp, goff, agg, gexcl, s_wtot, lane, wave);
+  const bool staged = agg <= static_cast<uint32_t>(kStageCap);
+  const bool in_arena = staged && agg > static_cast<uint32_t>(kCompactCap);
   if (tid == 0) {
-    counts[tile] = agg;
+    uint32_t c = agg;
+    if (!staged || in_arena) {
+      // whole 16-byte quads of the arena, so every tile's run starts aligned:
+      // a staged tile's entries, or a dense tile's change mask.  A tile that
+      // finds the arena full keeps nothing there and is handled as a dense
+      // tile whose mask is recomputed.
+      const uint64_t q = staged ? (agg + 3u) / 4u : kMaskQuads;
+      const uint64_t p = atomicAdd(ctr, static_cast<unsigned long long>(q));
+      const bool fits = p + q <= arena_quads;
+      s_pos = fits ? p : kNoArena;
+      tile_pos[tile] = fits ? p : kNoArena;
+      if (!fits && staged) c |= kDenseFlag;
+    }
+    counts[tile] = c;
     if (tile == 0) *ndense = 0u;  // the scan kernel, launched next, lists dense tiles
   }
-  if (agg <= static_cast<uint32_t>(kStageCap)) {
-    if (tid == 0 && agg > static_cast<uint32_t>(kCompactCap)) {
-      // whole 16-byte quads of the arena, so every tile's run starts aligned
-      const uint64_t p = atomicAdd(ctr, static_cast<unsigned long long>((agg + 3u) / 4u));
-      s_pos = p;
-      tile_pos[tile] = p;
-    }
+  if (staged) {
 #pragma unroll
     for (int j = 0; j < kDiffIters; ++j) {
       const uint32_t mm = m[j];
@@ -300,19 +321,21 @@ __global__ __launch_bounds__(kDiffBlock) void diff_count_kernel(
         stage_slot<7>(mm, pos, local, x, s_stage);
       }
     }
-    __syncthreads();
-    // 16-byte copies with the nontemporal hint (the entries are read once, by
-    // the placing kernel); the last one may carry up to three stale LDS words
-    // past `agg`, which stay inside the slot or the tile's arena quads and are
-    // never read.
-    uint32_t* slot = agg <= static_cast<uint32_t>(kCompactCap) ? compact + tile * kCompactWords
-                                                               : wide + s_pos * 4u;
+  }
+  __syncthreads();
+  const uint64_t at = (!staged || in_arena) ? s_pos : 0;
+  if (staged && !(in_arena && at == kNoArena)) {
+    // 16-byte copies with the nontemporal hint (the entries are read once,
+    // by the placing kernel); the last one may carry up to three stale LDS
+    // words past `agg`, which stay inside the slot or the tile's arena quads
+    // and are never read.
+    uint32_t* slot = in_arena ? wide + at * 4u : compact + tile * kCompactWords;
     for (uint32_t p = static_cast<uint32_t>(tid) * 4u; p < agg; p += kDiffBlock * 4u) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(&s_stage[p]);
       __builtin_nontemporal_store(w, global_ptr(reinterpret_cast<u32x4*>(slot + p)));
     }
-  } else {
-    // dense: the change mask, one byte per 16-byte chunk, 8 bytes per lane
+  } else if (!staged && at != kNoArena) {
+    // dense: the change mask in the arena, one byte per 16-byte chunk, 8 bytes per lane
     u32x2 w;
     w.x = 0u;
     w.y = 0u;
@@ -323,7 +346,7 @@ __global__ __launch_bounds__(kDiffBlock) void diff_count_kernel(
       else
         w.y |= m[j] << (8 * (j - 4));
     }
-    *global_ptr(reinterpret_cast<u32x2*>(compact + tile * kCompactWords) + tid) = w;
+    *global_ptr(reinterpret_cast<u32x2*>(wide + at * 4u) + tid) = w;
   }
 }
 
@@ -343,8 +366,10 @@ __global__ __launch_bounds__(kScanBlock) void diff_scan_chunks_kernel(
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t t = t0 + q;
-    v[q] = t < total_tiles ? counts[t] : 0u;
-    if (v[q] > static_cast<uint32_t>(kStageCap)) dense_list[atomicAdd(ndense, 1u)] = int32_t(t);
+    const uint32_t raw = t < total_tiles ? counts[t] : 0u;
+    v[q] = raw & ~kDenseFlag;
+    if (v[q] > static_cast<uint32_t>(kStageCap) || (raw & kDenseFlag) != 0u)
+      dense_list[atomicAdd(ndense, 1u)] = int32_t(t);
   }
   const uint32_t own = v[0] + v[1] + v[2] + v[3];
   const uint32_t inc = wave_inclusive(own, lane);
@@ -456,7 +481,9 @@ __global__ __launch_bounds__(kDiffBlock) void diff_place_kernel(
     int r = 0;
     for (int k = 0; k < nt; ++k) {
       const uint64_t c = s_off[k + 1] - s_off[k];
-      if (c != 0 && c <= static_cast<uint64_t>(kStageCap)) {
+      // staged: in its compact slot, or in the arena unless the arena was full
+      if (c != 0 && c <= static_cast<uint64_t>(kStageCap) &&
+          !(c > static_cast<uint64_t>(kCompactCap) && s_tpos[k] == kNoArena)) {
         s_tile[r] = k;
         s_run[r] = acc;
         acc += static_cast<uint32_t>(c);
@@ -503,15 +530,17 @@ __global__ __launch_bounds__(kDiffBlock) void diff_place_kernel(
 }
 
 // Phase 3b: dense tiles, from their change masks and a second read of the
-// changed 16-byte chunks of `new`.  Each of the tile's kDiffIters iterations
-// (at most kDiffBlock * kVec entries) is staged in LDS and copied out with
-// coalesced stores.
+// changed 16-byte chunks of `new` -- or, for a tile that found no room in the
+// arena, from a second read of both inputs.  Each of the tile's kDiffIters
+// iterations (at most kDiffBlock * kVec entries) is staged in LDS and copied
+// out with coalesced stores.
 template <bool kMany, typename IdxT>
 __global__ __launch_bounds__(kDiffBlock) void diff_dense_kernel(
     const TileDesc* __restrict__ tdesc, DiffParam single, const int32_t* __restrict__ dense_list,
     const uint32_t* __restrict__ ndense, const uint32_t* __restrict__ inpfx,
-    const uint64_t* __restrict__ chunk_base, const uint32_t* __restrict__ compact,
-    IdxT* __restrict__ idx, uint16_t* __restrict__ val, int64_t capacity) {
+    const uint64_t* __restrict__ chunk_base, const uint32_t* __restrict__ wide,
+    const uint64_t* __restrict__ tile_pos, IdxT* __restrict__ idx, uint16_t* __restrict__ val,
+    int64_t capacity) {
   static_assert(sizeof(IdxT) == 8 ? kMany : true, "global indices need a parameter table");
   static_assert(kDiffBlock * kVec <= kStageCap, "one iteration of a tile fits the stage");
   __shared__ __attribute__((aligned(16))) uint32_t s_stage[kDiffBlock * kVec];
@@ -528,15 +557,28 @@ __global__ __launch_bounds__(kDiffBlock) void diff_dense_kernel(
     asm volatile("" : "+v"(ltid));
     const int64_t t = dense_list[i];
     const TileView tv = tile_view<kMany>(tdesc, single, t);
-    const bool vec = tv.valid == kDiffTile && (reinterpret_cast<uintptr_t>(tv.nb) & 15u) == 0;
-    const u32x2 mw = *global_ptr(reinterpret_cast<const u32x2*>(compact + t * kCompactWords) + ltid);
+    const bool vec = tv.valid == kDiffTile &&
+                     ((reinterpret_cast<uintptr_t>(tv.ob) | reinterpret_cast<uintptr_t>(tv.nb)) &
+                      15u) == 0;
+    const uint64_t at = tile_pos[t];
     uint32_t m[kDiffIters];
     uint4 x[kDiffIters];
+    if (at != kNoArena) {  // the mask the count kernel stored
+      const u32x2 mw = *global_ptr(reinterpret_cast<const u32x2*>(wide + at * 4u) + ltid);
 #pragma unroll
-    for (int j = 0; j < kDiffIters; ++j) {
-      m[j] = ((j < 4 ? mw.x : mw.y) >> (8 * (j & 3))) & 0xFFu;
-      x[j] = m[j] != 0u ? load_chunk(tv.nb, j * kDiffBlock * kVec + ltid * kVec, tv.valid, vec)
-                        : make_uint4(0u, 0u, 0u, 0u);
+      for (int j = 0; j < kDiffIters; ++j) {
+        m[j] = ((j < 4 ? mw.x : mw.y) >> (8 * (j & 3))) & 0xFFu;
+        x[j] = m[j] != 0u ? load_chunk(tv.nb, j * kDiffBlock * kVec + ltid * kVec, tv.valid, vec)
+                          : make_uint4(0u, 0u, 0u, 0u);
+      }
+    } else {  // no room was left in the arena: compare the tile again
+#pragma unroll
+      for (int j = 0; j < kDiffIters; ++j) {
+        const int local = j * kDiffBlock * kVec + ltid * kVec;
+        const uint4 o = load_chunk(tv.ob, local, tv.valid, vec);
+        x[j] = load_chunk(tv.nb, local, tv.valid, vec);
+        m[j] = change_mask8(o, x[j]);
+      }
     }
     uint32_t lp[kDiffIters], goff[kDiffIters], agg, gexcl;
     tile_offsets(m, lp, goff, agg, gexcl, s_wtot, lane, wave);
@@ -627,7 +669,7 @@ void launch_place(const TileDesc* tdesc, const DiffParam& single, int64_t total_
       tdesc, total_tiles, nchunks, static_cast<int32_t>(per_wg), inpfx, chunk_base, compact, wide,
       idx, val, capacity, tile_pos);
   diff_dense_kernel<kMany, IdxT><<<dim3(dense_grid), dim3(kDiffBlock), 0, stream>>>(
-      tdesc, single, dense_list, ndense, inpfx, chunk_base, compact, idx, val, capacity);
+      tdesc, single, dense_list, ndense, inpfx, chunk_base, wide, tile_pos, idx, val, capacity);
 }
 
 }  // namespace
@@ -635,7 +677,7 @@ void launch_place(const TileDesc* tdesc, const DiffParam& single, int64_t total_
 hipError_t launch_diff(const DiffParam* d_table, const DiffParam& single, int32_t nparams,
                        int64_t total_tiles, void* idx, bool global_idx, uint16_t* val,
                        int64_t capacity, int64_t* nnz, int64_t* offsets, void* ws,
-                       const WsLayout& L, hipStream_t stream) {
+                       const WsLayout& L, uint64_t arena_quads, hipStream_t stream) {
   clear_stale_error();
   char* base = static_cast<char*>(ws);
   uint32_t* ndense = reinterpret_cast<uint32_t*>(base + L.ndense);
@@ -662,12 +704,12 @@ hipError_t launch_diff(const DiffParam* d_table, const DiffParam& single, int32_
       if (prep_blocks > 65536) prep_blocks = 65536;
       diff_prepare_kernel<<<dim3(unsigned(prep_blocks)), dim3(256), 0, stream>>>(
           d_table, nparams, total_tiles, tdesc, ctr);
-      diff_count_kernel<true><<<dim3(grid), dim3(kDiffBlock), 0, stream>>>(tdesc, single, counts,
-                                                                           compact, wide, ndense, tile_pos, ctr);
+      diff_count_kernel<true><<<dim3(grid), dim3(kDiffBlock), 0, stream>>>(
+          tdesc, single, counts, compact, wide, ndense, tile_pos, ctr, arena_quads);
     } else {
       zero_ctr_kernel<<<dim3(1), dim3(64), 0, stream>>>(ctr);
-      diff_count_kernel<false><<<dim3(grid), dim3(kDiffBlock), 0, stream>>>(nullptr, single,
-                                                                            counts, compact, wide, ndense, tile_pos, ctr);
+      diff_count_kernel<false><<<dim3(grid), dim3(kDiffBlock), 0, stream>>>(
+          nullptr, single, counts, compact, wide, ndense, tile_pos, ctr, arena_quads);
     }
     diff_scan_chunks_kernel<<<dim3(unsigned(nchunks)), dim3(kScanBlock), 0, stream>>>(
         counts, total_tiles, inpfx, chunk_tot, dense_list, ndense);

@@ -21,7 +21,9 @@ namespace sbd {
 namespace {
 
 constexpr size_t kNoAllocScratchBytes = size_t(48) << 20;
-constexpr int64_t kNoAllocMaxElems = int64_t(1) << 26;
+// The fixed regions for 2^28 elements take 17.7 MiB; the rest of the array
+// is staging arena (tiles that do not fit it are recomputed, same result).
+constexpr int64_t kNoAllocMaxElems = int64_t(1) << 28;
 
 __device__ __attribute__((aligned(256))) unsigned char scratch[kNoAllocScratchBytes];
 
@@ -75,9 +77,9 @@ delta_status delta_diff_noalloc(const uint16_t* old_bits, const uint16_t* new_bi
     return fail_with(DELTA_E_INVALID, "delta_diff_noalloc: null output with capacity=%lld",
                      (long long)capacity);
   const sbd::WsLayout L = sbd::ws_layout(sbd::max_tiles_for(n, 1), 1);
-  if (L.total > sbd::kNoAllocScratchBytes)  // cannot happen for n within the limit
+  if (L.wide > sbd::kNoAllocScratchBytes)  // cannot happen for n within the limit
     return fail_with(DELTA_E_WORKSPACE, "delta_diff_noalloc: layout of %zu bytes exceeds the "
-                     "static scratch", L.total);
+                     "static scratch", L.wide);
   const char* why = nullptr;
   void* ws = sbd::scratch_address(why);
   if (ws == nullptr)
@@ -85,8 +87,10 @@ delta_status delta_diff_noalloc(const uint16_t* old_bits, const uint16_t* new_bi
   sbd::DiffParam single{old_bits, new_bits, n, 0, 0};
   const int64_t tiles = (n + sbd::kDiffTile - 1) / sbd::kDiffTile;
   sbd::clear_last_error();
-  const hipError_t e = sbd::launch_diff(nullptr, single, 1, tiles, idx, false, val, capacity, nnz,
-                                        nullptr, ws, L, static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      sbd::launch_diff(nullptr, single, 1, tiles, idx, false, val, capacity, nnz, nullptr, ws, L,
+                       sbd::arena_quads_for(L, sbd::kNoAllocScratchBytes),
+                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail_with(DELTA_E_HIP, "delta_diff_noalloc launch: %s", hipGetErrorString(e));
   return DELTA_OK;

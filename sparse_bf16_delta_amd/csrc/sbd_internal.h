@@ -78,15 +78,16 @@ struct TileDesc {
 };
 
 // A tile with at most kStageCap changes is staged in LDS (4 bytes per entry)
-// and then copied out: into its own compact 4 KB slot when it has at most
-// kCompactCap changes, else into the shared staging arena (kWideWords words
-// per tile reserved in all, filled in whole 16-byte quads from a counter).
-// A denser tile stores its change mask (one byte per 16-byte chunk, 8 per
-// lane) in its compact slot.
+// and then copied out: into its own compact 2 KB slot when it has at most
+// kCompactCap changes, else into the staging arena shared by all tiles
+// (filled in whole 16-byte quads from a counter; the worst case reserves
+// kWideWords words per tile).  A denser tile stores its change mask (one byte
+// per 16-byte chunk, 4 KB) in the arena; a tile that finds the arena full
+// stores nothing and is recomputed from both inputs by the dense kernel.
 constexpr int kStageCap = 4096;
-constexpr int kCompactCap = 1024;
+constexpr int kCompactCap = 512;
 constexpr int64_t kCompactWords = kCompactCap;  // uint32 per compact slot
-constexpr int64_t kWideWords = kStageCap;       // arena uint32 reserved per tile
+constexpr int64_t kWideWords = kStageCap;       // arena uint32 reserved per tile (worst case)
 // Tile counts are scanned in chunks of kScanChunk tiles, four per lane.
 constexpr int kScanBlock = 1024;
 constexpr int64_t kScanChunk = int64_t(kScanBlock) * 4;
@@ -118,9 +119,10 @@ __device__ __forceinline__ int32_t find_param_wave0(const int64_t* __restrict__ 
 
 // Workspace layout (all offsets 256-byte aligned): a 256-byte header (the
 // dense-tile count and the arena fill counter), then per tile a count, an
-// in-chunk prefix, a dense-list entry, a descriptor, an arena position, a
-// compact slot and its share of the arena (20 KB), per chunk a total and a
-// base, and the parameter table.
+// in-chunk prefix, a dense-list entry, a descriptor, an arena position and a
+// 4 KB compact slot, per chunk a total and a base, the parameter table, and
+// last the staging arena: whatever the caller's workspace holds past
+// `wide`, up to the worst case of 16 KB per tile at `total`.
 struct WsLayout {
   size_t ndense;      // uint32: number of dense tiles
   size_t arena_next;  // uint64: arena quads handed out so far
@@ -153,10 +155,15 @@ inline void clear_stale_error() { (void)hipGetLastError(); }
 // Launchers return hipSuccess or the launch error.
 // idx is int32_t[capacity] (parameter-local indices) or, with global_idx,
 // int64_t[capacity] holding flat_offset + local index (parameter lists only).
+// arena_quads: 16-byte quads of staging arena at L.wide (any number, from 0
+// to the worst case (L.total - L.wide) / 16); a tile that does not fit is
+// handled as a dense tile.
 hipError_t launch_diff(const DiffParam* d_table, const DiffParam& single, int32_t nparams,
                        int64_t total_tiles, void* idx, bool global_idx, uint16_t* val,
                        int64_t capacity, int64_t* nnz, int64_t* offsets, void* ws,
-                       const WsLayout& L, hipStream_t stream);
+                       const WsLayout& L, uint64_t arena_quads, hipStream_t stream);
+// The arena a workspace of ws_bytes leaves after the fixed regions.
+uint64_t arena_quads_for(const WsLayout& L, size_t ws_bytes);
 
 // total_elems: the elements of all snapshots of the launch (the kernel is
 // chosen by the delta's size and its density bound max_nnz / total_elems).

@@ -70,14 +70,27 @@ def workspace_size(total_elems: int, nparams: int) -> int:
 
 def workspace(nbytes: int, device: torch.device) -> torch.Tensor:
     """A cached uint8 workspace per (device, stream), grown on demand.  Calls
-    sharing a stream are ordered, so they may share it."""
+    sharing a stream are ordered, so they may share it; release_workspaces()
+    drops the cache."""
     device = torch.device(device)
     key = (device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
+        _workspaces.pop(key, None)  # the old buffer goes back to torch first
         ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
+
+
+def release_workspaces() -> None:
+    """Drop every cached workspace (after the streams that used them have
+    passed their calls, e.g. after a synchronize)."""
+    _workspaces.clear()
+
+
+def diff_workspace_size(total_elems: int, nparams: int, capacity: int) -> int:
+    """The diff's workspace for a delta of at most `capacity` entries."""
+    return int(load().delta_workspace_size_for(int(total_elems), int(nparams), int(capacity)))
 
 
 def default_capacity(n: int) -> int:
@@ -99,9 +112,9 @@ def diff(old: torch.Tensor, new: torch.Tensor, capacity: int | None = None):
     dev = old.device
     lib = load()
     cap = default_capacity(n) if capacity is None else int(capacity)
-    ws = workspace(lib.delta_workspace_size(n, 1), dev)
     nnz = torch.empty(1, dtype=torch.int64, device=dev)
     while True:
+        ws = workspace(lib.delta_workspace_size_for(n, 1, cap), dev)
         idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
         val = torch.empty(max(cap, 1), dtype=torch.bfloat16, device=dev)
         check(lib.delta_diff(_ptr(old), _ptr(new), n, _ptr(idx), _ptr(val), cap, _ptr(nnz),
@@ -140,7 +153,6 @@ def diff_many(olds: Sequence[torch.Tensor], news: Sequence[torch.Tensor],
     total = sum(numels)
     lib = load()
     cap = default_capacity(total) if capacity is None else int(capacity)
-    ws = workspace(lib.delta_workspace_size(total, k), dev)
     optrs = (ctypes.c_void_p * k)(*[o.data_ptr() for o in olds])
     nptrs = (ctypes.c_void_p * k)(*[x.data_ptr() for x in news])
     nums = (ctypes.c_int64 * k)(*numels)
@@ -149,6 +161,7 @@ def diff_many(olds: Sequence[torch.Tensor], news: Sequence[torch.Tensor],
     fos = None if flat_offsets is None else (ctypes.c_int64 * k)(*[int(f) for f in flat_offsets])
     idx_dtype = torch.int32 if fos is None else torch.int64
     while True:
+        ws = workspace(lib.delta_workspace_size_for(total, k, cap), dev)
         idx = torch.empty(max(cap, 1), dtype=idx_dtype, device=dev)
         val = torch.empty(max(cap, 1), dtype=torch.bfloat16, device=dev)
         if fos is None:

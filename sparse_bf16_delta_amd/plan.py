@@ -46,7 +46,9 @@ class DiffPlan:
         self._nums = (ctypes.c_int64 * k)(*self.numels)
         lib = load()
         dev = self.device
-        self.ws = torch.empty(lib.delta_workspace_size(self.total, k), dtype=torch.uint8, device=dev)
+        # the minimum plus a staging arena for `capacity` entries
+        self.ws = torch.empty(lib.delta_workspace_size_for(self.total, k, self.capacity),
+                              dtype=torch.uint8, device=dev)
         if flat_offsets is not None and (len(flat_offsets) != k or
                                          any(int(f) < 0 for f in flat_offsets)):
             raise ValueError("need one flat offset >= 0 per parameter")

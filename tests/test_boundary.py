@@ -53,11 +53,11 @@ def test_workspace_size():
     b = lib.delta_workspace_size(1 << 30, 1)
     c = lib.delta_workspace_size(1 << 30, 300)
     assert 0 < a < b < c
-    # per 32768-element tile: a 4 KB staging slot and 16 KB of staging arena,
-    # count, prefix, dense-list entry, a 32-byte descriptor and an 8-byte arena
-    # position; each extra parameter may add a partial tile and a 32-byte
-    # table entry
-    per_tile = 4096 + 16384 + 4 + 4 + 4 + 32 + 8
+    # per 32768-element tile: a 2 KB staging slot and 16 KB of staging arena
+    # (its worst case), count, prefix, dense-list entry, a 32-byte descriptor
+    # and an 8-byte arena position; each extra parameter may add a partial
+    # tile and a 32-byte table entry
+    per_tile = 2048 + 16384 + 4 + 4 + 4 + 32 + 8
     tiles = (1 << 30) // 32768
     assert b >= per_tile * tiles
     # no more than the layout needs: the slots start past a 1 MB boundary
@@ -243,9 +243,10 @@ def test_noalloc_diff_argument_checks():
     arguments, before anything reaches the GPU."""
     lib = _abi.load()
     top = lib.delta_diff_noalloc_max_elems()
-    assert top == 1 << 26
-    # the scratch layout for the largest accepted tensor stays within 48 MiB
-    assert lib.delta_workspace_size(top, 1) <= 48 << 20
+    assert top == 1 << 28
+    # the fixed scratch regions for the largest accepted tensor leave a
+    # staging arena of at least a quarter of the 48 MiB
+    assert lib.delta_workspace_size_for(top, 1, 0) <= 36 << 20
     one = ctypes.c_void_p(16)
     assert lib.delta_diff_noalloc(one, one, top + 1, one, one, 5, one, None) == _abi.DELTA_E_RANGE
     assert "static scratch" in _err(lib)
@@ -254,3 +255,24 @@ def test_noalloc_diff_argument_checks():
     assert lib.delta_diff_noalloc(one, one, 10, one, one, 5, None, None) == _abi.DELTA_E_INVALID
     assert lib.delta_diff_noalloc(None, one, 10, one, one, 5, one, None) == _abi.DELTA_E_INVALID
     assert lib.delta_diff_noalloc(one, one, 10, None, one, 5, one, None) == _abi.DELTA_E_INVALID
+
+
+def test_workspace_sizes_from_capacity():
+    """The minimum workspace holds no arena; a capacity adds 4 bytes per kept
+    entry (plus quad rounding per tile) up to the worst case."""
+    lib = _abi.load()
+    n, k = 6_738_415_616, 291
+    worst = lib.delta_workspace_size(n, k)
+    low = lib.delta_workspace_size_for(n, k, 0)
+    mid = lib.delta_workspace_size_for(n, k, 80_000_000)
+    assert low < mid < worst
+    assert 4 * 80_000_000 <= mid - low <= 4 * 80_000_000 + 16 * (n // 32768 + k + 1) + 256
+    assert lib.delta_workspace_size_for(n, k, n) == worst
+    assert mid < 1 << 30  # the 7B-shaped list at the bench's capacity
+    assert lib.delta_workspace_size_for(-1, 1, 0) == 0
+    assert lib.delta_workspace_size_for(1, 1, -1) == 0
+    # a diff accepts the minimum and rejects one byte less, before any launch
+    one = ctypes.c_void_p(16)
+    m1 = lib.delta_workspace_size_for(1 << 20, 1, 0)
+    assert lib.delta_diff(one, one, 1 << 20, one, one, 5, one, ctypes.c_void_p(256), m1 - 1,
+                          None) == _abi.DELTA_E_WORKSPACE

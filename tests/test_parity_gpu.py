@@ -81,9 +81,11 @@ def test_diff_unaligned_views(sbd, oracle_mod, pad_old, pad_new, n):
     assert np.array_equal(np_bits(gv), rv)
 
 
-# changes per tile, straddling the compact-slot (1024), wide-slot (4096) and
-# dense limits; the last tile is ragged (5000 of 32768 elements, all changed)
-TILE_COUNTS = [0, 1, 1023, 1024, 1025, 4095, 4096, 4097, TILE, 3, TILE // 2, 1027, 5000]
+# changes per tile, straddling the compact-slot (512), arena (4096) and dense
+# limits, plus 1023-1025 (the compact limit of an earlier layout); the last
+# tile is ragged (5000 of 32768 elements, all changed)
+TILE_COUNTS = [0, 1, 1023, 1024, 1025, 4095, 4096, 4097, TILE, 3, TILE // 2, 1027, 511, 512,
+               513, 5000]
 
 
 def tile_kinds_case(seed, counts=TILE_COUNTS, last_valid=5000):
@@ -155,6 +157,68 @@ def test_diff_arena_mixed_tiles_repeated(sbd, oracle_mod, seed):
             assert np.array_equal(offsets.cpu().numpy(), ro2)
             assert np.array_equal(idx.cpu().numpy(), ri2)
             assert np.array_equal(np_bits(val), rv2)
+
+
+@pytest.mark.parametrize("arena", ["none", "some", "capacity"])
+@pytest.mark.parametrize("seed", [51, 52])
+def test_diff_arena_size_does_not_change_the_delta(sbd, oracle_mod, arena, seed):
+    """The staging arena is whatever the workspace holds past its minimum:
+    none at all, a few tiles' worth, or the size the capacity asks for.
+    Tiles that find no room (staged or dense) are recomputed from both
+    inputs; the delta equals the oracle's in every case, as one tensor and
+    as a list, and a capacity cut still writes nothing past the capacity."""
+    from sparse_bf16_delta_amd import _abi
+    from sparse_bf16_delta_amd.ops import _ptr, _stream
+
+    rng = np.random.default_rng(seed)
+    ntiles = 120
+    counts = rng.choice([0, 5, 511, 512, 513, 800, 2000, 4096, 4097, 9000, TILE], size=ntiles)
+    old, new = tile_kinds_case(seed, counts=list(counts), last_valid=TILE)
+    ri, rv = oracle_mod.diff(old, new)
+    n = old.size
+    lib = _abi.load()
+    o, x = gpu_bits(old), gpu_bits(new)
+    low = lib.delta_workspace_size_for(n, 1, 0)
+    size = {"none": low, "some": low + 48 * 1024,
+            "capacity": lib.delta_workspace_size_for(n, 1, ri.size)}[arena]
+    ws = torch.empty(size, dtype=torch.uint8, device="cuda")
+    for cap in (ri.size + 10, ri.size // 2):
+        guard = 4096
+        idx = torch.full((cap + guard,), -7, dtype=torch.int32, device="cuda")
+        val = torch.full((cap + guard,), -7, dtype=torch.int16, device="cuda")
+        nnz = torch.zeros(1, dtype=torch.int64, device="cuda")
+        _abi.check(lib.delta_diff(_ptr(o), _ptr(x), n, _ptr(idx), _ptr(val), cap, _ptr(nnz),
+                                  _ptr(ws), ws.numel(), _stream(o.device)))
+        m = min(cap, ri.size)
+        assert int(nnz.item()) == ri.size
+        assert np.array_equal(idx[:m].cpu().numpy(), ri[:m])
+        assert np.array_equal(np_bits(val[:m]), rv[:m])
+        assert bool((idx[m:] == -7).all()) and bool((val[m:] == -7).all())
+    # the list form, parameters cut across tiles, with the same arena budget
+    cuts = [0, 7 * TILE + 5, 30 * TILE, 31 * TILE + 1, 90 * TILE + 333, n]
+    olds = [gpu_bits(old[a:b]) for a, b in zip(cuts, cuts[1:])]
+    news = [gpu_bits(new[a:b]) for a, b in zip(cuts, cuts[1:])]
+    k = len(olds)
+    lowk = lib.delta_workspace_size_for(n, k, 0)
+    sizek = {"none": lowk, "some": lowk + 48 * 1024,
+             "capacity": lib.delta_workspace_size_for(n, k, ri.size)}[arena]
+    wsk = torch.empty(sizek, dtype=torch.uint8, device="cuda")
+    import ctypes
+    optrs = (ctypes.c_void_p * k)(*[t.data_ptr() for t in olds])
+    nptrs = (ctypes.c_void_p * k)(*[t.data_ptr() for t in news])
+    nums = (ctypes.c_int64 * k)(*[t.numel() for t in olds])
+    idx = torch.full((ri.size,), -7, dtype=torch.int32, device="cuda")
+    val = torch.full((ri.size,), -7, dtype=torch.int16, device="cuda")
+    nnzk = torch.zeros(k, dtype=torch.int64, device="cuda")
+    offk = torch.zeros(k + 1, dtype=torch.int64, device="cuda")
+    _abi.check(lib.delta_diff_many(k, optrs, nptrs, nums, _ptr(idx), _ptr(val), ri.size,
+                                   _ptr(nnzk), _ptr(offk), _ptr(wsk), wsk.numel(),
+                                   _stream(o.device)))
+    ri2, rv2, rn2, ro2 = oracle_mod.diff_many([old[a:b] for a, b in zip(cuts, cuts[1:])],
+                                              [new[a:b] for a, b in zip(cuts, cuts[1:])])
+    assert np.array_equal(offk.cpu().numpy(), ro2)
+    assert np.array_equal(idx.cpu().numpy(), ri2)
+    assert np.array_equal(np_bits(val), rv2)
 
 
 @pytest.mark.parametrize("cut", [1024 + 1023 + 1, 1 + 1023 + 1024 + 1025 + 4095 + 7,
