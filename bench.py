@@ -35,9 +35,10 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 METRIC = "GB/s of bf16 weights diffed+compacted and applied; % of MI355X HBM peak"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "sparse_bf16_delta_amd", "csrc")
-# HBM bytes measured by rocprofv3 counters, per kernel, for the default
-# workload; valid only while the kernel sources hash to the recorded value.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llama7b_traffic.json")
+# HBM bytes measured by rocprofv3 counters, per kernel and launch, for a
+# workload (profiles/<workload>_traffic.json); valid only while the kernel
+# sources hash to the recorded value.
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "delta_diff_many": ("diff.hip", "sbd_internal.h"),
     "delta_apply_many": ("apply.hip", "sbd_internal.h"),
@@ -57,10 +58,11 @@ def source_hash(kernel):
 
 
 def measured_traffic(workload_key):
-    """{kernel: bytes per launch} from the committed counter summary, for the
-    kernels whose sources are unchanged since the counters were taken."""
+    """{kernel: bytes per launch} from the committed counter summary of the
+    workload, for the kernels whose sources are unchanged since the counters
+    were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(PROFILES, workload_key.split(":")[0] + "_traffic.json")) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return {}
@@ -105,6 +107,9 @@ def parse():
                          "memory: copy only, copy then apply, and the streamed pipeline")
     ap.add_argument("--chunks", type=int, default=8,
                     help="--receiver: parameter chunks of the streamed sparse receiver")
+    ap.add_argument("--sweep-case", default=None,
+                    help="sweep256m: run one case only, as pattern:density (e.g. uniform:0.01), "
+                         "so a profiler sees that case alone")
     ap.add_argument("--shards", type=int, default=0,
                     help="W > 0: time delta_diff_many_sharded for each rank of a W-way Shard(0) "
                          "split of the list, one rank after another (table on stderr)")
@@ -813,8 +818,18 @@ def density_sweep(args, props):
     log(f"[bench] density sweep, {n:,} elements, {reps} reps per op")
     log(f"[bench] {'pattern':9s} {'density':>8s} {'changed':>11s} {'diff ms':>8s} {'%pk':>5s} "
         f"{'apply ms':>9s} {'%pk':>5s} {'xor_mask':>9s} {'xor_apply':>10s} {'sparse/xor':>10s}")
+    only = None
+    if args.sweep_case:
+        pat, _, dens = args.sweep_case.partition(":")
+        only = (pat, float(dens))
+        if pat not in ("uniform", "clustered") or only[1] not in workloads.DENSITIES:
+            print(f"bench.py: --sweep-case {args.sweep_case}: pattern uniform or clustered, "
+                  f"density one of {workloads.DENSITIES}", file=sys.stderr)
+            sys.exit(2)
     for pattern in ("uniform", "clustered"):
         for di, frac in enumerate(workloads.DENSITIES):
+            if only is not None and (pattern, frac) != only:
+                continue
             old, new, k = workloads.density_case(n, frac, pattern, di, device=dev)
             snap = old.clone()
             mask = torch.empty(n, dtype=torch.int16, device=dev)
@@ -976,12 +991,15 @@ def layer_stream_run(args, props):
     g128 = sum(x["g128"] for x in L)
     alg = [4 * n_model + 6 * nnz_total, 6 * nnz_total + 256 * g128, 6 * n_alloc,
            2 * n_alloc + 256 * g128]
+    traffic = measured_traffic(f"{cfg.key}:{mode}:{lr:g}")  # per launch, i.e. per layer
     kernels = []
     for name, ms, b in zip(names, op_ms, alg):
         gbs = b / (ms * 1e-3) / 1e9
+        t = traffic.get(name) * layers if traffic.get(name) else None
         kernels.append({"kernel": name, "ms": round(ms, 3), "launches": layers, "alg_bytes": b,
                         "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
-                        "traffic": None})
+                        "traffic": t,
+                        "moved_frac": round(t / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if t else None})
         log(f"[bench] {name:17s} {ms:9.3f} ms per step ({layers} launches)  {gbs:8.1f} GB/s "
             f"({100 * gbs / HBM_PEAK_GBS:.1f} % of peak)")
     dom = max(range(4), key=lambda i: op_ms[i])
@@ -999,8 +1017,9 @@ def layer_stream_run(args, props):
                    "step": "per layer: xor_mask, diff_many, apply_many, xor_apply, in place"},
         "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": kernels[dom]["achieved_gbs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["frac"],
-                     "traffic": None},
+                     "traffic": kernels[dom]["traffic"]},
         "kernels": kernels,
+        "sparse_sync_gbs": round(2 * n_model / ((op_ms[0] + op_ms[1]) * 1e-3) / 1e9, 2),
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None)},
         "cpu_baseline": None,
     }
