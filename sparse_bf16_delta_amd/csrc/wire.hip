@@ -93,6 +93,7 @@ __global__ __launch_bounds__(kWireBlock) void wire_code_kernel(
       int64_t seg_end = offsets[p + 1];
       int w = widths[p];
       int64_t base = pos_offsets[p] - offsets[p] * w;  // byte of entry j is base + j * w
+      int64_t span_lo = kDecode ? pos_offsets[p] : 0;
       int64_t span_end = kDecode ? pos_offsets[p + 1] : 0;
       int64_t bad = 0;
 #pragma unroll
@@ -105,13 +106,15 @@ __global__ __launch_bounds__(kWireBlock) void wire_code_kernel(
             } while (seg_end <= j);
             w = widths[p];
             base = pos_offsets[p] - offsets[p] * w;
-            if constexpr (kDecode) span_end = pos_offsets[p + 1];
+            if constexpr (kDecode) {
+              span_lo = pos_offsets[p];
+              span_end = pos_offsets[p + 1];
+            }
           }
           const int64_t at = base + j * w;
           auto half = reinterpret_cast<uint16_t*>(positions + at);
           if constexpr (kDecode) {
-            const int64_t first = pos_offsets[p];
-            if (at >= first && at >= 0 && at + w <= span_end && at + w <= positions_capacity &&
+            if (at >= span_lo && at >= 0 && at + w <= span_end && at + w <= positions_capacity &&
                 (at & 1) == 0) {
               uint32_t v = *global_ptr(half);
               if (w == 4) v |= uint32_t(*global_ptr(half + 1)) << 16;
@@ -330,6 +333,7 @@ __global__ __launch_bounds__(kWireBlock) void wire_blocked_decode_kernel(
     const uint8_t* __restrict__ in, int64_t in_bytes, const int64_t* __restrict__ offsets,
     int64_t max_entries, int32_t* __restrict__ idx, unsigned long long* __restrict__ violations) {
   __shared__ int32_t s_p0;
+  __shared__ int64_t s_b0;  // the block of the chunk's first entry in parameter s_p0
   __shared__ int64_t s_total;
   const auto words = global_ptr(reinterpret_cast<const uint32_t*>(in));
   const int64_t lows = 4 * nblocks;
@@ -341,7 +345,21 @@ __global__ __launch_bounds__(kWireBlock) void wire_blocked_decode_kernel(
       const int64_t total = t < max_entries ? t : max_entries;
       if (j0 < total) {
         const int32_t p0 = find_param_wave0(offsets, nparams, j0);
-        if (threadIdx.x == 0) s_p0 = p0;
+        if (threadIdx.x == 0) {
+          s_p0 = p0;
+          // last block whose base is <= the first entry's place in its parameter
+          const int64_t local = j0 - offsets[p0];
+          const int64_t tb = bp[p0].tbase;
+          int64_t lo = 0, hi = (bp[p0].numel + kPosBlockElems - 1) / kPosBlockElems - 1;
+          while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) >> 1;
+            if (int64_t(words[tb + mid]) <= local)
+              lo = mid;
+            else
+              hi = mid - 1;
+          }
+          s_b0 = lo < 0 ? 0 : lo;
+        }
       }
       if (threadIdx.x == 0) s_total = total;
     }
@@ -351,7 +369,9 @@ __global__ __launch_bounds__(kWireBlock) void wire_blocked_decode_kernel(
       int32_t p = s_p0;
       int64_t seg_end = offsets[p + 1];
       int64_t first = offsets[p];
-      int64_t nb = (bp[p].numel + kPosBlockElems - 1) / kPosBlockElems, tb = bp[p].tbase, b = -1;
+      // the chunk's entries in s_p0 start from its first entry's block and walk forward
+      int64_t numel = bp[p].numel, tb = bp[p].tbase, b = s_b0;
+      int64_t nb = (numel + kPosBlockElems - 1) / kPosBlockElems;
       int64_t bad = 0;
 #pragma unroll 4
       for (int r = 0; r < kWirePer; ++r) {
@@ -362,13 +382,18 @@ __global__ __launch_bounds__(kWireBlock) void wire_blocked_decode_kernel(
               seg_end = offsets[++p + 1];
             } while (seg_end <= j);
             first = offsets[p];
-            nb = (bp[p].numel + kPosBlockElems - 1) / kPosBlockElems;
+            numel = bp[p].numel;
+            nb = (numel + kPosBlockElems - 1) / kPosBlockElems;
             tb = bp[p].tbase;
             b = -1;
           }
           const int64_t local = j - first;
-          if (b < 0) {  // last block whose base is <= local
-            int64_t lo = 0, hi = nb - 1;
+          // last block whose base is <= local: one step forward from the
+          // cursor covers dense data; a search over the rest covers sparse
+          int64_t lo = b < 0 ? 0 : b;
+          if (b >= 0 && b + 1 < nb && int64_t(words[tb + b + 1]) <= local) lo = b + 1;
+          if (b < 0 || (lo + 1 < nb && int64_t(words[tb + lo + 1]) <= local)) {
+            int64_t hi = nb - 1;
             while (lo < hi) {
               const int64_t mid = (lo + hi + 1) >> 1;
               if (int64_t(words[tb + mid]) <= local)
@@ -376,15 +401,13 @@ __global__ __launch_bounds__(kWireBlock) void wire_blocked_decode_kernel(
               else
                 hi = mid - 1;
             }
-            b = lo;
-          } else {
-            while (b + 1 < nb && int64_t(words[tb + b + 1]) <= local) ++b;
           }
+          b = lo;
           const int64_t at = lows + 2 * j;
           int64_t v = -1;
           if (nb > 0 && at + 2 <= in_bytes) {
             v = b * kPosBlockElems + int64_t(*global_ptr(reinterpret_cast<const uint16_t*>(in + at)));
-            if (v >= bp[p].numel) v = -1;
+            if (v >= numel) v = -1;
           }
           idx[j] = static_cast<int32_t>(v);
           bad += v < 0 ? 1 : 0;
