@@ -658,8 +658,11 @@ void launch_place(const TileDesc* tdesc, const DiffParam& single, int64_t total_
                   const uint32_t* compact, const uint32_t* wide, const int32_t* dense_list,
                   const uint32_t* ndense, IdxT* idx, uint16_t* val, int64_t capacity,
                   const uint64_t* tile_pos, hipStream_t stream) {
-  // enough placing workgroups to fill the GPU, up to kPlaceTiles tiles each
-  int64_t per_wg = total_tiles / 2048;
+  // about 8192 placing workgroups (up to kPlaceTiles tiles each): several
+  // rounds of the GPU, so no long tail (on the Qwen3-0.6B-shaped list at 8 %,
+  // the whole diff: 0.582 ms with 2048 workgroups of 8 tiles, 0.564 with
+  // 8192 of 2; more entries in flight per lane was slower)
+  int64_t per_wg = total_tiles / 8192;
   per_wg = per_wg < 1 ? 1 : (per_wg > kPlaceTiles ? kPlaceTiles : per_wg);
   const unsigned place_grid = static_cast<unsigned>((total_tiles + per_wg - 1) / per_wg);
   const int64_t dense_max = dense_grid_limit<kMany, IdxT>();
