@@ -12,12 +12,14 @@
 // waits for another one.
 //  1. Count and stage.  One workgroup of 512 lanes (eight wave64s) per tile
 //     of 32768 elements; a tile never straddles a parameter.  A lane loads
-//     eight 16-byte chunks of `old` and eight of `new`; three such workgroups
-//     share a CU.  Per 16-byte chunk the lane forms an
-//     8-bit change mask; its popcount is prefix-summed across the wave with
-//     four ballots over its bits plus mbcnt, and the 64 (iteration, wave)
-//     group totals are scanned in LDS, giving every change its slot inside
-//     the tile in ascending element order.  A tile with at most 4096 changes
+//     eight 16-byte chunks of `old` and eight of `new`, in two halves of four
+//     one after the other, so that four such workgroups share a CU (all
+//     sixteen at once held the registers of only three: 2-4 % slower on the
+//     7B-shaped list at 1.2 % and 11.6 % density).  Per 16-byte chunk the
+//     lane forms an 8-bit change mask; its popcount is prefix-summed across
+//     the wave with four ballots over its bits plus mbcnt, and each half's 32
+//     (iteration, wave) group totals are scanned in LDS, giving every change
+//     its slot inside the tile in ascending element order.  A tile with at most 4096 changes
 //     is compacted in LDS as (tile-local index << 16 | new bits) and copied
 //     with 16-byte nontemporal stores: a tile with up to 512 changes into a
 //     2 KB workspace slot of its own, a tile with more into a staging arena
@@ -41,11 +43,17 @@
 //     outputs, so this is one contiguous run of coalesced idx and val
 //     stores.  Dense tiles are re-read (`new` only, steered by the stored
 //     mask) and written directly by a second, small grid.
-// Why not a single pass with a decoupled look-back: waiting for the
-// predecessors' prefix holds a workgroup's registers and LDS while its loads
-// are done, which keeps the next tile's loads from being issued; measured on
-// the 7B-shaped list it cost more than the 8 extra bytes per changed element
-// that the slot round trip adds here.
+// Why not a single pass with a look-back, in which a tile that learns the
+// count of all tiles before it writes its entries in place: the tiles'
+// states live in memory that workgroups on all eight XCDs read, so every
+// read is a device-scope round trip, and a workgroup that waits holds its
+// registers and LDS, which keeps the next tile's loads from being issued.
+// Measured on the 7B-shaped list at 1.2 % (diff, ms): three phases 4.73; a
+// bounded look-back where every tile placed itself after 1-3 reads of its
+// 512 predecessors' states 6.85; a single read with staging as the fallback
+// (7-15 % of the tiles placed) 5.07.  At 8 % and 11.6 % density the same
+// look-backs cost 10-20 %, more than the 8 bytes per changed element that
+// the staging round trip adds.
 // Traffic: the 4n-byte read happens once; a staged tile adds 4 bytes written
 // and 4 read per changed element, a dense tile re-reads `new` (2 bytes per
 // element; both inputs if its mask found no room), and the tile count,
@@ -178,27 +186,90 @@ __device__ __forceinline__ TileView tile_view(const TileDesc* __restrict__ tdesc
 // order -- iteration-major, then wave, then lane, then slot -- (goff), and the
 // tile's count (agg), in every lane; gexcl is the offset of group `lane`.
 // Contains one barrier; s_wtot must not be in use by other waves.
-__device__ __forceinline__ void tile_offsets(const uint32_t (&m)[kDiffIters],
-                                             uint32_t (&lp)[kDiffIters],
-                                             uint32_t (&goff)[kDiffIters], uint32_t& agg,
-                                             uint32_t& gexcl, uint32_t* s_wtot, int lane,
-                                             int wave) {
+template <int N>
+__device__ __forceinline__ void tile_offsets(const uint32_t (&m)[N], uint32_t (&lp)[N],
+                                             uint32_t (&goff)[N], uint32_t& agg, uint32_t& gexcl,
+                                             uint32_t* s_wtot, int lane, int wave) {
+  static_assert(N * kDiffWaves <= 64, "one group per lane of a wave");
 #pragma unroll
-  for (int j = 0; j < kDiffIters; ++j) {
+  for (int j = 0; j < N; ++j) {
     uint32_t tot;
     lp[j] = wave_prefix_c(static_cast<uint32_t>(__popc(m[j])), tot);
     if (lane == 0) s_wtot[j * kDiffWaves + wave] = tot;
   }
   __syncthreads();
   // every wave scans the 64 group totals itself: no second barrier
-  const uint32_t own = lane < kGroups ? s_wtot[lane] : 0u;
+  const uint32_t own = lane < N * kDiffWaves ? s_wtot[lane] : 0u;
   const uint32_t inc = wave_inclusive(own, lane);
   const uint32_t excl = inc - own;
   gexcl = excl;
   agg = static_cast<uint32_t>(__shfl(static_cast<int>(inc), 63, 64));
 #pragma unroll
-  for (int j = 0; j < kDiffIters; ++j)
+  for (int j = 0; j < N; ++j)
     goff[j] = static_cast<uint32_t>(__shfl(static_cast<int>(excl), j * kDiffWaves + wave, 64));
+}
+
+// One half of a tile in the count kernel: iterations [H * kHalfIters,
+// (H + 1) * kHalfIters), which hold the tile's elements [H * kDiffTile / 2,
+// (H + 1) * kDiffTile / 2).  Loads both inputs, stores the lanes' change masks
+// into m, and, if `stage` and the tile's entries so far fit, stages this
+// half's entries in LDS after the `base` entries of the halves before it.
+// Returns the half's count (uniform).  Contains one barrier; s_wtot must not
+// be in use by other waves.
+constexpr int kHalfIters = kDiffIters / 2;
+static_assert(kHalfIters * 2 == kDiffIters, "a tile is two halves");
+template <int H>
+__device__ __forceinline__ uint32_t count_half(const TileView& tv, bool vec, int tid, int lane,
+                                               int wave, uint32_t (&m)[kDiffIters], uint32_t base,
+                                               bool stage, uint32_t* s_wtot, uint32_t* s_stage) {
+  uint4 nv[kHalfIters];
+  uint32_t mh[kHalfIters];
+  if (vec) {
+    const uint4* o4 = reinterpret_cast<const uint4*>(tv.ob) + H * kHalfIters * kDiffBlock + tid;
+    const uint4* n4 = reinterpret_cast<const uint4*>(tv.nb) + H * kHalfIters * kDiffBlock + tid;
+    uint4 ov[kHalfIters];
+#pragma unroll
+    for (int j = 0; j < kHalfIters; ++j) {
+      ov[j] = load16_stream(o4 + j * kDiffBlock);
+      nv[j] = load16_stream(n4 + j * kDiffBlock);
+    }
+#pragma unroll
+    for (int j = 0; j < kHalfIters; ++j) mh[j] = change_mask8(ov[j], nv[j]);
+  } else {
+    // ragged last tile or unaligned parameter
+#pragma unroll
+    for (int j = 0; j < kHalfIters; ++j) {
+      const int local = (H * kHalfIters + j) * kDiffBlock * kVec + tid * kVec;
+      const uint4 o = load_chunk(tv.ob, local, tv.valid, false);
+      nv[j] = load_chunk(tv.nb, local, tv.valid, false);
+      mh[j] = change_mask8(o, nv[j]);
+    }
+  }
+  uint32_t lp[kHalfIters], goff[kHalfIters], agg, gexcl;
+  tile_offsets<kHalfIters>(mh, lp, goff, agg, gexcl, s_wtot, lane, wave);
+  if (stage && base + agg <= static_cast<uint32_t>(kStageCap)) {
+#pragma unroll
+    for (int j = 0; j < kHalfIters; ++j) {
+      const uint32_t mm = mh[j];
+      if (mm != 0u) {
+        uint32_t pos = base + goff[j] + lp[j];
+        const uint32_t local =
+            static_cast<uint32_t>((H * kHalfIters + j) * kDiffBlock * kVec + tid * kVec);
+        const uint4 x = nv[j];
+        stage_slot<0>(mm, pos, local, x, s_stage);
+        stage_slot<1>(mm, pos, local, x, s_stage);
+        stage_slot<2>(mm, pos, local, x, s_stage);
+        stage_slot<3>(mm, pos, local, x, s_stage);
+        stage_slot<4>(mm, pos, local, x, s_stage);
+        stage_slot<5>(mm, pos, local, x, s_stage);
+        stage_slot<6>(mm, pos, local, x, s_stage);
+        stage_slot<7>(mm, pos, local, x, s_stage);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kHalfIters; ++j) m[H * kHalfIters + j] = mh[j];
+  return agg;
 }
 
 // For a parameter list: every tile's descriptor (base pointers, first index,
@@ -247,7 +318,8 @@ __global__ __launch_bounds__(kDiffBlock) void diff_count_kernel(
     uint64_t* __restrict__ tile_pos, unsigned long long* __restrict__ ctr, uint64_t arena_quads) {
   __shared__ __attribute__((aligned(16))) uint32_t s_stage[kStageCap];
   __shared__ uint64_t s_pos;
-  __shared__ uint32_t s_wtot[kGroups];
+  __shared__ uint32_t s_wtot[kHalfIters * kDiffWaves];
+  __shared__ uint32_t s_wtot2[kHalfIters * kDiffWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -258,32 +330,15 @@ __global__ __launch_bounds__(kDiffBlock) void diff_count_kernel(
                    ((reinterpret_cast<uintptr_t>(tv.ob) | reinterpret_cast<uintptr_t>(tv.nb)) &
                     15u) == 0;
 
-  uint4 nv[kDiffIters];
+  // The tile in two halves, one after the other: half the tile's data is in
+  // registers at a time, so more workgroups share a CU; the tile still takes
+  // one count, one arena position and one copy-out.
   uint32_t m[kDiffIters];
-  if (vec) {
-    const uint4* o4 = reinterpret_cast<const uint4*>(tv.ob) + tid;
-    const uint4* n4 = reinterpret_cast<const uint4*>(tv.nb) + tid;
-    uint4 ov[kDiffIters];
-#pragma unroll
-    for (int j = 0; j < kDiffIters; ++j) {
-      ov[j] = load16_stream(o4 + j * kDiffBlock);
-      nv[j] = load16_stream(n4 + j * kDiffBlock);
-    }
-#pragma unroll
-    for (int j = 0; j < kDiffIters; ++j) m[j] = change_mask8(ov[j], nv[j]);
-  } else {
-    // ragged last tile or unaligned parameter
-#pragma unroll
-    for (int j = 0; j < kDiffIters; ++j) {
-      const int local = j * kDiffBlock * kVec + tid * kVec;
-      const uint4 o = load_chunk(tv.ob, local, tv.valid, false);
-      nv[j] = load_chunk(tv.nb, local, tv.valid, false);
-      m[j] = change_mask8(o, nv[j]);
-    }
-  }
-
-  uint32_t lp[kDiffIters], goff[kDiffIters], agg, gexcl;
-  tile_offsets(m, lp, goff, agg, gexcl, s_wtot, lane, wave);
+  const uint32_t agg0 =
+      count_half<0>(tv, vec, tid, lane, wave, m, 0u, true, s_wtot, s_stage);
+  const uint32_t agg1 = count_half<1>(tv, vec, tid, lane, wave, m, agg0,
+                                      agg0 <= static_cast<uint32_t>(kStageCap), s_wtot2, s_stage);
+  const uint32_t agg = agg0 + agg1;
   const bool staged = agg <= static_cast<uint32_t>(kStageCap);
   const bool in_arena = staged && agg > static_cast<uint32_t>(kCompactCap);
   if (tid == 0) {
@@ -302,25 +357,6 @@ __global__ __launch_bounds__(kDiffBlock) void diff_count_kernel(
     }
     counts[tile] = c;
     if (tile == 0) *ndense = 0u;  // the scan kernel, launched next, lists dense tiles
-  }
-  if (staged) {
-#pragma unroll
-    for (int j = 0; j < kDiffIters; ++j) {
-      const uint32_t mm = m[j];
-      if (mm != 0u) {
-        uint32_t pos = goff[j] + lp[j];
-        const uint32_t local = static_cast<uint32_t>(j * kDiffBlock * kVec + tid * kVec);
-        const uint4 x = nv[j];
-        stage_slot<0>(mm, pos, local, x, s_stage);
-        stage_slot<1>(mm, pos, local, x, s_stage);
-        stage_slot<2>(mm, pos, local, x, s_stage);
-        stage_slot<3>(mm, pos, local, x, s_stage);
-        stage_slot<4>(mm, pos, local, x, s_stage);
-        stage_slot<5>(mm, pos, local, x, s_stage);
-        stage_slot<6>(mm, pos, local, x, s_stage);
-        stage_slot<7>(mm, pos, local, x, s_stage);
-      }
-    }
   }
   __syncthreads();
   const uint64_t at = (!staged || in_arena) ? s_pos : 0;
