@@ -24,8 +24,11 @@
 namespace sbd {
 namespace {
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kWireBlock = 256;
 constexpr int kWirePer = 16;
+static_assert(kWirePer % 4 == 0, "the blocked decode takes four entries per lane");
 constexpr int64_t kWireChunk = int64_t(kWireBlock) * kWirePer;
 constexpr int kScanThreads = 1024;
 
@@ -372,45 +375,99 @@ __global__ __launch_bounds__(kWireBlock) void wire_blocked_decode_kernel(
       // the chunk's entries in s_p0 start from its first entry's block and walk forward
       int64_t numel = bp[p].numel, tb = bp[p].tbase, b = s_b0;
       int64_t nb = (numel + kPosBlockElems - 1) / kPosBlockElems;
+      // the base of the cursor's next block, kept in a register: the table
+      // is read again only when an entry passes it
+      constexpr int64_t kNone = INT64_MAX;
+      int64_t nxt = b + 1 < nb ? int64_t(words[tb + b + 1]) : kNone;
       int64_t bad = 0;
-#pragma unroll 4
-      for (int r = 0; r < kWirePer; ++r) {
-        const int64_t j = j0 + int64_t(r) * kWireBlock + threadIdx.x;
-        if (j < total) {
-          if (seg_end <= j) {
-            do {
-              seg_end = offsets[++p + 1];
-            } while (seg_end <= j);
-            first = offsets[p];
-            numel = bp[p].numel;
-            nb = (numel + kPosBlockElems - 1) / kPosBlockElems;
-            tb = bp[p].tbase;
-            b = -1;
+      // four consecutive entries per lane: one 8-byte (or two 4-byte) load of
+      // their offsets and one 16-byte store of their positions, where the
+      // buffers' alignment allows (uniform over the launch; `in` is 4-byte
+      // aligned, checked on the host, and so is every group of four offsets)
+      const bool off8 = ((reinterpret_cast<uintptr_t>(in) + uintptr_t(lows)) & 7u) == 0;
+      const bool out16 = (reinterpret_cast<uintptr_t>(idx) & 15u) == 0;
+#pragma unroll 2
+      for (int r = 0; r < kWirePer / 4; ++r) {
+        const int64_t jb = j0 + int64_t(r) * kWireBlock * 4 + int64_t(threadIdx.x) * 4;
+        if (jb < total) {
+          const int64_t at = lows + 2 * jb;
+          const bool whole = jb + 4 <= total && at + 8 <= in_bytes;
+          uint32_t o16[4];
+          if (whole && off8) {
+            const u32x2 w = *global_ptr(reinterpret_cast<const u32x2*>(in + at));
+            o16[0] = w.x & 0xFFFFu;
+            o16[1] = w.x >> 16;
+            o16[2] = w.y & 0xFFFFu;
+            o16[3] = w.y >> 16;
+          } else if (whole) {
+            const uint32_t w0 = *global_ptr(reinterpret_cast<const uint32_t*>(in + at));
+            const uint32_t w1 = *global_ptr(reinterpret_cast<const uint32_t*>(in + at + 4));
+            o16[0] = w0 & 0xFFFFu;
+            o16[1] = w0 >> 16;
+            o16[2] = w1 & 0xFFFFu;
+            o16[3] = w1 >> 16;
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              o16[k] = jb + k < total && at + 2 * k + 2 <= in_bytes
+                           ? uint32_t(*global_ptr(reinterpret_cast<const uint16_t*>(in + at + 2 * k)))
+                           : 0xFFFFFFFFu;  // missing: decoded as -1
           }
-          const int64_t local = j - first;
-          // last block whose base is <= local: one step forward from the
-          // cursor covers dense data; a search over the rest covers sparse
-          int64_t lo = b < 0 ? 0 : b;
-          if (b >= 0 && b + 1 < nb && int64_t(words[tb + b + 1]) <= local) lo = b + 1;
-          if (b < 0 || (lo + 1 < nb && int64_t(words[tb + lo + 1]) <= local)) {
-            int64_t hi = nb - 1;
-            while (lo < hi) {
-              const int64_t mid = (lo + hi + 1) >> 1;
-              if (int64_t(words[tb + mid]) <= local)
-                lo = mid;
-              else
-                hi = mid - 1;
+          int32_t out[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int64_t j = jb + k;
+            out[k] = -1;
+            if (j < total) {
+              if (seg_end <= j) {
+                do {
+                  seg_end = offsets[++p + 1];
+                } while (seg_end <= j);
+                first = offsets[p];
+                numel = bp[p].numel;
+                nb = (numel + kPosBlockElems - 1) / kPosBlockElems;
+                tb = bp[p].tbase;
+                b = -1;
+              }
+              const int64_t local = j - first;
+              if (b < 0 || local >= nxt) {
+                // the last block whose base is <= local lies past the cursor:
+                // one step forward covers dense data, a search the rest
+                int64_t lo = b < 0 ? 0 : b + 1;
+                if (b < 0 || (lo + 1 < nb && int64_t(words[tb + lo + 1]) <= local)) {
+                  int64_t hi = nb - 1;
+                  while (lo < hi) {
+                    const int64_t mid = (lo + hi + 1) >> 1;
+                    if (int64_t(words[tb + mid]) <= local)
+                      lo = mid;
+                    else
+                      hi = mid - 1;
+                  }
+                }
+                b = lo;
+                nxt = b + 1 < nb ? int64_t(words[tb + b + 1]) : kNone;
+              }
+              int64_t v = -1;
+              if (nb > 0 && o16[k] <= 0xFFFFu) {
+                v = b * kPosBlockElems + int64_t(o16[k]);
+                if (v >= numel) v = -1;
+              }
+              out[k] = static_cast<int32_t>(v);
+              bad += v < 0 ? 1 : 0;
             }
           }
-          b = lo;
-          const int64_t at = lows + 2 * j;
-          int64_t v = -1;
-          if (nb > 0 && at + 2 <= in_bytes) {
-            v = b * kPosBlockElems + int64_t(*global_ptr(reinterpret_cast<const uint16_t*>(in + at)));
-            if (v >= numel) v = -1;
+          if (jb + 4 <= total && out16) {
+            u32x4 w;
+            w.x = uint32_t(out[0]);
+            w.y = uint32_t(out[1]);
+            w.z = uint32_t(out[2]);
+            w.w = uint32_t(out[3]);
+            *global_ptr(reinterpret_cast<u32x4*>(idx + jb)) = w;
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (jb + k < total) idx[jb + k] = out[k];
           }
-          idx[j] = static_cast<int32_t>(v);
-          bad += v < 0 ? 1 : 0;
         }
       }
       if (violations != nullptr) {

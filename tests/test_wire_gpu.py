@@ -225,3 +225,41 @@ def test_wire_blocked_capacity_and_untrusted_bytes(sbd, oracle_mod):
     assert bad >= 1
     with pytest.raises(sbd.DeltaError, match="malformed"):
         sbd.wire_decode_blocked(torch.from_numpy(want[:-6].copy()).cuda(), off, BLOCKED_NUMELS)
+
+
+@pytest.mark.parametrize("in_shift", [0, 4, 8, 12])
+@pytest.mark.parametrize("out_shift", [0, 1, 3])
+def test_wire_blocked_decode_alignments(sbd, oracle_mod, in_shift, out_shift):
+    """Decode reads its bytes and writes its indices at any alignment the
+    contract allows: blocks placed 0, 4, 8 or 12 bytes past a 16-byte
+    aligned address (the offsets after the tables then start 8- or only
+    4-byte aligned), and indices written from 0, 1 or 3 elements past one,
+    match the oracle; the elements around the output are untouched."""
+    import ctypes
+    from sparse_bf16_delta_amd import _abi
+    from sparse_bf16_delta_amd.ops import _ptr, _stream
+
+    # 2 + 1 + 1 + 3 + 1 = 8 blocks, or 9 with the last parameter: the block
+    # tables end 8- or 4-byte aligned relative to the start
+    numels = [70_000, 3, 65536, 131_073, 9] + ([100] if out_shift == 1 else [])
+    olds, news = delta_case(31 + in_shift + 7 * out_shift, numels, 0.05)
+    ri, rv, rn, ro = oracle_mod.diff_many(olds, news)
+    want = oracle_mod.wire_encode_blocked(ri, ro, numels)
+    lib = _abi.load()
+    k = len(numels)
+    nums = (ctypes.c_int64 * k)(*numels)
+    ws = torch.empty(lib.delta_workspace_size(0, k), dtype=torch.uint8, device="cuda")
+    buf = torch.zeros(want.size + 16, dtype=torch.uint8, device="cuda")
+    buf[in_shift:in_shift + want.size] = torch.from_numpy(want).cuda()
+    data = buf[in_shift:in_shift + want.size]
+    off = torch.from_numpy(ro).cuda()
+    res = torch.full((ri.size + 8,), 77, dtype=torch.int32, device="cuda")
+    out = res[out_shift:out_shift + ri.size]
+    v = torch.full((1,), -1, dtype=torch.int64, device="cuda")
+    _abi.check(lib.delta_wire_decode_blocked(k, nums, _ptr(data), want.size, _ptr(off), ri.size,
+                                             _ptr(out), _ptr(v), _ptr(ws), ws.numel(),
+                                             _stream(off.device)))
+    got = res.cpu().numpy()
+    assert int(v.item()) == 0
+    assert np.array_equal(got[out_shift:out_shift + ri.size], ri)
+    assert np.all(got[:out_shift] == 77) and np.all(got[out_shift + ri.size:] == 77)
