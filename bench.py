@@ -508,6 +508,9 @@ def wire_run(args, props):
     po2 = torch.empty_like(pos_off)
     out = torch.empty_like(idx)
     hashes = torch.empty(2, dtype=torch.int64, device=dev)
+    # decodes are timed as a receiver runs them on untrusted bytes: with the
+    # violation count (and, for the blocked form, the table check) it implies
+    viol = torch.zeros(1, dtype=torch.int64, device=dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
 
     def enc():
@@ -518,7 +521,8 @@ def wire_run(args, props):
     def dec():
         _abi.check(lib.delta_wire_decode(k, nums, pos.data_ptr(), pos.numel(),
                                          pos_off.data_ptr(), offsets.data_ptr(), nnz,
-                                         out.data_ptr(), None, ws.data_ptr(), ws.numel(), sh))
+                                         out.data_ptr(), viol.data_ptr(), ws.data_ptr(),
+                                         ws.numel(), sh))
 
     data2 = torch.empty_like(data)
 
@@ -529,8 +533,8 @@ def wire_run(args, props):
 
     def dec_b():
         _abi.check(lib.delta_wire_decode_blocked(k, nums, data.data_ptr(), data.numel(),
-                                                 offsets.data_ptr(), nnz, out.data_ptr(), None,
-                                                 ws.data_ptr(), ws.numel(), sh))
+                                                 offsets.data_ptr(), nnz, out.data_ptr(),
+                                                 viol.data_ptr(), ws.data_ptr(), ws.numel(), sh))
 
     def hsh():
         _abi.check(lib.delta_wire_hash(pos.data_ptr(), pos.numel(), val.data_ptr(), nnz,
@@ -547,6 +551,9 @@ def wire_run(args, props):
                       "frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"[bench] {name:14s} {ms:8.3f} ms  {b / (ms * 1e-3) / 1e9:8.1f} GB/s "
             f"({100 * rows[name]['frac']:.1f} % of peak)")
+    if int(viol.item()) != 0:
+        print("bench.py: a timed decode found violations in well-formed bytes", file=sys.stderr)
+        sys.exit(1)
     print(json.dumps({
         "metric": "wire encoding of the delta: encode, decode and hash times",
         "value": None, "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
