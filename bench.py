@@ -1009,24 +1009,34 @@ def layer_stream_run(args, props):
                         "moved_frac": round(t / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if t else None})
         log(f"[bench] {name:17s} {ms:9.3f} ms per step ({layers} launches)  {gbs:8.1f} GB/s "
             f"({100 * gbs / HBM_PEAK_GBS:.1f} % of peak)")
-    dom = max(range(4), key=lambda i: op_ms[i])
+    # the step is the sparse-mode sync (diff + apply, as in the default run);
+    # the XOR mode's two ops run interleaved per layer and are reported beside it
+    dom = max(range(2), key=lambda i: op_ms[i])
+    sync_ms = op_ms[0] + op_ms[1]
+    xor_ms = op_ms[2] + op_ms[3]
     result = {
         "metric": METRIC,
-        "value": round(2 * n_model / (ms_step * 1e-3) / 1e9, 2),
+        "value": round(2 * n_model / (sync_ms * 1e-3) / 1e9, 2),
         "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
+        "ms_per_step": round(sync_ms, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "u16", "data": "synthetic",
         "config": {"workload": f"{cfg.title}: {len(numels)} tensors, {n_model} bf16 elements, "
                                f"{mode} step lr {lr:g}, streamed layer by layer",
                    "tensors": len(numels), "layers": layers, "elements": n_model,
                    "changed": nnz_total, "density": round(nnz_total / n_model, 6),
                    "touched_lines_128B": g128,
-                   "step": "per layer: xor_mask, diff_many, apply_many, xor_apply, in place"},
+                   "step": "one sparse-mode sync, layer by layer: diff_many, then apply_many into "
+                           "the resident old (which becomes new); value = one snapshot's bytes "
+                           "per summed diff + apply time (HIP events)"},
         "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": kernels[dom]["achieved_gbs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["frac"],
                      "traffic": kernels[dom]["traffic"]},
         "kernels": kernels,
-        "sparse_sync_gbs": round(2 * n_model / ((op_ms[0] + op_ms[1]) * 1e-3) / 1e9, 2),
+        "xor_mode": {"ms_per_step": round(xor_ms, 3),
+                     "weights_gbs": round(2 * n_model / (xor_ms * 1e-3) / 1e9, 2),
+                     "step": "per layer, around the sync: xor_mask (old, new) into a one-layer "
+                             "mask before it, xor_apply of the mask after it (old comes back)"},
+        "wall_ms_per_step_all_ops": round(ms_step, 3),
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None)},
         "cpu_baseline": None,
     }
