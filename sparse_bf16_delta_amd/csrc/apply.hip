@@ -55,7 +55,7 @@
 //    nontemporal accesses 3.0 ms; 32-byte units 4.0 ms, 128-byte lines 2.73.
 //    In each touched segment four lanes read 16 bytes each, patch them from
 //    the entries (staged in LDS) and write them back; a chunk's segments
-//    (about 860 at 1.2 % density) take a few passes, two in flight per lane.
+//    (about 860 at 1.2 % density) take a few passes, three in flight per lane.
 //  * Snapshot pointers come from the parameter table in memory; they are
 //    cast to the global address space so the stores are global, not flat.
 //  * The parameter of the chunk's first entry comes from one 64-way search
@@ -95,12 +95,13 @@ constexpr int kBigBlock = 1024;
 constexpr int kBigWaves = kBigBlock / 64;
 constexpr int kBigChunk = kBigBlock;
 constexpr int kBigSegPass = kBigBlock / kSegLanes;  // segments rewritten per pass
-// Segments in flight per four lanes: the loads of two passes are issued
+// Segments in flight per four lanes: the loads of three passes are issued
 // before the first pass is patched and written.  On the 7B-shaped delta, one
 // pass at a time 2.69 ms, two 2.60 ms, four 2.78 ms (the floor of the bare
 // read and rewrite of its touched segments, one pass per workgroup, 2.48 ms
-// on that machine).
-constexpr int kBigSegDepth = 2;
+// on that machine); on another, two 2.61, three 2.54, four 2.78 ms, and at
+// 2.4 % density 3.72 / 3.62 / 5.10 ms (at 3.5 %, two and three alike).
+constexpr int kBigSegDepth = 3;
 // At most this many workgroups per launch; each strides over chunks beyond
 // it (2^17 chunks of 1024 entries: a delta of 134 million entries takes one
 // pass).  A launch whose max_nnz (a buffer's capacity) far exceeds the true

@@ -124,6 +124,69 @@ def test_diff_tile_kinds(sbd, oracle_mod, pad):
     assert np.array_equal(np_bits(gv2), rv2)
 
 
+# (changes in the first half, changes in the second half) of each tile: the
+# count kernel loads and stages a tile as two halves of 16384 elements, so a
+# tile's entries may all sit in one half, or the first half may fill or
+# overflow the 4096-entry stage alone
+HALF = TILE // 2
+HALF_COUNTS = [(0, 1), (1, 0), (4096, 0), (0, 4096), (4097, 0), (0, 4097), (4095, 1),
+               (1, 4095), (2048, 2049), (2048, 2048), (512, 0), (0, 513), (HALF, 0), (0, HALF),
+               (600, 600), (0, 0)]
+
+
+def halves_case(seed, pairs=HALF_COUNTS, last_valid=20000):
+    """Tiles with the given per-half counts; elements HALF - 1 and HALF of
+    every tile with changes in both halves are among them (the seam); the
+    last tile is ragged, its second half partial, all of it changed."""
+    rng = np.random.default_rng(seed)
+    n = len(pairs) * TILE + last_valid
+    old = rng.integers(0, 1 << 16, size=n, dtype=np.uint32).astype(np.uint16)
+    new = old.copy()
+    for t, (a, b) in enumerate(pairs):
+        pos = []
+        if a:
+            pa = rng.choice(HALF, size=a, replace=False)
+            if b and (HALF - 1) not in pa:
+                pa[0] = HALF - 1
+            pos.append(pa)
+        if b:
+            pb = HALF + rng.choice(HALF, size=b, replace=False)
+            if a and HALF not in pb:
+                pb[0] = HALF
+            pos.append(pb)
+        if pos:
+            q = t * TILE + np.concatenate(pos)
+            off = rng.integers(1, 1 << 16, size=q.size, dtype=np.uint32).astype(np.uint16)
+            new[q] = (old[q].astype(np.uint32) + off).astype(np.uint16)
+    tail = np.arange(len(pairs) * TILE, n)
+    new[tail] = (old[tail].astype(np.uint32) + 1).astype(np.uint16)
+    return old, new
+
+
+@pytest.mark.parametrize("pad", [0, 3])
+def test_diff_tile_halves(sbd, oracle_mod, pad):
+    """Tiles whose changes sit in one half only, fill or overflow the stage
+    from one half, or meet at the seam between the halves, aligned and
+    unaligned, as one tensor and as a parameter list."""
+    old, new = halves_case(17 + pad)
+    ri, rv = oracle_mod.diff(old, new)
+    ntiles = len(HALF_COUNTS)
+    first = np.bincount(ri[ri < ntiles * TILE] // HALF, minlength=2 * ntiles)
+    assert first.tolist() == [c for ab in HALF_COUNTS for c in ab]  # the fixture is what it claims
+    gi, gv = sbd.diff(gpu_bits(old, pad), gpu_bits(new, pad))
+    assert np.array_equal(gi.cpu().numpy(), ri)
+    assert np.array_equal(np_bits(gv), rv)
+    olds = [old[t * TILE:(t + 1) * TILE] for t in range(ntiles + 1)] + [old]
+    news = [new[t * TILE:(t + 1) * TILE] for t in range(ntiles + 1)] + [new]
+    ri2, rv2, rn2, ro2 = oracle_mod.diff_many(olds, news)
+    gi2, gv2, gn2, go2 = sbd.diff_many([gpu_bits(o, pad) for o in olds],
+                                       [gpu_bits(x, pad) for x in news])
+    assert np.array_equal(gn2.cpu().numpy(), rn2)
+    assert np.array_equal(go2.cpu().numpy(), ro2)
+    assert np.array_equal(gi2.cpu().numpy(), ri2)
+    assert np.array_equal(np_bits(gv2), rv2)
+
+
 @pytest.mark.parametrize("seed", [41, 42])
 def test_diff_arena_mixed_tiles_repeated(sbd, oracle_mod, seed):
     """Hundreds of tiles whose counts fall on both sides of every staging
