@@ -254,7 +254,11 @@ delta_status delta_apply_checked(uint16_t *snapshot, int64_t n, const int32_t *i
  * The snapshot table is copied host-to-device as in delta_diff_many.  The
  * launch is bounded by the workgroups the GPU holds at once, and each stops
  * at the true total, so a max_nnz far above it (a buffer's capacity) costs
- * no idle work.
+ * no idle work.  The kernel, though, is chosen on the host from max_nnz and
+ * the snapshots' total size: pass the delta's true count when the caller has
+ * it (a receiver has it from the flush it received).  With a capacity far
+ * above a sparse delta's count the general kernel runs instead of the
+ * large-delta one: 2.89 against 2.53 ms on a 7B-shaped delta at 1.2 %.
  * Errors: DELTA_E_INVALID (nparams < 0, max_nnz < 0, a null array or pointer
  * when there are entries to apply, a negative numel, a null snapshot with
  * numel > 0), DELTA_E_RANGE (a numel above 2^31-1), DELTA_E_WORKSPACE (too

@@ -109,7 +109,10 @@ class ApplyPlan:
     def run(self, idx: torch.Tensor, val: torch.Tensor, offsets: torch.Tensor,
             max_nnz: int | None = None, violations: torch.Tensor | None = None):
         """Enqueue the scatter of a diff_many-layout delta; returns without syncing.
-        Entries j < min(offsets[nparams], max_nnz) are applied."""
+        Entries j < min(offsets[nparams], max_nnz) are applied.  Pass the true
+        count as max_nnz when it is known: the kernel is chosen from it, and a
+        sparse delta applied with only the buffer's capacity runs the general
+        kernel (about 14 % slower on a 7B-shaped delta at 1.2 %)."""
         dev = self.device
         _bits(val, "val")
         if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.device != dev:
