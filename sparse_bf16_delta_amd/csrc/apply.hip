@@ -35,13 +35,16 @@
 //     already merge into full lines in L2 without reading the snapshot.
 //
 // Two kernels share these rules:
-//  * apply_kernel (deltas below kSegMinTotal entries): 256-lane workgroups,
-//    chunks of 2048 entries (8 per lane, two 16-byte idx loads and one
-//    16-byte val load), a grid bounded at kApplyGridFactor times the
-//    workgroups the GPU holds at once, striding over the chunks; scatter and
-//    windows only.
-//  * apply_big_kernel (larger deltas): 1024-lane workgroups, chunks of 1024
-//    entries (one per lane), one chunk per workgroup in dispatch order.  The
+//  * apply_kernel (deltas below kSegMinTotal entries, and larger ones above
+//    about 2.8 % density): 256-lane workgroups, chunks of 2048 entries (8 per
+//    lane, two 16-byte idx loads and one 16-byte val load), a grid bounded at
+//    kApplyGridFactor times the workgroups the GPU holds at once, striding
+//    over the chunks; scatter, windows, and for deltas of kSegMinTotal
+//    entries or more the segment rewrite in passes of 64 segments, four in
+//    flight per lane.
+//  * apply_big_kernel (deltas of kSegMinTotal entries or more at about 2.8 %
+//    density or less): 1024-lane workgroups, chunks of 1024 entries (one per
+//    lane), one chunk per workgroup in dispatch order.  The
 //    segment rewrite's cost is set by how HBM sees the reads and writes, and
 //    it is lowest when the workgroups in flight cover one narrow, advancing
 //    band of the snapshot -- which the hardware dispatcher gives for free
@@ -87,6 +90,9 @@ constexpr int kSegGroups = kApplyBlock / kSegLanes;  // segments per apply_kerne
 constexpr int kSegUnroll = 4;                        // segments in flight per lane
 // Fewest delta entries for which sparse chunks rewrite whole segments.
 constexpr int64_t kSegMinTotal = int64_t(1) << 25;
+// Fewest elements per delta entry for the large-delta kernel (about 2.8 %
+// density or less; see launch_apply_kernels).
+constexpr int64_t kBigSpread = 36;
 constexpr int kMergeWindow = 8192;  // snapshot elements patched in LDS at a time
 static_assert(kMergeWindow % kSegElems == 0, "windows hold whole segments");
 
@@ -847,11 +853,15 @@ void launch_apply_kernel(const SnapParam* d_table, const SnapParam& single, int3
 }
 
 // Which kernel: apply_big_kernel when the delta is large enough for the
-// segment rewrite and sparse enough that its chunks take it (max_nnz entries
-// over total_elems elements leave more than kMergeSpread elements per entry);
-// else apply_kernel, which also rewrites the segments of sparse chunks when
-// max_nnz allows kSegMinTotal entries (a capacity far above the true count,
-// or a dense delta).  The windows of mid-density chunks run better in 256-lane
+// segment rewrite and sparse enough (max_nnz entries over total_elems
+// elements leave at least kBigSpread elements per entry); else apply_kernel,
+// which also rewrites the segments of sparse chunks when max_nnz allows
+// kSegMinTotal entries (a capacity far above the true count, or a denser
+// delta).  Where both rewrite segments, one chunk per 1024-lane workgroup
+// wins while the touched segments are few and far apart, and apply_kernel's
+// 256-lane passes win once most segments are touched; on the 7B-shaped list
+// (ms, large-delta / general): 1.2 % 2.53 / 2.89, 1.8 % 3.26 / 3.72, 2.4 %
+// 3.60 / 3.78, 2.9 % 4.22 / 4.16, 3.5 % 4.86 / 4.44.  The windows of mid-density chunks run better in 256-lane
 // workgroups issuing several loads per lane: a dense in-place read and
 // rewrite measured 6.1 TB/s in that shape against 4.0 TB/s in 1024-lane
 // workgroups with one load per lane (the Qwen3-0.6B-shaped list at 8 %:
@@ -861,7 +871,7 @@ void launch_apply_kernels(const SnapParam* d_table, const SnapParam& single, int
                           const int64_t* offsets, const int32_t* idx, const uint16_t* val,
                           int64_t max_nnz, int64_t total_elems, int64_t* violations,
                           hipStream_t stream) {
-  if (max_nnz >= kSegMinTotal && max_nnz <= total_elems / kMergeSpread) {
+  if (max_nnz >= kSegMinTotal && max_nnz <= total_elems / kBigSpread) {
     int64_t blocks = (max_nnz + kBigChunk - 1) / kBigChunk;
     if (blocks > kBigGridCap) blocks = kBigGridCap;
     apply_big_kernel<kMany><<<dim3(unsigned(blocks)), dim3(kBigBlock), 0, stream>>>(
