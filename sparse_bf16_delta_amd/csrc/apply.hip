@@ -17,13 +17,13 @@
 // with 2-byte stores, as is every entry of a chunk that breaks the
 // precondition or spans parameters.  How the interior is written depends on
 // the elements of span per entry:
-//   - sparse (more than kMergeSpread elements per entry, about 4 % density or
+//   - sparse (more than kMergeSpread elements per entry, about 5 % density or
 //     less): read, patch and write back each touched segment (the segment
 //     rewrite), but only for deltas of at least kSegMinTotal entries.  A
 //     smaller delta's touched segments fit in or near the 256 MB memory-side
 //     cache, which absorbs masked stores (measured at 2^28-2^30 elements and
 //     0.3-1 % density: 2-byte stores 1-3x faster than the rewrite);
-//   - dense (kMergeMinSpread to kMergeSpread elements per entry, about 4 % to
+//   - dense (kMergeMinSpread to kMergeSpread elements per entry, about 5 % to
 //     33 %): nearly every segment is touched, so the workgroup reads its
 //     whole span into LDS in 8192-element windows, patches it from its
 //     entries (held in registers) and writes it back, with nontemporal
@@ -81,8 +81,11 @@ constexpr int kApplyWaves = kApplyBlock / 64;
 constexpr int kApplyPer = 8;
 constexpr int kApplyChunk = kApplyBlock * kApplyPer;  // 2048 entries per chunk
 // Elements of span per entry that choose between the ways of writing a
-// well-formed chunk's interior segments (see above).
-constexpr int64_t kMergeSpread = 24;
+// well-formed chunk's interior segments (see above).  Segments against
+// windows on the 7B-shaped list, ms: at 4.7 % density 5.42 / 5.80, at 5.9 %
+// 5.85 / 5.85, at 3.5 % 4.44 / 4.71, on the Qwen3-0.6B list at 8 % windows
+// either way.
+constexpr int64_t kMergeSpread = 20;
 constexpr int64_t kMergeMinSpread = 3;
 constexpr int kSegElems = 32;                // bf16 per 64-byte segment
 constexpr int kSegLanes = kSegElems / kVec;  // 4 lanes x 16 bytes per segment
