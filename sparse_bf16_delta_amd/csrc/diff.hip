@@ -569,9 +569,11 @@ __global__ __launch_bounds__(kDiffBlock) void diff_place_kernel(
 // changed 16-byte chunks of `new` -- or, for a tile that found no room in the
 // arena, from a second read of both inputs.  Each of the tile's kDiffIters
 // iterations (at most kDiffBlock * kVec entries) is staged in LDS and copied
-// out with coalesced stores.
+// out with coalesced stores; the values are read a half tile at a time.
+// (six waves per SIMD asked of the compiler: 80 registers, three workgroups
+// per CU, without spilling to scratch; eight would spill)
 template <bool kMany, typename IdxT>
-__global__ __launch_bounds__(kDiffBlock) void diff_dense_kernel(
+__global__ __launch_bounds__(kDiffBlock) __attribute__((amdgpu_waves_per_eu(6))) void diff_dense_kernel(
     const TileDesc* __restrict__ tdesc, DiffParam single, const int32_t* __restrict__ dense_list,
     const uint32_t* __restrict__ ndense, const uint32_t* __restrict__ inpfx,
     const uint64_t* __restrict__ chunk_base, const uint32_t* __restrict__ wide,
@@ -598,22 +600,21 @@ __global__ __launch_bounds__(kDiffBlock) void diff_dense_kernel(
                       15u) == 0;
     const uint64_t at = tile_pos[t];
     uint32_t m[kDiffIters];
-    uint4 x[kDiffIters];
     if (at != kNoArena) {  // the mask the count kernel stored
       const u32x2 mw = *global_ptr(reinterpret_cast<const u32x2*>(wide + at * 4u) + ltid);
 #pragma unroll
-      for (int j = 0; j < kDiffIters; ++j) {
-        m[j] = ((j < 4 ? mw.x : mw.y) >> (8 * (j & 3))) & 0xFFu;
-        x[j] = m[j] != 0u ? load_chunk(tv.nb, j * kDiffBlock * kVec + ltid * kVec, tv.valid, vec)
-                          : make_uint4(0u, 0u, 0u, 0u);
-      }
-    } else {  // no room was left in the arena: compare the tile again
+      for (int j = 0; j < kDiffIters; ++j) m[j] = ((j < 4 ? mw.x : mw.y) >> (8 * (j & 3))) & 0xFFu;
+    } else {
+      // no room was left in the arena: compare the tile again, one chunk of
+      // each input in flight at a time (a rare path; it must not raise the
+      // kernel's register count), and read the changed values again below
 #pragma unroll
       for (int j = 0; j < kDiffIters; ++j) {
         const int local = j * kDiffBlock * kVec + ltid * kVec;
         const uint4 o = load_chunk(tv.ob, local, tv.valid, vec);
-        x[j] = load_chunk(tv.nb, local, tv.valid, vec);
-        m[j] = change_mask8(o, x[j]);
+        const uint4 n = load_chunk(tv.nb, local, tv.valid, vec);
+        m[j] = change_mask8(o, n);
+        asm volatile("" ::: "memory");  // keeps the next chunk's loads below this one
       }
     }
     uint32_t lp[kDiffIters], goff[kDiffIters], agg, gexcl;
@@ -621,37 +622,51 @@ __global__ __launch_bounds__(kDiffBlock) void diff_dense_kernel(
     const uint64_t tbase = chunk_base[t / kScanChunk] + inpfx[t];
     const IdxT first = sizeof(IdxT) == 8 ? static_cast<IdxT>(tv.flat_offset + tv.e0)
                                          : static_cast<IdxT>(tv.e0);
+    // the changed chunks of `new`, a half of the tile at a time: with half
+    // the values in registers, twice as many workgroups share a CU
 #pragma unroll
-    for (int j = 0; j < kDiffIters; ++j) {
-      // entries of iteration j occupy [jb, je) of the tile's output
-      const uint32_t jb = static_cast<uint32_t>(__shfl(static_cast<int>(gexcl), j * kDiffWaves, 64));
-      const uint32_t je =
-          j + 1 < kDiffIters
-              ? static_cast<uint32_t>(__shfl(static_cast<int>(gexcl), (j + 1) * kDiffWaves, 64))
-              : agg;
-      const uint32_t mm = m[j];
-      if (mm != 0u) {
-        uint32_t pos = goff[j] + lp[j] - jb;
-        const uint32_t local = static_cast<uint32_t>(j * kDiffBlock * kVec + ltid * kVec);
-        stage_slot<0>(mm, pos, local, x[j], s_stage);
-        stage_slot<1>(mm, pos, local, x[j], s_stage);
-        stage_slot<2>(mm, pos, local, x[j], s_stage);
-        stage_slot<3>(mm, pos, local, x[j], s_stage);
-        stage_slot<4>(mm, pos, local, x[j], s_stage);
-        stage_slot<5>(mm, pos, local, x[j], s_stage);
-        stage_slot<6>(mm, pos, local, x[j], s_stage);
-        stage_slot<7>(mm, pos, local, x[j], s_stage);
+    for (int h = 0; h < 2; ++h) {
+      uint4 x[kHalfIters];
+#pragma unroll
+      for (int k = 0; k < kHalfIters; ++k) {
+        const int j = h * kHalfIters + k;
+        x[k] = m[j] != 0u ? load_chunk(tv.nb, j * kDiffBlock * kVec + ltid * kVec, tv.valid, vec)
+                          : make_uint4(0u, 0u, 0u, 0u);
       }
-      __syncthreads();
-      for (uint32_t p = static_cast<uint32_t>(tid); p < je - jb; p += kDiffBlock) {
-        const uint64_t o = tbase + jb + p;
-        if (o < cap) {
-          const uint32_t w = s_stage[p];
-          idx[o] = first + static_cast<IdxT>(w >> 16);
-          val[o] = static_cast<uint16_t>(w & 0xFFFFu);
+#pragma unroll
+      for (int k = 0; k < kHalfIters; ++k) {
+        const int j = h * kHalfIters + k;
+        // entries of iteration j occupy [jb, je) of the tile's output
+        const uint32_t jb =
+            static_cast<uint32_t>(__shfl(static_cast<int>(gexcl), j * kDiffWaves, 64));
+        const uint32_t je =
+            j + 1 < kDiffIters
+                ? static_cast<uint32_t>(__shfl(static_cast<int>(gexcl), (j + 1) * kDiffWaves, 64))
+                : agg;
+        const uint32_t mm = m[j];
+        if (mm != 0u) {
+          uint32_t pos = goff[j] + lp[j] - jb;
+          const uint32_t local = static_cast<uint32_t>(j * kDiffBlock * kVec + ltid * kVec);
+          stage_slot<0>(mm, pos, local, x[k], s_stage);
+          stage_slot<1>(mm, pos, local, x[k], s_stage);
+          stage_slot<2>(mm, pos, local, x[k], s_stage);
+          stage_slot<3>(mm, pos, local, x[k], s_stage);
+          stage_slot<4>(mm, pos, local, x[k], s_stage);
+          stage_slot<5>(mm, pos, local, x[k], s_stage);
+          stage_slot<6>(mm, pos, local, x[k], s_stage);
+          stage_slot<7>(mm, pos, local, x[k], s_stage);
         }
+        __syncthreads();
+        for (uint32_t p = static_cast<uint32_t>(tid); p < je - jb; p += kDiffBlock) {
+          const uint64_t o = tbase + jb + p;
+          if (o < cap) {
+            const uint32_t w = s_stage[p];
+            idx[o] = first + static_cast<IdxT>(w >> 16);
+            val[o] = static_cast<uint16_t>(w & 0xFFFFu);
+          }
+        }
+        __syncthreads();  // the stage is refilled by the next iteration
       }
-      __syncthreads();  // the stage is refilled by the next iteration
     }
   }
 }
