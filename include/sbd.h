@@ -427,10 +427,11 @@ int64_t delta_wire_positions_size(int32_t nparams, const int64_t *numels,
  *  numels              (host) the parameters' sizes (they fix the widths).
  *  idx, offsets        device, as delta_diff_many wrote them; entries
  *                      j < min(offsets[nparams], max_entries) are encoded.
- *  positions           device bytes, room for `positions_capacity`: a
- *                      position is written only if all its bytes fit, so
- *                      nothing past the capacity is touched and the block
- *                      is exact up to the last whole position.
+ *  positions           device bytes, 2-byte aligned, room for
+ *                      `positions_capacity`: a position is written only if
+ *                      all its bytes fit, so nothing past the capacity is
+ *                      touched and the block is exact up to the last whole
+ *                      position.
  *  pos_offsets         device int64[nparams+1]: each parameter's start in the
  *                      block; pos_offsets[nparams] is the block's full size.
  *  ws, ws_bytes        at least delta_workspace_size(0, nparams).
@@ -447,6 +448,8 @@ delta_status delta_wire_encode(int32_t nparams, const int64_t *numels, const int
  * indices (the delta_diff_many layout) for entries j < min(offsets[nparams],
  * max_entries), from the byte block and the device pos_offsets and offsets,
  * which may come from a remote sender and are not trusted:
+ *  positions           device bytes, 2-byte aligned (a received block may
+ *                      have to be copied to such an address first).
  *  positions_bytes     size of the received block; no byte outside
  *                      [0, positions_bytes) is read.
  *  violations          optional device int64[1] (NULL to skip): receives the

@@ -418,6 +418,8 @@ delta_status delta_wire_encode(int32_t nparams, const int64_t* numels, const int
     return fail(DELTA_E_INVALID, "delta_wire_encode: null idx");
   if (positions_capacity > 0 && positions == nullptr)
     return fail(DELTA_E_INVALID, "delta_wire_encode: null positions");
+  if ((reinterpret_cast<uintptr_t>(positions) & 1u) != 0)
+    return fail(DELTA_E_INVALID, "delta_wire_encode: positions not 2-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* d_widths = nullptr;
   const delta_status st =
@@ -440,6 +442,8 @@ delta_status delta_wire_decode(int32_t nparams, const int64_t* numels, const uin
   if (max_entries > 0 && idx == nullptr) return fail(DELTA_E_INVALID, "delta_wire_decode: null idx");
   if (positions_bytes > 0 && positions == nullptr)
     return fail(DELTA_E_INVALID, "delta_wire_decode: null positions");
+  if ((reinterpret_cast<uintptr_t>(positions) & 1u) != 0)
+    return fail(DELTA_E_INVALID, "delta_wire_decode: positions not 2-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* d_widths = nullptr;
   const delta_status st =

@@ -313,16 +313,41 @@ __global__ __launch_bounds__(256) void wire_blocked_table_kernel(
   }
 }
 
-// Every entry's offset inside its block, 2 bytes at out[lows + 2j].
+// Every entry's offset inside its block, 2 bytes at out[lows + 2j]: the low
+// 16 bits of its parameter-local index, since blocks start at multiples of
+// 65536.  Four entries per lane: one 16-byte load of their indices and one
+// 8-byte store (two 4-byte ones where the offsets start only 4-byte aligned;
+// `out` is 4-byte aligned and `lows` a multiple of 4), entry by entry at the
+// capacity's edge or for an unaligned idx.
 __global__ __launch_bounds__(256) void wire_blocked_lows_kernel(
     int32_t nparams, const int32_t* __restrict__ idx, const int64_t* __restrict__ offsets,
     int64_t max_entries, uint8_t* __restrict__ out, int64_t lows, int64_t out_capacity) {
   const int64_t tot = offsets[nparams] < max_entries ? offsets[nparams] : max_entries;
-  const int64_t stride = int64_t(gridDim.x) * 256;
-  for (int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x; j < tot; j += stride) {
-    if (lows + 2 * j + 2 <= out_capacity)
-      *global_ptr(reinterpret_cast<uint16_t*>(out + lows + 2 * j)) =
-          static_cast<uint16_t>(static_cast<uint32_t>(idx[j]) & 0xFFFFu);
+  const bool in16 = (reinterpret_cast<uintptr_t>(idx) & 15u) == 0;
+  const bool out8 = ((reinterpret_cast<uintptr_t>(out) + uintptr_t(lows)) & 7u) == 0;
+  const int64_t stride = int64_t(gridDim.x) * 256 * 4;
+  for (int64_t j = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4; j < tot; j += stride) {
+    uint8_t* dst = out + lows + 2 * j;
+    if (in16 && j + 4 <= tot && lows + 2 * j + 8 <= out_capacity) {
+      const u32x4 v = *global_ptr(reinterpret_cast<const u32x4*>(idx + j));
+      const uint32_t w0 = (v.x & 0xFFFFu) | (v.y << 16);
+      const uint32_t w1 = (v.z & 0xFFFFu) | (v.w << 16);
+      if (out8) {
+        u32x2 w;
+        w.x = w0;
+        w.y = w1;
+        *global_ptr(reinterpret_cast<u32x2*>(dst)) = w;
+      } else {
+        *global_ptr(reinterpret_cast<uint32_t*>(dst)) = w0;
+        *global_ptr(reinterpret_cast<uint32_t*>(dst + 4)) = w1;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (j + k < tot && lows + 2 * (j + k) + 2 <= out_capacity)
+          *global_ptr(reinterpret_cast<uint16_t*>(dst + 2 * k)) =
+              static_cast<uint16_t>(static_cast<uint32_t>(idx[j + k]) & 0xFFFFu);
+    }
   }
 }
 
@@ -583,7 +608,7 @@ hipError_t launch_wire_encode_blocked(int32_t nparams, const BlockedParam* bp, i
         nparams, bp, nblocks, idx, offsets, max_entries, out, out_capacity);
   }
   if (max_entries > 0) {
-    int64_t g = (max_entries + 255) / 256;
+    int64_t g = (max_entries + 1023) / 1024;
     if (g > 65536) g = 65536;
     wire_blocked_lows_kernel<<<dim3(unsigned(g)), dim3(256), 0, stream>>>(
         nparams, idx, offsets, max_entries, out, 4 * nblocks, out_capacity);

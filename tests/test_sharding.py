@@ -153,6 +153,14 @@ def test_wire_abi_rejects_bad_arguments():
         _abi.DELTA_E_WORKSPACE
     assert lib.delta_wire_hash(None, 4, None, 0, one, None) == _abi.DELTA_E_INVALID
     assert lib.delta_wire_hash(one, -1, one, 0, one, None) == _abi.DELTA_E_INVALID
+    # positions move as 2-byte halves: an odd address is rejected before any launch
+    odd = ctypes.c_void_p(17)
+    assert lib.delta_wire_encode(1, ok, one, one, 5, odd, 10, one, one, 1 << 30, None) == \
+        _abi.DELTA_E_INVALID
+    assert "2-byte aligned" in lib.delta_last_error().decode()
+    assert lib.delta_wire_decode(1, ok, odd, 8, one, one, 5, one, None, one, 1 << 30,
+                                 None) == _abi.DELTA_E_INVALID
+    assert "2-byte aligned" in lib.delta_last_error().decode()
 
 
 def test_wire_sizes_are_the_library_rule():

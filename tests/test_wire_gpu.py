@@ -263,3 +263,73 @@ def test_wire_blocked_decode_alignments(sbd, oracle_mod, in_shift, out_shift):
     assert int(v.item()) == 0
     assert np.array_equal(got[out_shift:out_shift + ri.size], ri)
     assert np.all(got[:out_shift] == 77) and np.all(got[out_shift + ri.size:] == 77)
+
+
+@pytest.mark.parametrize("out_shift", [0, 4, 8, 12])
+@pytest.mark.parametrize("idx_shift", [0, 1, 3])
+def test_wire_blocked_encode_alignments(sbd, oracle_mod, out_shift, idx_shift):
+    """Encode reads indices and writes bytes at any alignment the contract
+    allows: indices from 0, 1 or 3 elements past a 16-byte aligned address,
+    the block 0, 4, 8 or 12 bytes past one (the offsets after the tables
+    then start 8- or only 4-byte aligned); its bytes equal the oracle's and
+    the bytes around them are untouched."""
+    import ctypes
+    from sparse_bf16_delta_amd import _abi
+    from sparse_bf16_delta_amd.ops import _ptr, _stream
+
+    numels = [70_000, 3, 65536, 131_073, 9] + ([100] if idx_shift == 1 else [])
+    olds, news = delta_case(51 + out_shift + 7 * idx_shift, numels, 0.05)
+    ri, rv, rn, ro = oracle_mod.diff_many(olds, news)
+    want = oracle_mod.wire_encode_blocked(ri, ro, numels)
+    lib = _abi.load()
+    k = len(numels)
+    nums = (ctypes.c_int64 * k)(*numels)
+    ws = torch.empty(lib.delta_workspace_size(0, k), dtype=torch.uint8, device="cuda")
+    ibuf = torch.zeros(ri.size + 8, dtype=torch.int32, device="cuda")
+    ibuf[idx_shift:idx_shift + ri.size] = torch.from_numpy(ri).cuda()
+    idx = ibuf[idx_shift:idx_shift + ri.size]
+    off = torch.from_numpy(ro).cuda()
+    buf = torch.full((want.size + 32,), 0xAB, dtype=torch.uint8, device="cuda")
+    out = buf[out_shift:out_shift + want.size]
+    _abi.check(lib.delta_wire_encode_blocked(k, nums, _ptr(idx), _ptr(off), ri.size, _ptr(out),
+                                             want.size, _ptr(ws), ws.numel(), _stream(off.device)))
+    got = buf.cpu().numpy()
+    assert np.array_equal(got[out_shift:out_shift + want.size], want)
+    assert np.all(got[:out_shift] == 0xAB) and np.all(got[out_shift + want.size:] == 0xAB)
+
+
+@pytest.mark.parametrize("shift", [2, 4, 6])
+def test_wire_positions_at_shifted_addresses(sbd, oracle_mod, shift):
+    """The per-parameter block encoded to, and decoded from, an address 2, 4
+    or 6 bytes past a 16-byte aligned one (4-byte positions then move as
+    words or as halves): the bytes and the indices equal the oracle's."""
+    import ctypes
+    from sparse_bf16_delta_amd import _abi
+    from sparse_bf16_delta_amd.ops import _ptr, _stream
+
+    olds, news = delta_case(61 + shift, NUMELS, 0.05)
+    ri, rv, rn, ro = oracle_mod.diff_many(olds, news)
+    want_pos, want_po = oracle_mod.wire_encode(ri, ro, NUMELS)
+    lib = _abi.load()
+    k = len(NUMELS)
+    nums = (ctypes.c_int64 * k)(*NUMELS)
+    ws = torch.empty(lib.delta_workspace_size(0, k), dtype=torch.uint8, device="cuda")
+    idx = torch.from_numpy(ri).cuda()
+    off = torch.from_numpy(ro).cuda()
+    po = torch.empty(k + 1, dtype=torch.int64, device="cuda")
+    buf = torch.full((want_pos.size + 32,), 0xAB, dtype=torch.uint8, device="cuda")
+    pos = buf[shift:shift + want_pos.size]
+    _abi.check(lib.delta_wire_encode(k, nums, _ptr(idx), _ptr(off), ri.size, _ptr(pos),
+                                     want_pos.size, _ptr(po), _ptr(ws), ws.numel(),
+                                     _stream(off.device)))
+    got = buf.cpu().numpy()
+    assert np.array_equal(po.cpu().numpy(), want_po)
+    assert np.array_equal(got[shift:shift + want_pos.size], want_pos)
+    assert np.all(got[:shift] == 0xAB) and np.all(got[shift + want_pos.size:] == 0xAB)
+    back = torch.full((ri.size,), 77, dtype=torch.int32, device="cuda")
+    v = torch.full((1,), -1, dtype=torch.int64, device="cuda")
+    _abi.check(lib.delta_wire_decode(k, nums, _ptr(pos), want_pos.size, _ptr(po), _ptr(off),
+                                     ri.size, _ptr(back), _ptr(v), _ptr(ws), ws.numel(),
+                                     _stream(off.device)))
+    assert int(v.item()) == 0
+    assert np.array_equal(back.cpu().numpy(), ri)
