@@ -373,20 +373,23 @@ __global__ __launch_bounds__(kWireBlock) void wire_blocked_decode_kernel(
       const int64_t total = t < max_entries ? t : max_entries;
       if (j0 < total) {
         const int32_t p0 = find_param_wave0(offsets, nparams, j0);
+        // the last block whose base is <= the first entry's place in its
+        // parameter, by a 64-way search over the parameter's bases (each step
+        // probes 64 evenly spaced bases at once; three steps for 2^18 blocks)
+        const int64_t local = j0 - offsets[p0];
+        const int64_t tb = bp[p0].tbase;
+        int64_t lo = 0, hi = (bp[p0].numel + kPosBlockElems - 1) / kPosBlockElems;
+        while (hi - lo > 1) {
+          const int64_t step = (hi - lo + 63) / 64;
+          const int64_t probe = lo + int64_t(threadIdx.x) * step;
+          const uint64_t ok = __ballot(probe < hi && int64_t(words[tb + probe]) <= local);
+          if (ok == 0u) break;  // a malformed table (its first base above the entry); checked apart
+          lo += int64_t(63 - __builtin_clzll(ok)) * step;
+          hi = lo + step < hi ? lo + step : hi;
+        }
         if (threadIdx.x == 0) {
           s_p0 = p0;
-          // last block whose base is <= the first entry's place in its parameter
-          const int64_t local = j0 - offsets[p0];
-          const int64_t tb = bp[p0].tbase;
-          int64_t lo = 0, hi = (bp[p0].numel + kPosBlockElems - 1) / kPosBlockElems - 1;
-          while (lo < hi) {
-            const int64_t mid = (lo + hi + 1) >> 1;
-            if (int64_t(words[tb + mid]) <= local)
-              lo = mid;
-            else
-              hi = mid - 1;
-          }
-          s_b0 = lo < 0 ? 0 : lo;
+          s_b0 = lo;
         }
       }
       if (threadIdx.x == 0) s_total = total;
