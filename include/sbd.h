@@ -59,8 +59,8 @@ typedef enum {
  * device copy of the parameter table (these are the minimum,
  * delta_workspace_size_for(total_elems, nparams, 0): about 0.06 bytes per
  * element), and then a staging arena for the compacted entries of tiles with
- * more than 512 changes and the change masks of tiles with more than 4096:
- * here its worst case, 16 KB per tile (about 0.5 bytes per element).  Every
+ * more than 512 changes and the change masks of tiles with more than 8192:
+ * here its worst case, 32 KB per tile (about 1 byte per element).  Every
  * function taking a workspace requires it to start on a 256-byte boundary
  * (device allocations do) and fails with DELTA_E_WORKSPACE otherwise.  Its
  * contents on entry do not matter and are clobbered.  Returns 0 for negative

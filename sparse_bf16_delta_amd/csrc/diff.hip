@@ -19,9 +19,10 @@
 //     lane forms an 8-bit change mask; its popcount is prefix-summed across
 //     the wave with four ballots over its bits plus mbcnt, and each half's 32
 //     (iteration, wave) group totals are scanned in LDS, giving every change
-//     its slot inside the tile in ascending element order.  A tile with at most 4096 changes
-//     is compacted in LDS as (tile-local index << 16 | new bits) and copied
-//     with 16-byte nontemporal stores: a tile with up to 512 changes into a
+//     its slot inside the tile in ascending element order.  A tile with at
+//     most 8192 changes (25 %) is compacted in LDS as (tile-local index << 16
+//     | new bits) and copied with 16-byte nontemporal stores: a tile with up
+//     to 512 changes into a
 //     2 KB workspace slot of its own, a tile with more into a staging arena
 //     shared by all tiles, at a position it takes with one atomic add on a
 //     workspace counter (so the arena fills as one dense, ascending write

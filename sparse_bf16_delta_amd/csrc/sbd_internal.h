@@ -84,7 +84,7 @@ struct TileDesc {
 // kWideWords words per tile).  A denser tile stores its change mask (one byte
 // per 16-byte chunk, 4 KB) in the arena; a tile that finds the arena full
 // stores nothing and is recomputed from both inputs by the dense kernel.
-constexpr int kStageCap = 4096;
+constexpr int kStageCap = 8192;
 constexpr int kCompactCap = 512;
 constexpr int64_t kCompactWords = kCompactCap;  // uint32 per compact slot
 constexpr int64_t kWideWords = kStageCap;       // arena uint32 reserved per tile (worst case)

@@ -4,8 +4,8 @@ Tolerance is zero everywhere: the path is integer and bit work, so nnz, the
 order of the indices and the value bits must be identical.  Sizes span
 several 32768-element tiles, ragged tails, unaligned views, empty and
 all-changed inputs, signed zeros and NaN payloads, and tiles whose change
-counts sit on each side of the compaction's staging limits (1024 and 4096
-changes per tile).  No oracle input or expected value comes from the GPU
+counts sit on each side of the compaction's staging limits (512 and 8192
+changes per tile, and 1024 and 4096, the limits of earlier layouts).  No oracle input or expected value comes from the GPU
 path.
 """
 import numpy as np
@@ -81,11 +81,11 @@ def test_diff_unaligned_views(sbd, oracle_mod, pad_old, pad_new, n):
     assert np.array_equal(np_bits(gv), rv)
 
 
-# changes per tile, straddling the compact-slot (512), arena (4096) and dense
-# limits, plus 1023-1025 (the compact limit of an earlier layout); the last
+# changes per tile, straddling the compact-slot (512) and staging (8192)
+# limits, plus 1023-1025 and 4095-4097 (limits of earlier layouts); the last
 # tile is ragged (5000 of 32768 elements, all changed)
 TILE_COUNTS = [0, 1, 1023, 1024, 1025, 4095, 4096, 4097, TILE, 3, TILE // 2, 1027, 511, 512,
-               513, 5000]
+               513, 8191, 8192, 8193, 5000]
 
 
 def tile_kinds_case(seed, counts=TILE_COUNTS, last_valid=5000):
@@ -127,11 +127,12 @@ def test_diff_tile_kinds(sbd, oracle_mod, pad):
 # (changes in the first half, changes in the second half) of each tile: the
 # count kernel loads and stages a tile as two halves of 16384 elements, so a
 # tile's entries may all sit in one half, or the first half may fill or
-# overflow the 4096-entry stage alone
+# overflow the 8192-entry stage alone
 HALF = TILE // 2
 HALF_COUNTS = [(0, 1), (1, 0), (4096, 0), (0, 4096), (4097, 0), (0, 4097), (4095, 1),
                (1, 4095), (2048, 2049), (2048, 2048), (512, 0), (0, 513), (HALF, 0), (0, HALF),
-               (600, 600), (0, 0)]
+               (600, 600), (8192, 0), (8193, 0), (0, 8193), (8191, 1), (4096, 4097),
+               (4096, 4096), (0, 0)]
 
 
 def halves_case(seed, pairs=HALF_COUNTS, last_valid=20000):
@@ -197,7 +198,8 @@ def test_diff_arena_mixed_tiles_repeated(sbd, oracle_mod, seed):
 
     rng = np.random.default_rng(seed)
     ntiles = 300
-    counts = rng.choice([0, 5, 600, 1024, 1025, 2000, 3500, 4096, 4097, 9000], size=ntiles)
+    counts = rng.choice([0, 5, 600, 1024, 1025, 2000, 3500, 4096, 4097, 8192, 8193, 9000],
+                        size=ntiles)
     cases = [tile_kinds_case(seed, counts=list(counts), last_valid=TILE),
              tile_kinds_case(seed + 100, counts=list(rng.permutation(counts)), last_valid=TILE)]
     n = ntiles * TILE
@@ -235,7 +237,8 @@ def test_diff_arena_size_does_not_change_the_delta(sbd, oracle_mod, arena, seed)
 
     rng = np.random.default_rng(seed)
     ntiles = 120
-    counts = rng.choice([0, 5, 511, 512, 513, 800, 2000, 4096, 4097, 9000, TILE], size=ntiles)
+    counts = rng.choice([0, 5, 511, 512, 513, 800, 2000, 4096, 4097, 8192, 8193, 9000, TILE],
+                        size=ntiles)
     old, new = tile_kinds_case(seed, counts=list(counts), last_valid=TILE)
     ri, rv = oracle_mod.diff(old, new)
     n = old.size
@@ -285,7 +288,8 @@ def test_diff_arena_size_does_not_change_the_delta(sbd, oracle_mod, arena, seed)
 
 
 @pytest.mark.parametrize("cut", [1024 + 1023 + 1, 1 + 1023 + 1024 + 1025 + 4095 + 7,
-                                 sum(TILE_COUNTS[:8]) + 100, sum(TILE_COUNTS) - 1])
+                                 sum(TILE_COUNTS[:8]) + 100, sum(TILE_COUNTS[:16]) + 4097,
+                                 sum(TILE_COUNTS) - 1])
 def test_diff_tile_kinds_capacity(sbd, oracle_mod, cut):
     """A capacity that ends inside a compact, a wide and a dense tile's run:
     the prefix is exact and nothing past the capacity is written."""
