@@ -20,8 +20,11 @@
  *    from host memory; HIP stages that copy before the call returns, without
  *    waiting for the stream.)
  *  - Ownership: the caller allocates and frees every buffer (outputs,
- *    counters, workspace).  The library allocates no device memory and keeps
- *    no state between calls except the calling thread's error message.
+ *    counters, workspace).  The library allocates no device memory at run
+ *    time (delta_diff_noalloc's static array is part of the loaded library)
+ *    and keeps no state between calls except the calling thread's error
+ *    message and per-device constants (occupancy limits, that array's
+ *    address).
  *  - Errors: a non-zero delta_status is returned before anything is
  *    enqueued when arguments are rejected; delta_last_error() describes it.
  *    DELTA_E_HIP reports a launch failure from the HIP runtime.
@@ -102,8 +105,8 @@ size_t delta_workspace_size_for(int64_t total_elems, int32_t nparams, int64_t ca
  *  ws, ws_bytes        workspace of at least delta_workspace_size_for(n, 1, 0)
  *                      bytes; delta_workspace_size_for(n, 1, capacity) keeps
  *                      every staged tile in the arena (see there).
- * The work is five kernel launches on `stream` (count and stage, two scans,
- * place, dense tiles); no workgroup waits for another.
+ * The work is six kernel launches on `stream` (a counter clear, count and
+ * stage, two scans, place, dense tiles); no workgroup waits for another.
  * Errors: DELTA_E_INVALID (null pointers, n < 0, capacity < 0),
  * DELTA_E_RANGE (n > 2^31-1), DELTA_E_WORKSPACE, DELTA_E_HIP.
  */
