@@ -19,6 +19,10 @@
  *    their last apply is done.  (The *_many calls copy their parameter table
  *    from host memory; HIP stages that copy before the call returns, without
  *    waiting for the stream.)
+ *  - Device: every call works on the calling thread's current device
+ *    (hipSetDevice): its buffers and `stream` must belong to that device,
+ *    and the per-device state below is that device's.  delta_diff_noalloc
+ *    rejects a stream of another device with DELTA_E_INVALID.
  *  - Ownership: the caller allocates and frees every buffer (outputs,
  *    counters, workspace).  The library allocates no device memory at run
  *    time (delta_diff_noalloc's static array is part of the loaded library)
@@ -124,8 +128,10 @@ delta_status delta_diff(const uint16_t *old_bits, const uint16_t *new_bits, int6
  * with DELTA_E_RANGE before anything is enqueued.  Arguments, outputs and the
  * capacity protocol as delta_diff.  Every call on one GPU shares that GPU's
  * array: calls that overlap on one GPU (two streams or two threads at once)
- * race and must be serialised by the caller.
- * Errors: DELTA_E_INVALID, DELTA_E_RANGE (n above the limit), DELTA_E_HIP.
+ * race and must be serialised by the caller.  The array used is the current
+ * device's, so `stream` must belong to the current device.
+ * Errors: DELTA_E_INVALID (also: a stream of another device), DELTA_E_RANGE
+ * (n above the limit), DELTA_E_HIP.
  */
 delta_status delta_diff_noalloc(const uint16_t *old_bits, const uint16_t *new_bits, int64_t n,
                                 int32_t *idx, uint16_t *val, int64_t capacity, int64_t *nnz,

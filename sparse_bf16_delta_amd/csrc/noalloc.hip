@@ -80,6 +80,23 @@ delta_status delta_diff_noalloc(const uint16_t* old_bits, const uint16_t* new_bi
   if (L.wide > sbd::kNoAllocScratchBytes)  // cannot happen for n within the limit
     return fail_with(DELTA_E_WORKSPACE, "delta_diff_noalloc: layout of %zu bytes exceeds the "
                      "static scratch", L.wide);
+  // the kernels run on the stream's device and take the current device's
+  // array, so the two must be the same device
+  if (stream != nullptr) {
+    int cur = 0;
+    hipDevice_t sdev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess) e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail_with(DELTA_E_HIP, "delta_diff_noalloc: stream device: %s", hipGetErrorString(e));
+    }
+    if (static_cast<int>(sdev) != cur)
+      return fail_with(DELTA_E_INVALID,
+                       "delta_diff_noalloc: the stream belongs to device %d, the current "
+                       "device is %d",
+                       static_cast<int>(sdev), cur);
+  }
   const char* why = nullptr;
   void* ws = sbd::scratch_address(why);
   if (ws == nullptr)

@@ -26,6 +26,7 @@ indices are int32, counts and offsets int64, all on the same device.
 from __future__ import annotations
 
 import ctypes
+import functools
 from typing import Sequence
 
 import torch
@@ -44,6 +45,30 @@ def _stream(device: torch.device) -> ctypes.c_void_p:
 
 def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _device_of(args):
+    """The device of the first GPU tensor among `args` (or in a list there)."""
+    for a in args:
+        if isinstance(a, (list, tuple)) and a:
+            a = a[0]
+        if isinstance(a, torch.Tensor) and a.device.type == "cuda":
+            return a.device
+    return None
+
+
+def _on_device(fn):
+    """Run `fn` with the device of its GPU tensors current: libsbd works on the
+    calling thread's current device (its streams, buffers and per-device
+    state), whichever device the caller has made current."""
+    @functools.wraps(fn)
+    def run(*args, **kwargs):
+        dev = _device_of(list(args) + list(kwargs.values()))
+        if dev is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.device(dev):
+            return fn(*args, **kwargs)
+    return run
 
 
 def _bits(t, what: str) -> torch.Tensor:
@@ -101,6 +126,7 @@ def default_capacity(n: int) -> int:
     return n // 8 + 65536
 
 
+@_on_device
 def diff(old: torch.Tensor, new: torch.Tensor, capacity: int | None = None):
     """(idx int32[k], val bfloat16[k]) of the positions whose bits differ."""
     _bits(old, "old")
@@ -125,6 +151,7 @@ def diff(old: torch.Tensor, new: torch.Tensor, capacity: int | None = None):
         cap = k
 
 
+@_on_device
 def diff_many(olds: Sequence[torch.Tensor], news: Sequence[torch.Tensor],
               capacity: int | None = None, flat_offsets: Sequence[int] | None = None):
     """Batched diff: (idx_cat, val_cat bf16, nnz int64[P], offsets int64[P+1]),
@@ -189,6 +216,7 @@ def _raise_on_violations(v):
             raise DeltaError(1, f"{bad} delta entries out of range or not strictly ascending")
 
 
+@_on_device
 def apply_(snap: torch.Tensor, idx: torch.Tensor, val: torch.Tensor, check_indices=False):
     """snap.view(-1)[idx] = val in place; returns snap."""
     _bits(snap, "snapshot")
@@ -211,6 +239,7 @@ def apply_(snap: torch.Tensor, idx: torch.Tensor, val: torch.Tensor, check_indic
     return snap
 
 
+@_on_device
 def apply_many_(snaps: Sequence[torch.Tensor], idx: torch.Tensor, val: torch.Tensor,
                 offsets: torch.Tensor, max_nnz: int | None = None, check_indices=False):
     """Batched in-place scatter of a diff_many result into `snaps`."""
@@ -263,6 +292,7 @@ def _host_bits(t, what: str) -> torch.Tensor:
     return t
 
 
+@_on_device
 def apply_many_host_(snaps: Sequence[torch.Tensor], idx: torch.Tensor, val: torch.Tensor,
                      offsets: torch.Tensor, max_nnz: int | None = None, check_indices=False,
                      wait=True):
@@ -308,6 +338,7 @@ def apply_many_host_(snaps: Sequence[torch.Tensor], idx: torch.Tensor, val: torc
     return snaps
 
 
+@_on_device
 def apply_streamed_(snaps: Sequence[torch.Tensor], idx: torch.Tensor, val: torch.Tensor,
                     offsets: torch.Tensor, bounds: Sequence[int]):
     """Apply a delta held in host memory -- idx int32, val bf16 bits, offsets
@@ -367,6 +398,7 @@ def apply_streamed_(snaps: Sequence[torch.Tensor], idx: torch.Tensor, val: torch
     return snaps
 
 
+@_on_device
 def xor_apply_streamed_(snap: torch.Tensor, mask: torch.Tensor, chunk_elems: int = 1 << 27):
     """snap ^= mask with `mask` in host memory (should be pinned), copied and
     applied chunk_elems elements at a time.  Returns after snap is updated."""
@@ -400,6 +432,7 @@ def _wire_args(idx, offsets, numels):
     return k, (ctypes.c_int64 * max(k, 1))(*[int(n) for n in numels])
 
 
+@_on_device
 def wire_encode(idx: torch.Tensor, offsets: torch.Tensor, numels: Sequence[int]):
     """Positions byte block of a diff_many result: (positions uint8, pos_offsets
     int64[P+1]) on the device; one device-to-host read of the offsets sizes it."""
@@ -425,6 +458,7 @@ def _raise_on_wire_violations(v):
         raise DeltaError(1, f"{bad} malformed entries or spans in the received positions")
 
 
+@_on_device
 def wire_decode(positions: torch.Tensor, pos_offsets: torch.Tensor, offsets: torch.Tensor,
                 numels: Sequence[int]) -> torch.Tensor:
     """int32 parameter-local indices back from a positions block (which may
@@ -453,6 +487,7 @@ def wire_decode(positions: torch.Tensor, pos_offsets: torch.Tensor, offsets: tor
     return idx[:total]
 
 
+@_on_device
 def wire_encode_blocked(idx: torch.Tensor, offsets: torch.Tensor, numels: Sequence[int]):
     """Blocked positions (2 bytes per position for any parameter size) of a
     diff_many result, as a uint8 device tensor; one device-to-host read of
@@ -471,6 +506,7 @@ def wire_encode_blocked(idx: torch.Tensor, offsets: torch.Tensor, numels: Sequen
     return out[:size]
 
 
+@_on_device
 def wire_decode_blocked(data: torch.Tensor, offsets: torch.Tensor,
                         numels: Sequence[int]) -> torch.Tensor:
     """int32 parameter-local indices back from blocked positions (untrusted
@@ -495,6 +531,7 @@ def wire_decode_blocked(data: torch.Tensor, offsets: torch.Tensor,
     return idx[:total]
 
 
+@_on_device
 def wire_hashes(positions: torch.Tensor, values: torch.Tensor) -> tuple[int, int]:
     """(hash of the position bytes, hash of the bf16 values) as unsigned ints."""
     _bits(values, "values")
@@ -507,6 +544,7 @@ def wire_hashes(positions: torch.Tensor, values: torch.Tensor) -> tuple[int, int
     return a & (2 ** 64 - 1), b & (2 ** 64 - 1)
 
 
+@_on_device
 def wire_checksum(positions: torch.Tensor, values: torch.Tensor) -> int:
     """The flush checksum hash(positions) ^ (hash(values) << 1), computed by
     the library as 65 bits in two words, returned as one Python int."""
@@ -520,6 +558,7 @@ def wire_checksum(positions: torch.Tensor, values: torch.Tensor) -> int:
     return lo | (hi << 64)
 
 
+@_on_device
 def xor_mask(old: torch.Tensor, new: torch.Tensor, out: torch.Tensor | None = None):
     """mask = old ^ new (bit patterns) as an int16 tensor shaped like old."""
     _bits(old, "old")
@@ -536,6 +575,7 @@ def xor_mask(old: torch.Tensor, new: torch.Tensor, out: torch.Tensor | None = No
     return out
 
 
+@_on_device
 def xor_apply_(snap: torch.Tensor, mask: torch.Tensor):
     """snap ^= mask in place; returns snap."""
     _bits(snap, "snapshot")

@@ -62,17 +62,18 @@ class DiffPlan:
     def run(self):
         """Enqueue the diff on the current stream; returns without syncing."""
         lib = load()
-        if self._fos is None:
-            check(lib.delta_diff_many(self.nparams, self._optrs, self._nptrs, self._nums,
-                                      _ptr(self.idx), _ptr(self.val), self.capacity,
-                                      _ptr(self.nnz), _ptr(self.offsets), _ptr(self.ws),
-                                      self.ws.numel(), _stream(self.device)))
-        else:
-            check(lib.delta_diff_many_sharded(self.nparams, self._optrs, self._nptrs, self._nums,
-                                              self._fos, _ptr(self.idx), _ptr(self.val),
-                                              self.capacity, _ptr(self.nnz), _ptr(self.offsets),
-                                              _ptr(self.ws), self.ws.numel(),
-                                              _stream(self.device)))
+        with torch.cuda.device(self.device):  # the library works on the current device
+            if self._fos is None:
+                check(lib.delta_diff_many(self.nparams, self._optrs, self._nptrs, self._nums,
+                                          _ptr(self.idx), _ptr(self.val), self.capacity,
+                                          _ptr(self.nnz), _ptr(self.offsets), _ptr(self.ws),
+                                          self.ws.numel(), _stream(self.device)))
+            else:
+                check(lib.delta_diff_many_sharded(self.nparams, self._optrs, self._nptrs,
+                                                  self._nums, self._fos, _ptr(self.idx),
+                                                  _ptr(self.val), self.capacity, _ptr(self.nnz),
+                                                  _ptr(self.offsets), _ptr(self.ws),
+                                                  self.ws.numel(), _stream(self.device)))
 
     def changed(self) -> int:
         """True total count of the last run (one device-to-host read)."""
@@ -128,10 +129,11 @@ class ApplyPlan:
             raise ValueError("violations must be an int64 tensor on the snapshots' device")
         # the kernel never reads past the buffers, whatever the device offsets say
         m = idx.numel() if max_nnz is None else min(int(max_nnz), idx.numel())
-        check(load().delta_apply_many(self.nparams, self._sptrs, self._nums, _ptr(idx), _ptr(val),
-                                      _ptr(offsets), m,
-                                      _ptr(violations) if violations is not None else None,
-                                      _ptr(self.ws), self.ws.numel(), _stream(self.device)))
+        with torch.cuda.device(dev):  # the library works on the current device
+            check(load().delta_apply_many(self.nparams, self._sptrs, self._nums, _ptr(idx),
+                                          _ptr(val), _ptr(offsets), m,
+                                          _ptr(violations) if violations is not None else None,
+                                          _ptr(self.ws), self.ws.numel(), _stream(dev)))
 
 
 class StreamedApplyPlan:
@@ -203,7 +205,9 @@ class StreamedApplyPlan:
         cur = torch.cuda.current_stream(self.device)
         cs.wait_stream(cur)
         as_.wait_stream(cur)
-        check(load().delta_apply_streamed(self.nparams, self._sptrs, self._nums, self.nchunks,
-                                          self._chunks, _ptr(self.staging), self.staging.numel(),
-                                          ctypes.c_void_p(cs.cuda_stream),
-                                          ctypes.c_void_p(as_.cuda_stream)))
+        with torch.cuda.device(self.device):  # the library works on the current device
+            check(load().delta_apply_streamed(self.nparams, self._sptrs, self._nums,
+                                              self.nchunks, self._chunks, _ptr(self.staging),
+                                              self.staging.numel(),
+                                              ctypes.c_void_p(cs.cuda_stream),
+                                              ctypes.c_void_p(as_.cuda_stream)))

@@ -175,6 +175,23 @@ def test_python_layer_rejects_bad_tensors():
         sbd.diff_many([], [])
 
 
+def test_binding_makes_the_tensors_device_current():
+    """The library works on the calling thread's current device, so every
+    wrapper that calls it runs under its tensors' device; host-only
+    arguments leave the current device alone."""
+    from sparse_bf16_delta_amd import ops
+
+    for name in ("diff", "diff_many", "apply_", "apply_many_", "apply_many_host_",
+                 "apply_streamed_", "xor_apply_streamed_", "xor_mask", "xor_apply_",
+                 "wire_encode", "wire_decode", "wire_encode_blocked", "wire_decode_blocked",
+                 "wire_hashes", "wire_checksum"):
+        assert hasattr(getattr(ops, name), "__wrapped__"), name
+    cpu = torch.zeros(4, dtype=torch.bfloat16)
+    assert ops._device_of([cpu, [cpu], (), 3, None]) is None
+    src = open(os.path.join(ROOT, "sparse_bf16_delta_amd", "plan.py")).read()
+    assert src.count("with torch.cuda.device(") == 3  # the three plans' run()
+
+
 def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(_abi, "_lib", None)
     monkeypatch.setattr(_abi, "LIB_PATH", os.path.join(ROOT, "no_such_libsbd.so"))

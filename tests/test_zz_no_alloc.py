@@ -54,3 +54,27 @@ def test_noalloc_diff_matches_delta_diff_twice():
         assert torch.equal(i[:k], i_ref[:k]) and torch.equal(v[:k], v_ref[:k])
         assert bool((i[k:] == -7).all()) and bool((v[k:] == -7).all())
         print(f"n={n}: {k} changed, identical to delta_diff", flush=True)
+
+
+def test_noalloc_diff_on_a_side_stream():
+    """On a stream of its own (a non-null handle, checked to belong to the
+    current device) the result is the same as delta_diff's on that stream."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_bf16_delta_amd import _abi
+
+    lib = _abi.load()
+    dev = torch.device("cuda:0")
+    n = 5 * 32768 + 3
+    old, new = workloads.make_step_pair(n, *workloads.seeds(1, 13), 3e-6, "fp32_master",
+                                        device=dev)
+    cap = n // 4
+    ws = torch.empty(lib.delta_workspace_size(n, 1), dtype=torch.uint8, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        assert torch.cuda.current_stream(dev).cuda_stream != 0
+        k_ref, i_ref, v_ref = _delta(lib, lib.delta_diff, old, new, cap, ws)
+        k, i, v = _delta(lib, lib.delta_diff_noalloc, old, new, cap)
+    assert 0 < k_ref <= cap and k == k_ref
+    assert torch.equal(i[:k], i_ref[:k]) and torch.equal(v[:k], v_ref[:k])
