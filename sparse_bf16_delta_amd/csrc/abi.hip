@@ -76,9 +76,10 @@ WsLayout ws_layout(int64_t max_tiles, int32_t nparams) {
   L.table = L.tile_desc + align256(sizeof(TileDesc) * tiles);
   L.tile_pos = L.table + align256(entry * size_t(nparams > 0 ? nparams : 1));
   // The slots start a fixed 9472 bytes past a 1 MB boundary of the workspace,
-  // whatever the table sizes before them.  Where the 4 KB compact slots fall
+  // whatever the table sizes before them.  Where the compact slots fall
   // relative to HBM's channel interleave measurably changes the cost of the
-  // count kernel's slot writes; on the 7B-shaped list (diff_many, ms): 1 MB
+  // count kernel's slot writes; with 4 KB slots, on the 7B-shaped list
+  // (diff_many, ms): 1 MB
   // aligned 4.64, +256 B 4.66, +1280 B 4.56, +2048 B 4.65, +9472 B 4.55
   // (the best of those tried; rotating each tile's start in its slot was
   // worse still).

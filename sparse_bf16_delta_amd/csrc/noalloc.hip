@@ -21,7 +21,7 @@ namespace sbd {
 namespace {
 
 constexpr size_t kNoAllocScratchBytes = size_t(48) << 20;
-// The fixed regions for 2^28 elements take 17.7 MiB; the rest of the array
+// The fixed regions for 2^28 elements take 17.0 MiB; the rest of the array
 // is staging arena (tiles that do not fit it are recomputed, same result).
 constexpr int64_t kNoAllocMaxElems = int64_t(1) << 28;
 
