@@ -8,8 +8,9 @@
 // concatenates the parameters' outputs in list order with per-parameter
 // counts (same review, `gather_v_batched_to_rank0`).
 //
-// How, on gfx950: three phases in five short launches, and no workgroup ever
-// waits for another one.
+// How, on gfx950: three phases in six short launches (the tile table or a
+// counter reset, count and stage, two scans, place, dense tiles), and no
+// workgroup ever waits for another one.
 //  1. Count and stage.  One workgroup of 512 lanes (eight wave64s) per tile
 //     of 32768 elements; a tile never straddles a parameter.  A lane loads
 //     eight 16-byte chunks of `old` and eight of `new`, in two halves of four

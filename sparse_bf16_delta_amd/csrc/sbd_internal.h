@@ -120,9 +120,9 @@ __device__ __forceinline__ int32_t find_param_wave0(const int64_t* __restrict__ 
 // Workspace layout (all offsets 256-byte aligned): a 256-byte header (the
 // dense-tile count and the arena fill counter), then per tile a count, an
 // in-chunk prefix, a dense-list entry, a descriptor, an arena position and a
-// 4 KB compact slot, per chunk a total and a base, the parameter table, and
+// 2 KB compact slot, per chunk a total and a base, the parameter table, and
 // last the staging arena: whatever the caller's workspace holds past
-// `wide`, up to the worst case of 16 KB per tile at `total`.
+// `wide`, up to the worst case of 32 KB per tile at `total`.
 struct WsLayout {
   size_t ndense;      // uint32: number of dense tiles
   size_t arena_next;  // uint64: arena quads handed out so far
