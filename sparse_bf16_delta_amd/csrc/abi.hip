@@ -112,9 +112,13 @@ size_t delta_workspace_size_for(int64_t total_elems, int32_t nparams, int64_t ca
   const sbd::WsLayout L = sbd::ws_layout(tiles, nparams);
   const int64_t keep = capacity < total_elems ? capacity : total_elems;
   // 4 bytes per kept entry, plus up to 16 bytes of quad rounding per tile;
-  // none at all for capacity 0 (the minimum)
-  const size_t arena = keep > 0 ? align256(size_t(4 * keep) + 16 * size_t(tiles)) : 0;
+  // none at all for capacity 0 (the minimum).  The worst case caps it, and is
+  // taken directly where 4 bytes per entry would exceed it (so the product
+  // cannot overflow).
   const size_t most = L.total - L.wide;
+  size_t arena = 0;
+  if (keep > 0)
+    arena = size_t(keep) <= most / 4 ? align256(4 * size_t(keep) + 16 * size_t(tiles)) : most;
   return L.wide + (arena < most ? arena : most);
 }
 

@@ -288,6 +288,11 @@ def test_workspace_sizes_from_capacity():
     assert mid < 1 << 30  # the 7B-shaped list at the bench's capacity
     assert lib.delta_workspace_size_for(-1, 1, 0) == 0
     assert lib.delta_workspace_size_for(1, 1, -1) == 0
+    # capacities whose 4 bytes per entry pass the worst case (or int64) get it
+    big = 1 << 62
+    assert lib.delta_workspace_size_for(big, 1, big) == lib.delta_workspace_size(big, 1)
+    top = (1 << 63) - 1
+    assert lib.delta_workspace_size_for(top, 1, top) == lib.delta_workspace_size(top, 1) > 0
     # a diff accepts the minimum and rejects one byte less, before any launch
     one = ctypes.c_void_p(16)
     m1 = lib.delta_workspace_size_for(1 << 20, 1, 0)
