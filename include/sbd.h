@@ -426,7 +426,8 @@ delta_status xor_apply_streamed(uint16_t *snapshot, const uint16_t *mask_host, i
  * delta_wire_positions_size -- exact bytes of the positions block of a delta
  * whose per-parameter counts are given by offsets_host (host int64[nparams+1],
  * e.g. delta_diff_many's offsets after the one device-to-host read).  Pure
- * host function; -1 for bad arguments.
+ * host function; -1 for bad arguments (negative or decreasing offsets) or a
+ * size beyond int64.
  */
 int64_t delta_wire_positions_size(int32_t nparams, const int64_t *numels,
                                   const int64_t *offsets_host);
@@ -505,7 +506,8 @@ delta_status delta_wire_checksum(const uint8_t *positions, int64_t npos, const u
 
 /*
  * delta_wire_blocked_size -- bytes of the blocked positions of `entries`
- * entries over the list.  Pure host function; -1 for bad arguments.
+ * entries over the list.  Pure host function; -1 for bad arguments or a size
+ * beyond int64.
  */
 int64_t delta_wire_blocked_size(int32_t nparams, const int64_t *numels, int64_t entries);
 

@@ -466,9 +466,12 @@ int64_t delta_wire_positions_size(int32_t nparams, const int64_t* numels,
   if (nparams < 0 || (nparams > 0 && (numels == nullptr || offsets_host == nullptr))) return -1;
   int64_t bytes = 0;
   for (int32_t p = 0; p < nparams; ++p) {
+    if (offsets_host[p] < 0 || offsets_host[p + 1] < offsets_host[p]) return -1;
     const int64_t count = offsets_host[p + 1] - offsets_host[p];
-    if (numels[p] < 0 || numels[p] > kInt32Max || count < 0) return -1;
-    bytes += count * wire_width(numels[p]);
+    if (numels[p] < 0 || numels[p] > kInt32Max) return -1;
+    const int w = wire_width(numels[p]);
+    if (count > (INT64_MAX - bytes) / w) return -1;  // the size would not fit int64
+    bytes += count * w;
   }
   return bytes;
 }
@@ -545,6 +548,7 @@ int64_t delta_wire_blocked_size(int32_t nparams, const int64_t* numels, int64_t 
     if (numels[p] < 0 || numels[p] > kInt32Max) return -1;
     blocks += (numels[p] + sbd::kPosBlockElems - 1) / sbd::kPosBlockElems;
   }
+  if (entries > (INT64_MAX - 4 * blocks) / 2) return -1;  // the size would not fit int64
   return 4 * blocks + 2 * entries;
 }
 

@@ -180,6 +180,14 @@ def test_wire_sizes_are_the_library_rule():
     bad = (ctypes.c_int64 * 6)(0, 3, 2, 12, 20, 20)
     assert lib.delta_wire_positions_size(len(numels), nums, bad) == -1
     assert lib.delta_wire_blocked_size(-1, nums, 0) == -1
+    # sizes past int64 are reported as -1, not wrapped
+    top = (1 << 63) - 1
+    assert lib.delta_wire_blocked_size(len(numels), nums, top) == -1
+    assert lib.delta_wire_blocked_size(len(numels), nums, (top - 36) // 2) == top - 1
+    wide = (ctypes.c_int64 * 6)(0, 0, 0, 0, (1 << 62) - 1, (1 << 62) - 1)  # 4 bytes each
+    assert lib.delta_wire_positions_size(len(numels), nums, wide) == -1
+    neg = (ctypes.c_int64 * 6)(-5, 3, 10, 12, 20, 20)
+    assert lib.delta_wire_positions_size(len(numels), nums, neg) == -1
 
 
 def test_blocked_wire_abi_rejects_bad_arguments():
