@@ -340,7 +340,8 @@ typedef struct {
  * receiver list of `nparams` snapshots and `nchunks` chunks of at most
  * `max_chunk_params` parameters and `max_chunk_nnz` entries each: the
  * snapshot table, every chunk's offsets, and two slots for idx/val.  0 for
- * negative arguments.
+ * negative arguments, or a size that does not fit size_t (more than 2^59
+ * entries per chunk).
  */
 size_t delta_streamed_staging_size(int32_t nparams, int32_t nchunks, int32_t max_chunk_params,
                                    int64_t max_chunk_nnz);
@@ -354,8 +355,8 @@ size_t delta_streamed_staging_size(int32_t nparams, int32_t nchunks, int32_t max
  *                      bytes for the largest chunk.
  * Index contract per parameter as delta_apply.
  * Errors: DELTA_E_INVALID (chunk outside the list, offsets not starting at 0
- * or decreasing, null pointers), DELTA_E_RANGE (numel > 2^31-1),
- * DELTA_E_WORKSPACE (staging too small), DELTA_E_HIP.
+ * or decreasing, null pointers), DELTA_E_RANGE (numel > 2^31-1, or a chunk of
+ * more than 2^59 entries), DELTA_E_WORKSPACE (staging too small), DELTA_E_HIP.
  */
 delta_status delta_apply_streamed(int32_t nparams, uint16_t *const *snap_ptrs,
                                   const int64_t *numels, int32_t nchunks,
@@ -394,7 +395,8 @@ delta_status delta_apply_many_host(int32_t nparams, uint16_t *const *snap_ptrs,
 
 /*
  * xor_streamed_staging_size -- device bytes of the staging buffer of
- * xor_apply_streamed for chunks of `chunk_elems` elements (0 if <= 0).
+ * xor_apply_streamed for chunks of `chunk_elems` elements (0 if <= 0 or
+ * above 2^59).
  */
 size_t xor_streamed_staging_size(int64_t chunk_elems);
 
@@ -404,7 +406,7 @@ size_t xor_streamed_staging_size(int64_t chunk_elems);
  *  snapshot            n uint16 on the device, updated in place.
  *  mask_host           (host) n uint16.
  * Errors: DELTA_E_INVALID (n < 0, chunk_elems <= 0, null pointers),
- * DELTA_E_WORKSPACE, DELTA_E_HIP.
+ * DELTA_E_RANGE (chunk_elems above 2^59), DELTA_E_WORKSPACE, DELTA_E_HIP.
  */
 delta_status xor_apply_streamed(uint16_t *snapshot, const uint16_t *mask_host, int64_t n,
                                 int64_t chunk_elems, void *staging, size_t staging_bytes,

@@ -39,6 +39,10 @@ namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The most entries (or XOR elements) a staging slot is sized for: beyond it
+// the slot's byte size would not fit size_t.
+constexpr int64_t kMaxStagedEntries = INT64_MAX / 16;
+
 // Staging layout: [table: SnapParam x nparams][offsets: int64 x nchunks x
 // (max_params + 1)][slot 0][slot 1], each slot [idx: int32 x max_nnz][val:
 // uint16 x max_nnz].
@@ -49,9 +53,16 @@ struct StagingLayout {
   size_t total;
 };
 
+// total == SIZE_MAX: the layout would not fit size_t (no buffer can hold it).
 StagingLayout staging_layout(int32_t nparams, int32_t nchunks, int32_t max_chunk_params,
                              int64_t max_chunk_nnz) {
-  StagingLayout L;
+  StagingLayout L{};
+  const uint64_t noffsets =
+      uint64_t(nchunks > 0 ? nchunks : 1) * (uint64_t(max_chunk_params > 0 ? max_chunk_params : 0) + 1);
+  if (noffsets > SIZE_MAX / 64 || max_chunk_nnz > kMaxStagedEntries) {
+    L.total = SIZE_MAX;
+    return L;
+  }
   L.table = 0;
   L.offsets = align256(sizeof(sbd::SnapParam) * size_t(nparams > 0 ? nparams : 1));
   const size_t off_bytes =
@@ -94,10 +105,12 @@ namespace sbd {
 
 size_t streamed_staging_size(int32_t nparams, int32_t nchunks, int32_t max_chunk_params,
                              int64_t max_chunk_nnz) {
-  return staging_layout(nparams, nchunks, max_chunk_params, max_chunk_nnz).total;
+  const size_t t = staging_layout(nparams, nchunks, max_chunk_params, max_chunk_nnz).total;
+  return t == SIZE_MAX ? 0 : t;
 }
 
 size_t xor_streamed_staging_size(int64_t chunk_elems) {
+  if (chunk_elems > kMaxStagedEntries) return 0;
   return 2 * align256(sizeof(uint16_t) * size_t(chunk_elems));
 }
 
@@ -148,6 +161,11 @@ delta_status apply_streamed_impl(int32_t nparams, uint16_t* const* snap_ptrs,
         return fail(DELTA_E_INVALID, buf);
       }
     const int64_t nnz = ch.offsets[ch.nparams];
+    if (nnz > kMaxStagedEntries) {
+      snprintf(buf, sizeof buf, "delta_apply_streamed: chunk %d holds %lld entries, more than "
+               "a staging buffer can address", c, (long long)nnz);
+      return fail(DELTA_E_RANGE, buf);
+    }
     if (nnz > 0 && (ch.idx == nullptr || ch.val == nullptr)) {
       snprintf(buf, sizeof buf, "delta_apply_streamed: chunk %d has entries but null idx/val", c);
       return fail(DELTA_E_INVALID, buf);
@@ -156,6 +174,8 @@ delta_status apply_streamed_impl(int32_t nparams, uint16_t* const* snap_ptrs,
     max_nnz = nnz > max_nnz ? nnz : max_nnz;
   }
   const StagingLayout L = staging_layout(nparams, nchunks, max_params, max_nnz);
+  if (L.total == SIZE_MAX)
+    return fail(DELTA_E_RANGE, "delta_apply_streamed: the staging layout does not fit size_t");
   if (staging == nullptr || staging_bytes < L.total) {
     snprintf(buf, sizeof buf, "delta_apply_streamed: staging %zu bytes, need %zu", staging_bytes,
              L.total);
@@ -224,6 +244,8 @@ delta_status xor_apply_streamed_impl(uint16_t* snapshot, const uint16_t* mask_ho
     return s;
   };
   if (n < 0 || chunk_elems <= 0) return fail(DELTA_E_INVALID, "xor_apply_streamed: n < 0 or chunk_elems <= 0");
+  if (chunk_elems > kMaxStagedEntries)
+    return fail(DELTA_E_RANGE, "xor_apply_streamed: chunk_elems too large for a staging slot");
   if (n > 0 && (snapshot == nullptr || mask_host == nullptr))
     return fail(DELTA_E_INVALID, "xor_apply_streamed: null pointer");
   // two slots of chunk_elems bf16, each 256-byte aligned
@@ -273,6 +295,7 @@ namespace {
 // leaves the runtime's per-thread error set, which the next launch check
 // would report as its own, so it is cleared here.
 const void* mapped(const void* p, int64_t count, size_t size) {
+  if (count < 0 || uint64_t(count) > UINT64_MAX / size) return nullptr;  // no byte count wraps
   uint64_t start = 0, range = 0;
   void* d = nullptr;
   const uint64_t a = reinterpret_cast<uintptr_t>(p);

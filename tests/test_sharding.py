@@ -103,6 +103,15 @@ def test_streamed_abi_rejects_bad_chunks():
                                   ctypes.c_void_p(256), 8, None, None) == _abi.DELTA_E_WORKSPACE
     assert lib.delta_streamed_staging_size(-1, 1, 0, 0) == 0
     assert lib.xor_streamed_staging_size(0) == 0
+    # counts whose staging would not fit size_t are refused, not wrapped
+    huge = (ctypes.c_int64 * 3)(0, 2, 1 << 62)
+    assert call([chunk(0, 2, huge)]) == _abi.DELTA_E_RANGE
+    assert "more than a staging buffer" in lib.delta_last_error().decode()
+    assert lib.delta_streamed_staging_size(3, 1, 2, 1 << 62) == 0
+    assert lib.delta_streamed_staging_size(3, 1, 2, 1000) > 0
+    assert lib.xor_streamed_staging_size(1 << 62) == 0
+    assert lib.xor_apply_streamed(ctypes.c_void_p(16), ctypes.c_void_p(16), 100, 1 << 62,
+                                  ctypes.c_void_p(256), 1 << 40, None, None) == _abi.DELTA_E_RANGE
 
 
 def test_host_apply_abi_rejects_bad_arguments():
@@ -132,6 +141,10 @@ def test_host_apply_abi_rejects_bad_arguments():
     assert "offsets[0]" in lib.delta_last_error().decode()
     assert call((ctypes.c_int64 * 3)(0, 3, 2)) == _abi.DELTA_E_INVALID
     assert "decrease" in lib.delta_last_error().decode()
+    # an entry count whose byte size wraps 64 bits never passes the pinned-range check
+    huge = (1 << 62) + 4
+    assert call((ctypes.c_int64 * 3)(0, 2, huge), max_nnz=huge) == _abi.DELTA_E_INVALID
+    assert "pinned host memory" in lib.delta_last_error().decode()
 
 
 def test_wire_abi_rejects_bad_arguments():
