@@ -31,7 +31,9 @@
  *    address).
  *  - Errors: a non-zero delta_status is returned before anything is
  *    enqueued when arguments are rejected; delta_last_error() describes it.
- *    DELTA_E_HIP reports a launch failure from the HIP runtime.
+ *    DELTA_E_HIP reports a launch failure from the HIP runtime.  An int64
+ *    count or byte size above 2^62 (more than any buffer holds) is rejected
+ *    with DELTA_E_RANGE.
  *  - Index layout ([TRL] section 4.1; [VERL] encode.py): indices are 0-based,
  *    flat, local to their parameter, int32, strictly ascending.  A tensor of
  *    more than 2^31-1 elements is rejected with DELTA_E_RANGE ([VERL] risks

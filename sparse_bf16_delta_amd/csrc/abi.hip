@@ -31,6 +31,9 @@ delta_status hip_status(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kInt32Max = 2147483647LL;
+// No buffer holds 2^62 elements: a count above it is refused before any size
+// or grid computation could overflow.
+constexpr int64_t kMaxCount = int64_t(1) << 62;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -253,6 +256,7 @@ delta_status apply_one(const char* fn, uint16_t* snapshot, int64_t n, const int3
     return fail(DELTA_E_INVALID, "%s: n=%lld nnz=%lld", fn, (long long)n, (long long)nnz);
   if (n > kInt32Max)
     return fail(DELTA_E_RANGE, "%s: n=%lld exceeds the int32 index range", fn, (long long)n);
+  if (nnz > kMaxCount) return fail(DELTA_E_RANGE, "%s: nnz=%lld above 2^62", fn, (long long)nnz);
   if (nnz > 0 && (snapshot == nullptr || idx == nullptr || val == nullptr))
     return fail(DELTA_E_INVALID, "%s: null pointer with nnz=%lld", fn, (long long)nnz);
   sbd::SnapParam single{snapshot, n};
@@ -286,6 +290,8 @@ delta_status delta_apply_many(int32_t nparams, uint16_t* const* snap_ptrs, const
   if (nparams < 0 || max_nnz < 0)
     return fail(DELTA_E_INVALID, "delta_apply_many: nparams=%d max_nnz=%lld", nparams,
                 (long long)max_nnz);
+  if (max_nnz > kMaxCount)
+    return fail(DELTA_E_RANGE, "delta_apply_many: max_nnz=%lld above 2^62", (long long)max_nnz);
   if (nparams == 0 || max_nnz == 0) {
     g_error.clear();
     return hip_status(sbd::launch_apply(nullptr, sbd::SnapParam{nullptr, 0}, 0, nullptr, nullptr,
@@ -351,6 +357,9 @@ delta_status delta_apply_many_host(int32_t nparams, uint16_t* const* snap_ptrs,
                                    const uint16_t* val_host, const int64_t* offsets_host,
                                    int64_t max_nnz, int64_t* violations, void* ws,
                                    size_t ws_bytes, void* stream) {
+  if (max_nnz > kMaxCount)
+    return fail(DELTA_E_RANGE, "delta_apply_many_host: max_nnz=%lld above 2^62",
+                (long long)max_nnz);
   std::string err;
   const delta_status st =
       sbd::apply_host_impl(nparams, snap_ptrs, numels, idx_host, val_host, offsets_host, max_nnz,
@@ -367,6 +376,7 @@ size_t xor_streamed_staging_size(int64_t chunk_elems) {
 delta_status xor_apply_streamed(uint16_t* snapshot, const uint16_t* mask_host, int64_t n,
                                 int64_t chunk_elems, void* staging, size_t staging_bytes,
                                 void* copy_stream, void* apply_stream) {
+  if (n > kMaxCount) return fail(DELTA_E_RANGE, "xor_apply_streamed: n=%lld above 2^62", (long long)n);
   std::string err;
   const delta_status st = sbd::xor_apply_streamed_impl(snapshot, mask_host, n, chunk_elems,
                                                        staging, staging_bytes, copy_stream,
@@ -417,6 +427,8 @@ delta_status delta_wire_encode(int32_t nparams, const int64_t* numels, const int
                                size_t ws_bytes, void* stream) {
   if (max_entries < 0 || positions_capacity < 0)
     return fail(DELTA_E_INVALID, "delta_wire_encode: negative size");
+  if (max_entries > kMaxCount || positions_capacity > kMaxCount)
+    return fail(DELTA_E_RANGE, "delta_wire_encode: size above 2^62");
   if (offsets == nullptr || pos_offsets == nullptr)
     return fail(DELTA_E_INVALID, "delta_wire_encode: null offsets");
   if (max_entries > 0 && idx == nullptr)
@@ -442,6 +454,8 @@ delta_status delta_wire_decode(int32_t nparams, const int64_t* numels, const uin
                                int64_t* violations, void* ws, size_t ws_bytes, void* stream) {
   if (max_entries < 0 || positions_bytes < 0)
     return fail(DELTA_E_INVALID, "delta_wire_decode: negative size");
+  if (max_entries > kMaxCount || positions_bytes > kMaxCount)
+    return fail(DELTA_E_RANGE, "delta_wire_decode: size above 2^62");
   if (offsets == nullptr || pos_offsets == nullptr)
     return fail(DELTA_E_INVALID, "delta_wire_decode: null offsets");
   if (max_entries > 0 && idx == nullptr) return fail(DELTA_E_INVALID, "delta_wire_decode: null idx");
@@ -479,6 +493,8 @@ int64_t delta_wire_positions_size(int32_t nparams, const int64_t* numels,
 delta_status delta_wire_hash(const uint8_t* positions, int64_t npos, const uint16_t* values,
                              int64_t nval, uint64_t* hashes, void* stream) {
   if (npos < 0 || nval < 0) return fail(DELTA_E_INVALID, "delta_wire_hash: negative size");
+  if (npos > kMaxCount || nval > kMaxCount)
+    return fail(DELTA_E_RANGE, "delta_wire_hash: size above 2^62");
   if (hashes == nullptr || (npos > 0 && positions == nullptr) || (nval > 0 && values == nullptr))
     return fail(DELTA_E_INVALID, "delta_wire_hash: null pointer");
   g_error.clear();
@@ -490,6 +506,8 @@ delta_status delta_wire_hash(const uint8_t* positions, int64_t npos, const uint1
 delta_status delta_wire_checksum(const uint8_t* positions, int64_t npos, const uint16_t* values,
                                  int64_t nval, uint64_t* checksum, void* stream) {
   if (npos < 0 || nval < 0) return fail(DELTA_E_INVALID, "delta_wire_checksum: negative size");
+  if (npos > kMaxCount || nval > kMaxCount)
+    return fail(DELTA_E_RANGE, "delta_wire_checksum: size above 2^62");
   if (checksum == nullptr || (npos > 0 && positions == nullptr) ||
       (nval > 0 && values == nullptr))
     return fail(DELTA_E_INVALID, "delta_wire_checksum: null pointer");
@@ -558,6 +576,8 @@ delta_status delta_wire_encode_blocked(int32_t nparams, const int64_t* numels, c
                                        void* stream) {
   if (max_entries < 0 || out_capacity < 0)
     return fail(DELTA_E_INVALID, "delta_wire_encode_blocked: negative size");
+  if (max_entries > kMaxCount || out_capacity > kMaxCount)
+    return fail(DELTA_E_RANGE, "delta_wire_encode_blocked: size above 2^62");
   if (offsets == nullptr) return fail(DELTA_E_INVALID, "delta_wire_encode_blocked: null offsets");
   if (max_entries > 0 && idx == nullptr)
     return fail(DELTA_E_INVALID, "delta_wire_encode_blocked: null idx");
@@ -583,6 +603,8 @@ delta_status delta_wire_decode_blocked(int32_t nparams, const int64_t* numels, c
                                        void* ws, size_t ws_bytes, void* stream) {
   if (max_entries < 0 || in_bytes < 0)
     return fail(DELTA_E_INVALID, "delta_wire_decode_blocked: negative size");
+  if (max_entries > kMaxCount || in_bytes > kMaxCount)
+    return fail(DELTA_E_RANGE, "delta_wire_decode_blocked: size above 2^62");
   if (offsets == nullptr) return fail(DELTA_E_INVALID, "delta_wire_decode_blocked: null offsets");
   if (max_entries > 0 && idx == nullptr)
     return fail(DELTA_E_INVALID, "delta_wire_decode_blocked: null idx");
@@ -605,6 +627,7 @@ delta_status delta_wire_decode_blocked(int32_t nparams, const int64_t* numels, c
 delta_status xor_mask(const uint16_t* old_bits, const uint16_t* new_bits, uint16_t* mask,
                       int64_t n, void* stream) {
   if (n < 0) return fail(DELTA_E_INVALID, "xor_mask: n=%lld < 0", (long long)n);
+  if (n > kMaxCount) return fail(DELTA_E_RANGE, "xor_mask: n=%lld above 2^62", (long long)n);
   if (n > 0 && (old_bits == nullptr || new_bits == nullptr || mask == nullptr))
     return fail(DELTA_E_INVALID, "xor_mask: null pointer with n=%lld", (long long)n);
   g_error.clear();
@@ -615,6 +638,7 @@ delta_status xor_mask(const uint16_t* old_bits, const uint16_t* new_bits, uint16
 
 delta_status xor_apply(uint16_t* snapshot, const uint16_t* mask, int64_t n, void* stream) {
   if (n < 0) return fail(DELTA_E_INVALID, "xor_apply: n=%lld < 0", (long long)n);
+  if (n > kMaxCount) return fail(DELTA_E_RANGE, "xor_apply: n=%lld above 2^62", (long long)n);
   if (n > 0 && (snapshot == nullptr || mask == nullptr))
     return fail(DELTA_E_INVALID, "xor_apply: null pointer with n=%lld", (long long)n);
   g_error.clear();

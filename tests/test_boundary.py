@@ -131,6 +131,27 @@ def test_argument_errors_return_before_any_launch():
     assert lib.xor_mask(one, None, one, 5, None) == _abi.DELTA_E_INVALID
     assert lib.xor_mask(one, one, one, -5, None) == _abi.DELTA_E_INVALID
     assert lib.xor_apply(None, one, 5, None) == _abi.DELTA_E_INVALID
+    # counts above 2^62 (e.g. INT64_MAX as "no limit") are refused, not rounded
+    # into an overflowing grid
+    top = (1 << 63) - 1
+    assert lib.delta_apply_many(2, ptrs, ok2, one, one, one, top, None, one, 1 << 20,
+                                None) == _abi.DELTA_E_RANGE
+    assert "above 2^62" in _err(lib)
+    assert lib.delta_apply(one, 10, one, one, top, None) == _abi.DELTA_E_RANGE
+    assert lib.xor_mask(one, one, one, top, None) == _abi.DELTA_E_RANGE
+    assert lib.xor_apply(one, one, top, None) == _abi.DELTA_E_RANGE
+    assert lib.xor_apply_streamed(one, one, top, 64, one, 1 << 40, None, None) == _abi.DELTA_E_RANGE
+    assert lib.delta_wire_checksum(one, top, one, 4, one, None) == _abi.DELTA_E_RANGE
+    assert lib.delta_wire_hash(one, 4, one, top, one, None) == _abi.DELTA_E_RANGE
+    w1 = (ctypes.c_int64 * 1)(10)
+    assert lib.delta_wire_encode(1, w1, one, one, top, one, 10, one, one, 1 << 30,
+                                 None) == _abi.DELTA_E_RANGE
+    assert lib.delta_wire_decode(1, w1, one, top, one, one, 5, one, None, one, 1 << 30,
+                                 None) == _abi.DELTA_E_RANGE
+    assert lib.delta_wire_encode_blocked(1, w1, one, one, top, one, 64, one, 1 << 30,
+                                         None) == _abi.DELTA_E_RANGE
+    assert lib.delta_wire_decode_blocked(1, w1, one, 64, one, top, one, None, one, 1 << 30,
+                                         None) == _abi.DELTA_E_RANGE
 
 
 def test_error_message_is_per_thread():

@@ -141,9 +141,12 @@ def test_host_apply_abi_rejects_bad_arguments():
     assert "offsets[0]" in lib.delta_last_error().decode()
     assert call((ctypes.c_int64 * 3)(0, 3, 2)) == _abi.DELTA_E_INVALID
     assert "decrease" in lib.delta_last_error().decode()
-    # an entry count whose byte size wraps 64 bits never passes the pinned-range check
+    # a count above 2^62 is refused; one of 2^62, whose int32 bytes wrap 64 bits,
+    # never passes the pinned-range check
     huge = (1 << 62) + 4
-    assert call((ctypes.c_int64 * 3)(0, 2, huge), max_nnz=huge) == _abi.DELTA_E_INVALID
+    assert call((ctypes.c_int64 * 3)(0, 2, huge), max_nnz=huge) == _abi.DELTA_E_RANGE
+    edge = 1 << 62
+    assert call((ctypes.c_int64 * 3)(0, 2, edge), max_nnz=edge) == _abi.DELTA_E_INVALID
     assert "pinned host memory" in lib.delta_last_error().decode()
 
 
