@@ -306,7 +306,7 @@ def test_workspace_sizes_from_capacity():
     assert low < mid < worst
     assert 4 * 80_000_000 <= mid - low <= 4 * 80_000_000 + 16 * (n // 32768 + k + 1) + 256
     assert lib.delta_workspace_size_for(n, k, n) == worst
-    assert mid < 1 << 30  # the 7B-shaped list at the bench's capacity
+    assert mid < 1 << 30  # the 7B-shaped list sized for about its headline delta's count
     assert lib.delta_workspace_size_for(-1, 1, 0) == 0
     assert lib.delta_workspace_size_for(1, 1, -1) == 0
     # capacities whose 4 bytes per entry pass the worst case (or int64) get it
