@@ -116,3 +116,62 @@ def test_random_lists_match_oracle(sbd, oracle_mod, seed):
         snap = go_.clone()
         sbd.xor_apply_(snap, mask)
         assert np.array_equal(np_bits(snap), x)
+
+
+SMALL_MENU = [0, 0, 0, 1, 2, 31, 33, 64, 1000, 4096, 33_000, 70_000]
+
+
+@pytest.mark.parametrize("k,seed", [(300, 0), (4100, 1), (9000, 2)])
+def test_many_small_parameters_match_oracle(sbd, oracle_mod, k, seed):
+    """Lists of hundreds to thousands of mostly tiny (often empty) tensors:
+    the parameter searches take two and three 64-way steps, apply chunks
+    straddle many parameters, and the placing walk crosses many small tiles.
+    Diff, apply and both wire encodings match the oracle bit for bit."""
+    from sparse_bf16_delta_amd.plan import DiffPlan
+
+    rng = np.random.default_rng(70_000 + seed)
+    sizes = [int(rng.choice(SMALL_MENU)) for _ in range(k)]
+    olds, news = [], []
+    for n in sizes:
+        old = rng.integers(0, 1 << 16, size=n, dtype=np.uint32).astype(np.uint16)
+        new = old.copy()
+        c = int(round(float(rng.choice(FRAC_MENU)) * n))
+        if c:
+            pos = rng.choice(n, size=c, replace=False)
+            new[pos] = (old[pos].astype(np.uint32)
+                        + rng.integers(1, 1 << 16, size=c, dtype=np.uint32)).astype(np.uint16)
+        olds.append(old)
+        news.append(new)
+    gaps = [int(g) for g in rng.integers(0, 3, size=k)]
+    ri, rv, rn, ro = oracle_mod.diff_many(olds, news)
+    _, g_old, host_old = pack(olds, gaps, 1)
+    _, g_new, _ = pack(news, gaps, 3)
+
+    plan = DiffPlan(g_old, g_new, int(ro[-1]))
+    plan.run()
+    assert plan.changed() == int(ro[-1])
+    assert np.array_equal(plan.offsets.cpu().numpy(), ro)
+    assert np.array_equal(plan.nnz.cpu().numpy(), rn)
+    assert np.array_equal(plan.idx[:ro[-1]].cpu().numpy(), ri)
+    assert np.array_equal(np_bits(plan.val[:ro[-1]]), rv)
+
+    buf, snaps, host_old = pack(olds, gaps, 1)
+    sbd.apply_many_(snaps, plan.idx[:ro[-1]], plan.val[:ro[-1]], plan.offsets, check_indices=True)
+    want = host_old.copy()
+    pos = 1
+    for x, g in zip(news, gaps):
+        want[pos:pos + x.size] = x
+        pos += x.size + g
+    assert np.array_equal(np_bits(buf), want)
+
+    gi = plan.idx[:ro[-1]]
+    want_pos, want_po = oracle_mod.wire_encode(ri, ro, sizes)
+    wpos, wpo = sbd.wire_encode(gi, plan.offsets, sizes)
+    assert np.array_equal(wpos.cpu().numpy(), want_pos)
+    assert np.array_equal(wpo.cpu().numpy(), want_po)
+    assert np.array_equal(sbd.wire_decode(wpos, wpo, plan.offsets, sizes).cpu().numpy(), ri)
+    want_blk = oracle_mod.wire_encode_blocked(ri, ro, sizes)
+    blk = sbd.wire_encode_blocked(gi, plan.offsets, sizes)
+    assert np.array_equal(blk.cpu().numpy(), want_blk)
+    assert np.array_equal(sbd.wire_decode_blocked(blk, plan.offsets, sizes).cpu().numpy(), ri)
+    print(f"k={k}: {sum(sizes)} elements, {int(ro[-1])} changed", flush=True)
