@@ -36,12 +36,14 @@
 //
 // Two kernels share these rules:
 //  * apply_kernel (deltas below kSegMinTotal entries, and larger ones above
-//    about 2.8 % density): 256-lane workgroups, chunks of 2048 entries (8 per
-//    lane, two 16-byte idx loads and one 16-byte val load), a grid bounded at
-//    kApplyGridFactor times the workgroups the GPU holds at once, striding
-//    over the chunks; scatter, windows, and for deltas of kSegMinTotal
-//    entries or more the segment rewrite in passes of 64 segments, four in
-//    flight per lane.
+//    about 2.8 % density): 256-lane workgroups with chunks of 2048 entries,
+//    or for deltas of kSegMinTotal entries or more that average
+//    kWidePerParam entries per parameter 512-lane ones with chunks of 4096
+//    (8 entries per lane: two 16-byte idx loads and one 16-byte val load), a
+//    grid bounded at kApplyGridFactor times the workgroups the GPU holds at
+//    once, striding over the chunks; scatter, windows, and for deltas of
+//    kSegMinTotal entries or more the segment rewrite in passes of a
+//    quarter of the workgroup's lanes' segments, four in flight per lane.
 //  * apply_big_kernel (deltas of kSegMinTotal entries or more at about 2.8 %
 //    density or less): 1024-lane workgroups, chunks of 1024 entries (one per
 //    lane), one chunk per workgroup in dispatch order.  The
@@ -76,10 +78,12 @@
 namespace sbd {
 namespace {
 
-constexpr int kApplyBlock = 256;
-constexpr int kApplyWaves = kApplyBlock / 64;
+// apply_kernel's workgroup width, 8 entries per lane: 256 lanes (2048-entry
+// chunks), or 512 (4096-entry chunks) for the large deltas that
+// launch_apply_kernel picks.
+constexpr int kApplyNarrow = 256;
+constexpr int kApplyWide = 512;
 constexpr int kApplyPer = 8;
-constexpr int kApplyChunk = kApplyBlock * kApplyPer;  // 2048 entries per chunk
 // Elements of span per entry that choose between the ways of writing a
 // well-formed chunk's interior segments (see above).  Segments against
 // windows on the 7B-shaped list, ms: at 4.7 % density 5.42 / 5.80, at 5.9 %
@@ -89,7 +93,6 @@ constexpr int64_t kMergeSpread = 20;
 constexpr int64_t kMergeMinSpread = 3;
 constexpr int kSegElems = 32;                // bf16 per 64-byte segment
 constexpr int kSegLanes = kSegElems / kVec;  // 4 lanes x 16 bytes per segment
-constexpr int kSegGroups = kApplyBlock / kSegLanes;  // segments per apply_kernel pass
 constexpr int kSegUnroll = 4;                        // segments in flight per lane
 // Fewest delta entries for which sparse chunks rewrite whole segments.
 constexpr int64_t kSegMinTotal = int64_t(1) << 25;
@@ -119,14 +122,18 @@ constexpr int64_t kBigGridCap = int64_t(1) << 17;
 
 enum ApplyMode : int { kScatter = 0, kWindows = 1, kSegments = 2 };
 
-// The touched-segment list of a sparse workgroup (16 KB, the window's size).
+// The touched-segment list of a sparse workgroup (8 bytes per entry of its
+// chunk: 16 KB, the window's size, for 256 lanes).
+template <int kChunk>
 struct SegList {
-  uint32_t pos[kApplyChunk];    // per entry: its index plus the segment shift
-  uint16_t val[kApplyChunk];    // per entry: its value
-  uint16_t first[kApplyChunk];  // the first entry of each listed segment
+  uint32_t pos[kChunk];    // per entry: its index plus the segment shift
+  uint16_t val[kChunk];    // per entry: its value
+  uint16_t first[kChunk];  // the first entry of each listed segment
 };
 
+template <int kB>
 struct ApplyShared {
+  static constexpr int kApplyWaves = kB / 64;
   int64_t total;
   int32_t p0;
   int32_t one_param;  // every entry of the chunk belongs to parameter p0
@@ -139,7 +146,7 @@ struct ApplyShared {
   uint32_t last_first;          // the first entry in the last touched segment
   union {
     __attribute__((aligned(16))) uint16_t win[kMergeWindow];  // snapshot window being patched
-    __attribute__((aligned(16))) SegList sl;
+    __attribute__((aligned(16))) SegList<kB * kApplyPer> sl;
   };
 };
 
@@ -217,12 +224,16 @@ __device__ __forceinline__ void chunk_head(int64_t j0, int chunk, int32_t nparam
 // delta's total, and then does nothing.
 // kSegOK: the segment rewrite is compiled in (the launch's capacity allows a
 // delta of kSegMinTotal entries); without it the kernel needs fewer registers.
-template <bool kMany, bool kSegOK>
+template <bool kMany, bool kSegOK, int kB>
 __device__ __forceinline__ bool apply_chunk(
     int64_t j0, const SnapParam* __restrict__ table, const SnapParam& single, int32_t nparams,
     const int64_t* __restrict__ offsets, const int32_t* __restrict__ idx,
     const uint16_t* __restrict__ val, int64_t max_nnz, int64_t* __restrict__ violations,
-    ApplyShared& sh) {
+    ApplyShared<kB>& sh) {
+  constexpr int kApplyBlock = kB;
+  constexpr int kApplyWaves = kB / 64;
+  constexpr int kApplyChunk = kB * kApplyPer;
+  constexpr int kSegGroups = kB / kSegLanes;  // segments per pass
   if (threadIdx.x < 64) {
     int64_t total = max_nnz;
     if constexpr (kMany) {
@@ -576,16 +587,17 @@ __device__ __forceinline__ bool apply_chunk(
   return false;
 }
 
-template <bool kMany, bool kSegOK>
-__global__ __launch_bounds__(kApplyBlock) void apply_kernel(
+template <bool kMany, bool kSegOK, int kB>
+__global__ __launch_bounds__(kB) void apply_kernel(
     const SnapParam* __restrict__ table, SnapParam single, int32_t nparams,
     const int64_t* __restrict__ offsets, const int32_t* __restrict__ idx,
     const uint16_t* __restrict__ val, int64_t max_nnz, int64_t* __restrict__ violations) {
-  __shared__ ApplyShared sh;
+  constexpr int kApplyChunk = kB * kApplyPer;
+  __shared__ ApplyShared<kB> sh;
   const int64_t nchunks = (max_nnz + kApplyChunk - 1) / kApplyChunk;
   for (int64_t chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {
-    const bool past = apply_chunk<kMany, kSegOK>(chunk * kApplyChunk, table, single, nparams,
-                                                 offsets, idx, val, max_nnz, violations, sh);
+    const bool past = apply_chunk<kMany, kSegOK, kB>(chunk * kApplyChunk, table, single, nparams,
+                                                     offsets, idx, val, max_nnz, violations, sh);
     __syncthreads();  // the shared state is rewritten by the next chunk
     if (past) break;  // this workgroup's later chunks lie past the total too
   }
@@ -819,7 +831,7 @@ __global__ __launch_bounds__(kBigBlock) void apply_big_kernel(
 // slower (too little dynamic balancing between chunks of different cost).
 constexpr int64_t kApplyGridFactor = 16;
 
-template <bool kMany, bool kSegOK>
+template <bool kMany, bool kSegOK, int kB>
 int64_t apply_grid_limit() {
   static std::atomic<int64_t> cached[64];  // zero-initialised; threads may race to fill it
   constexpr int64_t kFallback = 256 * 8 * kApplyGridFactor;
@@ -831,8 +843,8 @@ int64_t apply_grid_limit() {
   int64_t lim = cached[dev].load(std::memory_order_relaxed);
   if (lim == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, apply_kernel<kMany, kSegOK>,
-                                                     kApplyBlock, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, apply_kernel<kMany, kSegOK, kB>,
+                                                     kB, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         per_cu < 1 || cus < 1) {
       (void)hipGetLastError();
@@ -844,16 +856,27 @@ int64_t apply_grid_limit() {
   return lim;
 }
 
-template <bool kMany, bool kSegOK>
+template <bool kMany, bool kSegOK, int kB>
 void launch_apply_kernel(const SnapParam* d_table, const SnapParam& single, int32_t nparams,
                          const int64_t* offsets, const int32_t* idx, const uint16_t* val,
                          int64_t max_nnz, int64_t* violations, hipStream_t stream) {
+  constexpr int64_t kApplyChunk = int64_t(kB) * kApplyPer;
   int64_t blocks = (max_nnz + kApplyChunk - 1) / kApplyChunk;
-  const int64_t lim = apply_grid_limit<kMany, kSegOK>();
+  const int64_t lim = apply_grid_limit<kMany, kSegOK, kB>();
   if (blocks > lim) blocks = lim;
-  apply_kernel<kMany, kSegOK><<<dim3(unsigned(blocks)), dim3(kApplyBlock), 0, stream>>>(
+  apply_kernel<kMany, kSegOK, kB><<<dim3(unsigned(blocks)), dim3(kB), 0, stream>>>(
       d_table, single, nparams, offsets, idx, val, max_nnz, violations);
 }
+
+// Entries per parameter (max_nnz over nparams) from which a delta of at
+// least kSegMinTotal entries runs in 512-lane workgroups.  A chunk that
+// straddles parameters writes every entry with 2-byte stores, so longer
+// chunks pay off only where parameters hold many chunks each.  Measured (ms,
+// 256 / 512 lanes): one 405B-shaped layer at 8 % 2.84 / 2.72; 7B-shaped list
+// fp32-master 8 % 6.04 / 5.84, bf16 3.5 % 4.45 / 4.35, 11.6 % 5.34 / 5.29,
+// its first 48 million entries alone 0.727 / 0.723; the Qwen3-0.6B-shaped
+// list at 8 % (155,000 entries per parameter) 0.465 / 0.490.
+constexpr int64_t kWidePerParam = int64_t(1) << 20;
 
 // Which kernel: apply_big_kernel when the delta is large enough for the
 // segment rewrite and sparse enough (max_nnz entries over total_elems
@@ -879,12 +902,15 @@ void launch_apply_kernels(const SnapParam* d_table, const SnapParam& single, int
     if (blocks > kBigGridCap) blocks = kBigGridCap;
     apply_big_kernel<kMany><<<dim3(unsigned(blocks)), dim3(kBigBlock), 0, stream>>>(
         d_table, single, nparams, offsets, idx, val, max_nnz, violations);
+  } else if (max_nnz >= kSegMinTotal && max_nnz / nparams >= kWidePerParam) {
+    launch_apply_kernel<kMany, true, kApplyWide>(d_table, single, nparams, offsets, idx, val,
+                                                 max_nnz, violations, stream);
   } else if (max_nnz >= kSegMinTotal) {
-    launch_apply_kernel<kMany, true>(d_table, single, nparams, offsets, idx, val, max_nnz,
-                                     violations, stream);
+    launch_apply_kernel<kMany, true, kApplyNarrow>(d_table, single, nparams, offsets, idx, val,
+                                                   max_nnz, violations, stream);
   } else {
-    launch_apply_kernel<kMany, false>(d_table, single, nparams, offsets, idx, val, max_nnz,
-                                      violations, stream);
+    launch_apply_kernel<kMany, false, kApplyNarrow>(d_table, single, nparams, offsets, idx, val,
+                                                    max_nnz, violations, stream);
   }
 }
 
