@@ -42,8 +42,8 @@
 //    (8 entries per lane: two 16-byte idx loads and one 16-byte val load), a
 //    grid bounded at kApplyGridFactor times the workgroups the GPU holds at
 //    once, striding over the chunks; scatter, windows, and for deltas of
-//    kSegMinTotal entries or more the segment rewrite in passes of a
-//    quarter of the workgroup's lanes' segments, four in flight per lane.
+//    kSegMinTotal entries or more the segment rewrite in passes of one
+//    segment per four lanes, four passes in flight.
 //  * apply_big_kernel (deltas of kSegMinTotal entries or more at about 2.8 %
 //    density or less): 1024-lane workgroups, chunks of 1024 entries (one per
 //    lane), one chunk per workgroup in dispatch order.  The
